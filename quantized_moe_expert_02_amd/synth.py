@@ -1,0 +1,220 @@
+"""Seeded synthetic inputs for the 4-bit MoE FFN layer.
+
+This module only draws random numbers and encodes them into the canonical
+storage format; it holds none of the layer's arithmetic (no routing, no
+decode of codes back to weights, no products).  Both the GPU path and the
+CPU oracle consume the bytes it produces.
+
+Canonical storage format (all row-major, little-endian):
+
+* ``q[rows][cols/2]`` uint8 per matrix (gate ``[I][H]``, up ``[I][H]``,
+  down ``[H][I]``); element ``2j`` sits in the low nibble of byte ``j``,
+  element ``2j+1`` in the high nibble.
+* INT4_ROW: a nibble is a two's-complement integer in [-8, 7]; one binary16
+  scale per output row (``s[rows]``).  This is the
+  "int4 with a per-row scale" format of the Colibrì engine (hakusoku.com
+  story 8412, section 実装済み機能).
+* E2M1_B16: a nibble is an OCP FP4 E2M1 code; one OCP FP8 E4M3 scale byte per
+  16 consecutive weights along the row (``s[rows][cols/16]``) and one fp32
+  tensor scale per matrix (``g``).  This is the NVFP4-style format that the
+  Ornith engine decodes inside its matmul kernel (648news.com, Ornith
+  inference engine article, section on splitting weights between VRAM and
+  system memory).
+
+Value distributions follow the layer workloads: activations ~ N(0, 1) rounded
+to binary16, router weights ~ N(0, 0.02) fp32, expert weights ~ N(0, 0.02)
+quantised symmetrically (int4: scale = amax_row / 7; e2m1: tensor scale
+g = amax / (6 * 448), block scale = e4m3(amax_block / (6 g))).
+"""
+from __future__ import annotations
+
+import dataclasses
+import hashlib
+from typing import List, Optional
+
+import numpy as np
+import torch
+
+INT4_ROW = 0
+E2M1_B16 = 1
+
+# Binary16/E4M3 encoders are torch's own conversions; the e2m1 encoder below
+# picks the nearest representable magnitude by bucketing at the midpoints of
+# the E2M1 value grid.  These choose *inputs*; any deterministic choice would
+# serve, since both implementations consume the resulting codes as given.
+_E2M1_MIDPOINTS = (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0)
+
+
+@dataclasses.dataclass(frozen=True)
+class Dims:
+    hidden: int
+    inter: int
+    n_experts: int
+    top_k: int
+    has_shared: int = 1
+    wfmt: int = INT4_ROW
+
+    def as_tuple(self):
+        return (self.hidden, self.inter, self.n_experts, self.top_k, self.has_shared, self.wfmt)
+
+
+# Named workloads.  Sizes follow the pages: ~19 MB per int4 expert and 256
+# experts per MoE layer (hakusoku.com story 8412, section Colibrì), 8 experts
+# per token (same page, section 性能・要件).
+WORKLOADS = {
+    "tiny": dict(dims=Dims(256, 128, 8, 2, 1, INT4_ROW), tokens=4),
+    "decode_b1": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=1),
+    "decode_b8": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=8),
+    "e2m1_b1": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=1),
+    "e2m1_b4": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=4),
+    "prefill_2048": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=2048, zipf=1.1),
+}
+
+
+def _seed(*parts) -> int:
+    h = hashlib.sha256(("moe:" + ":".join(str(p) for p in parts)).encode()).digest()
+    return int.from_bytes(h[:8], "little") & ((1 << 63) - 1)
+
+
+def _gen(device, *parts) -> torch.Generator:
+    g = torch.Generator(device=device)
+    g.manual_seed(_seed(*parts))
+    return g
+
+
+def pack_nibbles(codes: torch.Tensor) -> torch.Tensor:
+    """codes int [.., cols] with values 0..15 -> uint8 [.., cols/2], even element in the low nibble."""
+    c = codes.to(torch.uint8) & 0xF
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).contiguous()
+
+
+def quantize_int4_rows(w: torch.Tensor):
+    """fp32 [.., rows, cols] -> (q uint8 [.., rows, cols/2], s binary16 [.., rows])."""
+    amax = w.abs().amax(dim=-1)
+    s16 = (amax / 7.0).to(torch.float16)
+    s16 = torch.where(s16 == 0, torch.ones_like(s16), s16)
+    q = torch.clamp(torch.round(w / s16.float().unsqueeze(-1)), -8, 7).to(torch.int16)
+    return pack_nibbles(q & 0xF), s16
+
+
+def quantize_e2m1_blocks(w: torch.Tensor):
+    """fp32 [.., rows, cols] -> (q uint8 [.., rows, cols/2], s uint8 e4m3 [.., rows, cols/16], g fp32 [..])."""
+    lead = w.shape[:-2]
+    rows, cols = w.shape[-2], w.shape[-1]
+    amax_t = w.abs().flatten(-2).amax(dim=-1)
+    g = (amax_t / (6.0 * 448.0)).clamp_min(1e-30)
+    blk = w.reshape(*lead, rows, cols // 16, 16)
+    amax_b = blk.abs().amax(dim=-1)
+    sc = (amax_b / (6.0 * g[..., None, None])).clamp(max=448.0).to(torch.float8_e4m3fn)
+    sc_val = sc.float()
+    denom = (g[..., None, None] * sc_val).unsqueeze(-1)
+    v = torch.where(denom > 0, blk / torch.where(denom > 0, denom, torch.ones_like(denom)), torch.zeros_like(blk))
+    mids = torch.tensor(_E2M1_MIDPOINTS, dtype=v.dtype, device=v.device)
+    mag = torch.bucketize(v.abs().contiguous(), mids, right=False)  # 0..7
+    sign = (v < 0).to(torch.int64) << 3
+    codes = (mag | sign).reshape(*lead, rows, cols)
+    return pack_nibbles(codes), sc.view(torch.uint8), g.to(torch.float32)
+
+
+@dataclasses.dataclass
+class Layer:
+    """One MoE layer in canonical format.  Expert tensors are stacked with
+    index ``n_experts`` holding the shared expert (when ``has_shared``)."""
+    dims: Dims
+    q_gate: torch.Tensor  # uint8 [E+S][I][H/2]
+    s_gate: torch.Tensor  # int4: binary16 [E+S][I]; e2m1: uint8 e4m3 [E+S][I][H/16]
+    q_up: torch.Tensor
+    s_up: torch.Tensor
+    q_down: torch.Tensor  # uint8 [E+S][H][I/2]
+    s_down: torch.Tensor
+    g3: torch.Tensor      # fp32 [E+S][3] (1.0 for INT4_ROW)
+    router_w: torch.Tensor  # fp32 [E][H]
+    router_b: Optional[torch.Tensor]  # fp32 [E] or None
+
+    @property
+    def n_stored(self):
+        return self.q_gate.shape[0]
+
+    def to(self, device):
+        f = lambda t: None if t is None else t.to(device)
+        return Layer(self.dims, *(f(getattr(self, n)) for n in
+                     ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down", "g3", "router_w", "router_b")))
+
+
+def make_experts(dims: Dims, n: int, seed_tag, device="cpu", std=0.02, batch=8):
+    """Quantised expert weights for ``n`` experts (the last one is the shared
+    expert when the caller counts it in ``n``)."""
+    H, I = dims.hidden, dims.inter
+    qg = torch.empty((n, I, H // 2), dtype=torch.uint8, device=device)
+    qu = torch.empty_like(qg)
+    qd = torch.empty((n, H, I // 2), dtype=torch.uint8, device=device)
+    if dims.wfmt == INT4_ROW:
+        sg = torch.empty((n, I), dtype=torch.float16, device=device)
+        su = torch.empty_like(sg)
+        sd = torch.empty((n, H), dtype=torch.float16, device=device)
+    else:
+        sg = torch.empty((n, I, H // 16), dtype=torch.uint8, device=device)
+        su = torch.empty_like(sg)
+        sd = torch.empty((n, H, I // 16), dtype=torch.uint8, device=device)
+    g3 = torch.ones((n, 3), dtype=torch.float32, device=device)
+    for e0 in range(0, n, batch):
+        e1 = min(n, e0 + batch)
+        mats = []
+        for m, shape in enumerate(((I, H), (I, H), (H, I))):
+            w = torch.stack([
+                torch.randn(shape, generator=_gen(device, seed_tag, e, m), device=device, dtype=torch.float32)
+                for e in range(e0, e1)]) * std
+            mats.append(w)
+        for m, (qdst, sdst) in enumerate(((qg, sg), (qu, su), (qd, sd))):
+            if dims.wfmt == INT4_ROW:
+                q, s = quantize_int4_rows(mats[m])
+                qdst[e0:e1] = q
+                sdst[e0:e1] = s
+            else:
+                q, s, g = quantize_e2m1_blocks(mats[m])
+                qdst[e0:e1] = q
+                sdst[e0:e1] = s
+                g3[e0:e1, m] = g
+        del mats
+    return qg, sg, qu, su, qd, sd, g3
+
+
+def make_router(dims: Dims, seed_tag, device="cpu", zipf: float = 0.0):
+    E, H = dims.n_experts, dims.hidden
+    rw = torch.randn((E, H), generator=_gen(device, seed_tag, "router"), device=device, dtype=torch.float32) * 0.02
+    rb = None
+    if zipf > 0:
+        # Skewed per-expert logit bias: b_e = ln p_{pi(e)} - mean, p_r ~ r^-zipf,
+        # pi a seeded permutation, so token counts per expert are uneven.
+        rng = np.random.Generator(np.random.PCG64(_seed(seed_tag, "zipf")))
+        perm = rng.permutation(E)
+        r = np.arange(1, E + 1, dtype=np.float64)
+        logp = -zipf * np.log(r)
+        logp = logp - np.log(np.exp(logp).sum())
+        b = logp[perm]
+        b = b - b.mean()
+        rb = torch.tensor(b, dtype=torch.float32, device=device)
+    return rw, rb
+
+
+def make_layer(dims: Dims, seed_tag, device="cpu", zipf: float = 0.0) -> Layer:
+    n = dims.n_experts + (1 if dims.has_shared else 0)
+    qg, sg, qu, su, qd, sd, g3 = make_experts(dims, n, (seed_tag, "experts"), device=device)
+    rw, rb = make_router(dims, seed_tag, device=device, zipf=zipf)
+    return Layer(dims, qg, sg, qu, su, qd, sd, g3, rw, rb)
+
+
+def make_tokens(dims: Dims, T: int, seed_tag, device="cpu") -> torch.Tensor:
+    """x ~ N(0,1) rounded to binary16, shape [T][H]."""
+    if T == 0:
+        return torch.empty((0, dims.hidden), dtype=torch.float16, device=device)
+    return torch.randn((T, dims.hidden), generator=_gen(device, seed_tag, "x"), device=device,
+                       dtype=torch.float32).to(torch.float16)
+
+
+def workload(name: str, seed=0, device="cpu", layer_idx=0):
+    w = WORKLOADS[name]
+    dims = w["dims"]
+    layer = make_layer(dims, (name, seed, layer_idx), device=device, zipf=w.get("zipf", 0.0))
+    x = make_tokens(dims, w["tokens"], (name, seed, layer_idx), device=device)
+    return layer, x

@@ -1,0 +1,295 @@
+"""Pins for the CPU oracle: each check compares it with something other than
+itself -- numpy/torch library conversions, the OCP E2M1 value table, brute
+force over subsets, a dense SwiGLU FFN built from numpy matmuls, or an
+invariant that the layer's definition fixes."""
+import itertools
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+from quantized_moe_expert_02_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _np_int4_codes(q: np.ndarray) -> np.ndarray:
+    """Two's-complement nibbles via numpy's arithmetic shift on int8."""
+    q = np.asarray(q, dtype=np.uint8)
+    lo = (q << 4).view(np.int8) >> 4
+    hi = q.view(np.int8) >> 4
+    out = np.empty(q.shape[:-1] + (2 * q.shape[-1],), dtype=np.int64)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def _golden_e2m1():
+    vals = {}
+    with open(os.path.join(GOLDEN, "e2m1_values.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            c, v = line.split()
+            vals[int(c)] = float(v)
+    return np.array([vals[c] for c in range(16)])
+
+
+def _np_dequant(layer, e, which):
+    """Dense float64 weights by an independent route: numpy sign extension,
+    numpy binary16, torch E4M3 and the OCP E2M1 table."""
+    q = getattr(layer, "q_" + which)[e].numpy()
+    s = getattr(layer, "s_" + which)[e]
+    if layer.dims.wfmt == synth.INT4_ROW:
+        codes = _np_int4_codes(q).astype(np.float64)
+        return codes * s.numpy().astype(np.float64)[:, None]
+    table = _golden_e2m1()
+    nib = np.empty(q.shape[:-1] + (2 * q.shape[-1],), dtype=np.int64)
+    nib[..., 0::2] = q & 0xF
+    nib[..., 1::2] = q >> 4
+    sc = s.view(torch.float8_e4m3fn).double().numpy()
+    g = float(layer.g3[e, ["gate", "up", "down"].index(which)])
+    return table[nib] * np.repeat(sc, 16, axis=-1) * g
+
+
+def _dense_swiglu(layer, e, x64):
+    wg, wu, wd = (_np_dequant(layer, e, m) for m in ("gate", "up", "down"))
+    g = x64 @ wg.T
+    u = x64 @ wu.T
+    h = g * expit(g) * u
+    return h @ wd.T
+
+
+# ---- code tables ---------------------------------------------------------
+def test_fp16_decode_all_bit_patterns(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    ref = bits.view(np.float16).astype(np.float64)
+    got = orc.fp16_values(bits)
+    fin = np.isfinite(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.array_equal(np.signbit(got[fin]), np.signbit(ref[fin]))
+
+
+def test_int4_all_256_bytes(orc):
+    q = np.arange(256, dtype=np.uint8)
+    got = orc.int4_values(q)
+    assert np.array_equal(got, _np_int4_codes(q[None, :])[0])
+    assert got.min() == -8 and got.max() == 7
+
+
+def test_int4_pack_unpack_round_trip(orc):
+    rng = np.random.default_rng(1)
+    codes = rng.integers(-8, 8, size=(37, 64))
+    packed = synth.pack_nibbles(torch.tensor(codes & 0xF)).numpy()
+    assert packed.shape == (37, 32)
+    assert np.array_equal(orc.int4_values(packed).reshape(37, 64), codes)
+
+
+def test_e2m1_all_16_codes(orc):
+    q = np.array([c | (c2 << 4) for c in range(16) for c2 in (0,)], dtype=np.uint8)
+    got = orc.e2m1_values(q)[0::2]
+    ref = _golden_e2m1()
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+
+
+def test_e4m3_all_256_codes(orc):
+    b = np.arange(256, dtype=np.uint8)
+    ref = torch.tensor(b).view(torch.float8_e4m3fn).double().numpy()
+    got = orc.e4m3_values(b)
+    fin = ~np.isnan(ref)
+    assert np.array_equal(got[fin], ref[fin])
+    assert np.array_equal(np.isnan(got), np.isnan(ref))
+    assert np.isnan(ref).sum() == 2  # 0x7F and 0xFF only
+
+
+def test_e2m1_times_e4m3_exact_in_fp16():
+    """Every e2m1 x e4m3 product is a binary16 number (so decoding a weight
+    tile to fp16 before the block scale is applied loses nothing)."""
+    e2 = _golden_e2m1()
+    e4 = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    e4 = e4[np.isfinite(e4)]
+    prod = np.outer(e2, e4).ravel()
+    assert np.array_equal(prod.astype(np.float16).astype(np.float64), prod)
+
+
+@pytest.mark.parametrize("fmt", [synth.INT4_ROW, synth.E2M1_B16])
+def test_dequant_matches_independent_decode(orc, fmt):
+    dims = synth.Dims(64, 128, 2, 1, 0, fmt)
+    layer = synth.make_layer(dims, ("dequant", fmt))
+    for which, (rows, cols) in (("gate", (128, 64)), ("down", (64, 128))):
+        m = ["gate", "up", "down"].index(which)
+        got = orc.dequant(fmt, getattr(layer, "q_" + which)[1], getattr(layer, "s_" + which)[1],
+                          float(layer.g3[1, m]), rows, cols)
+        assert np.array_equal(got, _np_dequant(layer, 1, which))
+
+
+# ---- routing -------------------------------------------------------------
+def _tiny_route_layer(E, k, H=64, seed=0, bias=False):
+    dims = synth.Dims(H, 32, E, k, 1, synth.INT4_ROW)
+    rw, _ = synth.make_router(dims, ("route", E, k, seed))
+    rb = torch.randn(E, generator=torch.Generator().manual_seed(seed)) if bias else None
+    x = synth.make_tokens(dims, 6, ("route", E, k, seed))
+    return dims, x, rw, rb
+
+
+@pytest.mark.parametrize("E,k,bias", [(4, 1, False), (6, 2, True), (8, 3, False), (10, 4, True), (10, 10, False)])
+def test_topk_brute_force_subsets(orc, E, k, bias):
+    dims, x, rw, rb = _tiny_route_layer(E, k, bias=bias)
+    r = orc.route(dims, x, rw, rb)
+    z_np = x.double().numpy() @ rw.double().numpy().T + (rb.double().numpy() if rb is not None else 0.0)
+    np.testing.assert_allclose(r.z, z_np, rtol=1e-12, atol=1e-12)
+    for t in range(x.shape[0]):
+        best = max(itertools.combinations(range(E), k), key=lambda s: sum(z_np[t, list(s)]))
+        assert set(r.topk_idx[t]) == set(best)
+        zs = z_np[t, r.topk_idx[t]]
+        assert np.all(np.diff(zs) < 0), "slots must be in descending score order"
+        s = expit(zs)
+        np.testing.assert_allclose(r.topk_w[t], s / s.sum(), rtol=1e-6)
+        assert abs(float(np.sum(r.topk_w[t].astype(np.float64))) - 1.0) <= k * 2.0 ** -24
+        assert np.all(r.topk_w[t] > 0)
+
+
+def test_topk_ties_go_to_lower_index(orc):
+    """Duplicated router rows give bitwise-equal logits; the lower expert
+    index must win (a fixed, deterministic top-k)."""
+    E, k = 8, 3
+    dims, x, rw, _ = _tiny_route_layer(E, k, seed=3)
+    rw = rw.clone()
+    r0 = orc.route(dims, x, rw, None)
+    top = int(r0.topk_idx[0, 0])
+    for twin in range(E):
+        if twin == top:
+            continue
+        rw2 = rw.clone()
+        rw2[twin] = rw[top]
+        r = orc.route(dims, x, rw2, None)
+        a, b = min(top, twin), max(top, twin)
+        assert r.z[0, a] == r.z[0, b]
+        row = list(r.topk_idx[0])
+        assert row.index(a) + 1 == row.index(b), (row, a, b)
+
+
+def test_union_definition_and_batch_consistency(orc):
+    dims, x, rw, rb = _tiny_route_layer(10, 3, seed=5)
+    r = orc.route(dims, x, rw, rb)
+    T, k = r.topk_idx.shape
+    chosen = sorted(set(int(e) for e in r.topk_idx.ravel()))
+    assert list(r.uniq_ids) == chosen
+    for u, e in enumerate(chosen):
+        seg = list(r.pairs[r.uniq_off[u]:r.uniq_off[u + 1]])
+        want = [t * k + j for t in range(T) for j in range(k) if r.topk_idx[t, j] == e]
+        assert seg == want
+    assert r.uniq_off[-1] == T * k
+    # Union of per-token results equals the batch result.
+    per = [orc.route(dims, x[t:t + 1], rw, rb) for t in range(T)]
+    assert sorted(set().union(*[set(p.uniq_ids.tolist()) for p in per])) == chosen
+    for t in range(T):
+        assert np.array_equal(per[t].topk_idx[0], r.topk_idx[t])
+        assert np.array_equal(per[t].topk_w[0], r.topk_w[t])
+
+
+def test_route_empty_batch(orc):
+    dims, x, rw, rb = _tiny_route_layer(6, 2)
+    r = orc.route(dims, x[:0], rw, rb)
+    assert r.n_unique == 0 and list(r.uniq_off) == [0]
+
+
+# ---- expert FFN and the whole layer ---------------------------------------
+@pytest.mark.parametrize("fmt", [synth.INT4_ROW, synth.E2M1_B16])
+def test_single_expert_equals_dense_swiglu(orc, fmt):
+    """E=1, k=1, no shared expert: the routing weight is exactly one and the
+    layer is a dense SwiGLU FFN, computed here with numpy matmuls."""
+    dims = synth.Dims(128, 256, 1, 1, 0, fmt)
+    layer = synth.make_layer(dims, ("dense", fmt))
+    x = synth.make_tokens(dims, 3, ("dense", fmt))
+    y = orc.forward(layer, x)
+    ref = _dense_swiglu(layer, 0, x.double().numpy())
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-14)
+
+
+def test_shared_expert_added_with_weight_one(orc):
+    dims = synth.Dims(128, 64, 1, 1, 1, synth.INT4_ROW)
+    layer = synth.make_layer(dims, "shared1")
+    x = synth.make_tokens(dims, 2, "shared1")
+    y = orc.forward(layer, x)
+    x64 = x.double().numpy()
+    ref = _dense_swiglu(layer, 0, x64) + _dense_swiglu(layer, 1, x64)
+    np.testing.assert_allclose(y, ref, rtol=1e-11, atol=1e-14)
+
+
+def test_identical_experts_sum_to_one_copy(orc):
+    """When every routed expert holds the same weights, the renormalised
+    weights sum to one and the routed part equals one dense FFN."""
+    dims = synth.Dims(128, 64, 6, 3, 1, synth.INT4_ROW)
+    layer = synth.make_layer(dims, "ident")
+    for name in ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down"):
+        t = getattr(layer, name)
+        t[:6] = t[0].clone()
+    x = synth.make_tokens(dims, 3, "ident")
+    y = orc.forward(layer, x)
+    x64 = x.double().numpy()
+    ref = _dense_swiglu(layer, 0, x64) + _dense_swiglu(layer, 6, x64)
+    np.testing.assert_allclose(y, ref, rtol=1e-10, atol=1e-14)
+
+
+def test_slot_weight_linearity(orc):
+    """Doubling the down-projection scales of the expert in slot j adds
+    w_j * FFN_{e_j}(x) to y: the weight applied to each slot is its own."""
+    dims = synth.Dims(128, 64, 8, 3, 1, synth.INT4_ROW)
+    layer = synth.make_layer(dims, "lin")
+    x = synth.make_tokens(dims, 1, "lin")
+    r = orc.route(dims, x, layer.router_w, layer.router_b)
+    y0 = orc.forward(layer, x)
+    x64 = x.double().numpy()
+    for j in range(3):
+        e = int(r.topk_idx[0, j])
+        l2 = synth.Layer(**{f.name: getattr(layer, f.name) for f in __import__("dataclasses").fields(layer)})
+        l2.s_down = layer.s_down.clone()
+        l2.s_down[e] = (layer.s_down[e].float() * 2).half()
+        y1 = orc.forward(l2, x)
+        s = expit(r.z[0, r.topk_idx[0]])
+        wj = s[j] / s.sum()
+        np.testing.assert_allclose(y1 - y0, wj * _dense_swiglu(layer, e, x64), rtol=1e-9, atol=1e-13)
+
+
+def test_batch_equals_per_token_bitwise(orc):
+    layer, x = synth.workload("tiny")
+    yb = orc.forward(layer, x)
+    for t in range(x.shape[0]):
+        assert np.array_equal(orc.forward(layer, x, tokens=[t])[0], yb[t])
+    # and the token list may be any order / subset
+    yp = orc.forward(layer, x, tokens=[3, 1])
+    assert np.array_equal(yp[0], yb[3]) and np.array_equal(yp[1], yb[1])
+
+
+def test_thread_count_does_not_change_bits(orc):
+    layer, x = synth.workload("tiny")
+    assert np.array_equal(orc.forward(layer, x, threads=1), orc.forward(layer, x, threads=4))
+
+
+def test_zero_input_gives_zero_output(orc):
+    layer, x = synth.workload("tiny")
+    y = orc.forward(layer, torch.zeros_like(x))
+    assert np.all(y == 0.0)
+
+
+def test_expert_permutation_invariance(orc):
+    layer, x = synth.workload("tiny")
+    E = layer.dims.n_experts
+    perm = torch.tensor(np.random.default_rng(7).permutation(E))
+    full = torch.cat([perm, torch.tensor([E])])
+    l2 = synth.Layer(layer.dims, *(getattr(layer, n)[full] for n in
+                                   ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down", "g3")),
+                     layer.router_w[perm], None)
+    np.testing.assert_array_equal(orc.forward(l2, x), orc.forward(layer, x))
+
+
+def test_token_permutation_equivariance(orc):
+    layer, x = synth.workload("tiny")
+    perm = [2, 0, 3, 1]
+    np.testing.assert_array_equal(orc.forward(layer, x[perm]), orc.forward(layer, x)[perm])
