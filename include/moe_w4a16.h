@@ -1,0 +1,166 @@
+/*
+ * moe_w4a16.h -- C ABI of the MI355X (gfx950) 4-bit-weight Mixture-of-Experts
+ * FFN layer.
+ *
+ * The layer (one MoE FFN block of a large MoE language model):
+ *   - weights are 4-bit and activations binary16 ("W4A16": INT4 weights with
+ *     FP16 activations; "GLM-5.3-Flash 320B MoEを4枚のCMP 170HXで動かすvLLMレシピ",
+ *     648news.com, section "OpenAI互換APIで動く320BパラメータのMoE構成").  Two
+ *     weight formats: int4 with one scale per row ("Show HN: 低速のコンピュータで
+ *     GLM 5.2を動かす方法", hakusoku.com, section 実装済み機能), and NVFP4-style
+ *     e2m1 codes with block scales, decoded in registers inside the matmul
+ *     ("GTX 1070向け35BパラメータMoEモデル推論エンジン公開", 648news.com, section
+ *     "VRAMとシステムメモリで重みを分割する設計");
+ *   - a DeepSeek-V3-style sigmoid router picks top_k of n_experts routed
+ *     experts per token, and a shared expert is always added (hakusoku.com,
+ *     section 実装済み機能);
+ *   - the unique experts chosen across the batch are gathered once and each is
+ *     applied to every token that chose it (hakusoku.com, section 実装済み機能,
+ *     "batch-wise MoE union");
+ *   - each expert is a SwiGLU FFN: h = silu(Wg x) * (Wu x), o = Wd h;
+ *   - y[t] = sum_j w[t][j] * o_{e(t,j)} + o_shared, with w the sigmoid scores
+ *     of the kept experts renormalised to sum to one.
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
+ *     allocates every buffer; the library never allocates or frees memory and
+ *     keeps no global mutable state, so calls on different streams with
+ *     different workspaces may run concurrently.
+ *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *     Each call validates its arguments on the host, enqueues its kernels and
+ *     returns; outputs are valid once the stream has synchronised.  No call
+ *     copies, synchronises or allocates, so every call can be captured in a
+ *     HIP graph.
+ *   - Validation happens before any launch; on failure the call returns a
+ *     negative moe_status_t, launches nothing and leaves outputs untouched.
+ *     No call prints or throws.
+ *   - Inputs must be finite.  The same inputs give bitwise-identical outputs
+ *     (no floating-point atomics; all reductions run in a fixed order).
+ *   - All device pointers must be 16-byte aligned; packed experts 256-byte.
+ *   - The workspace must be zero-filled once before its first use (e.g.
+ *     allocated with torch.zeros).  Its first moe_workspace_sync_bytes(d)
+ *     bytes hold completion counters that every call leaves at zero again,
+ *     so a zeroed workspace stays valid for any later call and any T, but
+ *     two calls that overlap in time must not share one workspace.
+ */
+#ifndef MOE_W4A16_H
+#define MOE_W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVAL = -1,       /* null/misaligned pointer, bad size, T < 0, k > E ... */
+  MOE_E_UNSUPPORTED = -2, /* shape or format outside the supported set          */
+  MOE_E_WORKSPACE = -3,   /* ws_bytes < moe_workspace_bytes(d, T)               */
+  MOE_E_HIP = -4          /* a kernel launch failed                              */
+} moe_status_t;
+
+typedef enum {
+  /* int4 two's complement in [-8, 7]; one binary16 scale per output row:
+   * W[r][c] = q[r][c] * s[r]. */
+  MOE_W_INT4_ROW = 0,
+  /* OCP FP4 E2M1 codes; one OCP FP8 E4M3 (FN) scale per 16 consecutive
+   * weights along the row, and one fp32 tensor scale g per matrix:
+   * W[r][c] = e2m1(q[r][c]) * e4m3(s[r][c/16]) * g. */
+  MOE_W_E2M1_B16 = 1
+} moe_wfmt_t;
+
+/* Layer shape (host struct).  Supported: hidden and inter multiples of 128,
+ * 1 <= top_k <= min(n_experts, 32), n_experts <= 1024, has_shared in {0,1},
+ * wfmt a moe_wfmt_t. */
+typedef struct {
+  int32_t hidden;     /* H: model width                                  */
+  int32_t inter;      /* I: expert intermediate width                    */
+  int32_t n_experts;  /* E: routed experts                               */
+  int32_t top_k;      /* k: routed experts kept per token                */
+  int32_t has_shared; /* 1 if a shared expert is added to every token    */
+  int32_t wfmt;       /* moe_wfmt_t                                      */
+} moe_dims_t;
+
+/* Weights of one layer (host struct holding device pointers). */
+typedef struct {
+  /* DEVICE array of n_experts DEVICE pointers; entry e points to routed
+   * expert e packed by moe_pack (moe_packed_bytes(d) bytes, 256-B aligned). */
+  const void* const* experts;
+  /* The packed shared expert; NULL iff has_shared == 0. */
+  const void* shared;
+  /* Router weights, fp32 [E][H] row-major. */
+  const float* router_w;
+  /* Router logit bias, fp32 [E], or NULL for none.  It is added to the
+   * logits before the top-k and the sigmoid. */
+  const float* router_b;
+} moe_weights_t;
+
+/* Bytes of one packed expert (gate, up, down and their scales). */
+size_t moe_packed_bytes(const moe_dims_t* d);
+
+/* Bytes of scratch memory that moe_route / moe_w4a16_forward need for T
+ * tokens (see the zero-fill rule above).  Returns 0 for invalid dims. */
+size_t moe_workspace_bytes(const moe_dims_t* d, int32_t T);
+
+/* Bytes at the start of the workspace that hold completion counters. */
+size_t moe_workspace_sync_bytes(const moe_dims_t* d);
+
+/* Canonical expert -> packed device layout (a byte permutation; the values
+ * are unchanged).  Canonical inputs, all row-major on the device:
+ *   q_gate, q_up: uint8 [I][H/2]; q_down: uint8 [H][I/2]; element 2j in the
+ *     low nibble of byte j, element 2j+1 in the high nibble;
+ *   INT4_ROW: s_gate, s_up: binary16 [I]; s_down: binary16 [H]; g3 ignored;
+ *   E2M1_B16: s_gate, s_up: uint8 E4M3 [I][H/16]; s_down: uint8 [H][I/16];
+ *     g3: fp32 [3] tensor scales (gate, up, down), or NULL for 1.0.
+ * packed_out receives moe_packed_bytes(d) bytes. */
+int moe_pack(const moe_dims_t* d, const void* q_gate, const void* s_gate, const void* q_up,
+             const void* s_up, const void* q_down, const void* s_down, const float* g3,
+             void* packed_out, void* stream);
+
+/* Inverse of moe_pack (for tests): writes the canonical tensors back.
+ * g3 may be NULL. */
+int moe_unpack(const moe_dims_t* d, const void* packed, void* q_gate, void* s_gate, void* q_up,
+               void* s_up, void* q_down, void* s_down, float* g3, void* stream);
+
+/* Router and batch union for T tokens (x: binary16 [T][H]).
+ * Logits are accumulated in fp64: z[t][e] = b[e] + sum_h x[t][h]*Wr[e][h].
+ * Experts are ranked by (z descending, index ascending); the first k are
+ * kept in that order.  w[t][j] = sigmoid(z_j) / sum_j' sigmoid(z_j').
+ * Outputs:
+ *   topk_idx int32 [T][k], topk_w fp32 [T][k];
+ *   n_unique int32 [1]: distinct experts chosen by the batch;
+ *   uniq_ids int32 [min(E, T*k)]: those experts, ascending;
+ *   uniq_off int32 [min(E, T*k) + 1]: uniq_off[u]..uniq_off[u+1] is expert
+ *     u's range in pairs;
+ *   pairs int32 [T*k]: pair ids t*k + j, grouped by expert and in ascending
+ *     token order within each group.
+ * Entries past n_unique are unspecified.  T == 0 launches nothing and
+ * returns MOE_OK (outputs untouched). */
+int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
+              int32_t* topk_idx, float* topk_w, int32_t* n_unique, int32_t* uniq_ids,
+              int32_t* uniq_off, int32_t* pairs, void* ws, size_t ws_bytes, void* stream);
+
+/* The whole layer for T tokens: route, union, experts, combine.
+ *   x: binary16 [T][H]; y: binary16 [T][H] (output);
+ *   topk_idx_out int32 [T][k] and topk_w_out fp32 [T][k]: optional copies of
+ *   the routing decision (NULL to skip).
+ * Small batches take the GEMV path (weights streamed once per unique
+ * expert); larger batches take the grouped-GEMM path on the matrix cores.
+ * Both compute the same function.  T == 0 is a no-op. */
+int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
+                      uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                      void* stream);
+
+/* Largest T served by the GEMV path of moe_w4a16_forward. */
+int32_t moe_decode_max_tokens(void);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4A16_H */

@@ -1,0 +1,233 @@
+"""Python binding of the MI355X 4-bit MoE FFN layer library (libmoe_w4a16.so).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  PyTorch provides device memory and the current stream.  The
+functions carry the names of the C entry points declared in
+include/moe_w4a16.h.  If the built library is missing, importing the binding
+succeeds but every call raises -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
+
+MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4
+MOE_W_INT4_ROW, MOE_W_E2M1_B16 = 0, 1
+
+EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
+           "moe_route", "moe_w4a16_forward", "moe_decode_max_tokens", "moe_status_string")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("wfmt", ctypes.c_int32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("experts", ctypes.c_void_p), ("shared", ctypes.c_void_p), ("router_w", ctypes.c_void_p),
+                ("router_b", ctypes.c_void_p)]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {moe_status_string(code)} ({code})")
+
+
+_lib = None
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing; build it with quantized_moe_expert_02_amd/build.py")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        D = ctypes.POINTER(MoeDims)
+        W = ctypes.POINTER(MoeWeights)
+        L.moe_packed_bytes.argtypes = [D]
+        L.moe_packed_bytes.restype = sz
+        L.moe_workspace_bytes.argtypes = [D, i32]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_workspace_sync_bytes.argtypes = [D]
+        L.moe_workspace_sync_bytes.restype = sz
+        L.moe_pack.argtypes = [D, P, P, P, P, P, P, P, P, P]
+        L.moe_pack.restype = ctypes.c_int
+        L.moe_unpack.argtypes = [D, P, P, P, P, P, P, P, P, P]
+        L.moe_unpack.restype = ctypes.c_int
+        L.moe_route.argtypes = [D, W, P, i32, P, P, P, P, P, P, P, sz, P]
+        L.moe_route.restype = ctypes.c_int
+        L.moe_w4a16_forward.argtypes = [D, W, P, i32, P, P, P, P, sz, P]
+        L.moe_w4a16_forward.restype = ctypes.c_int
+        L.moe_decode_max_tokens.restype = i32
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _dims(d) -> MoeDims:
+    if isinstance(d, MoeDims):
+        return d
+    t = d.as_tuple() if hasattr(d, "as_tuple") else tuple(d)
+    return MoeDims(*[int(v) for v in t])
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def moe_status_string(code: int) -> str:
+    return lib().moe_status_string(int(code)).decode()
+
+
+def moe_packed_bytes(dims) -> int:
+    return int(lib().moe_packed_bytes(ctypes.byref(_dims(dims))))
+
+
+def moe_workspace_bytes(dims, T: int) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(_dims(dims)), int(T)))
+
+
+def moe_workspace_sync_bytes(dims) -> int:
+    return int(lib().moe_workspace_sync_bytes(ctypes.byref(_dims(dims))))
+
+
+def moe_decode_max_tokens() -> int:
+    return int(lib().moe_decode_max_tokens())
+
+
+def workspace(dims, T: int, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of moe_workspace_bytes(dims, T) bytes."""
+    n = moe_workspace_bytes(dims, T)
+    if n == 0:
+        raise MoeError(MOE_E_INVAL, "moe_workspace_bytes")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def moe_pack(dims, q_gate, s_gate, q_up, s_up, q_down, s_down, g3=None, out=None, stream=None) -> torch.Tensor:
+    d = _dims(dims)
+    if out is None:
+        out = torch.empty(moe_packed_bytes(d), dtype=torch.uint8, device=q_gate.device)
+    rc = lib().moe_pack(ctypes.byref(d), _p(q_gate), _p(s_gate), _p(q_up), _p(s_up), _p(q_down), _p(s_down),
+                        _p(g3), _p(out), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_pack")
+    return out
+
+
+def moe_unpack(dims, packed, stream=None):
+    d = _dims(dims)
+    H, I = d.hidden, d.inter
+    dev = packed.device
+    qg = torch.empty((I, H // 2), dtype=torch.uint8, device=dev)
+    qu = torch.empty_like(qg)
+    qd = torch.empty((H, I // 2), dtype=torch.uint8, device=dev)
+    if d.wfmt == MOE_W_INT4_ROW:
+        sg = torch.empty(I, dtype=torch.float16, device=dev)
+        su = torch.empty_like(sg)
+        sd = torch.empty(H, dtype=torch.float16, device=dev)
+    else:
+        sg = torch.empty((I, H // 16), dtype=torch.uint8, device=dev)
+        su = torch.empty_like(sg)
+        sd = torch.empty((H, I // 16), dtype=torch.uint8, device=dev)
+    g3 = torch.empty(4, dtype=torch.float32, device=dev)
+    rc = lib().moe_unpack(ctypes.byref(d), _p(packed), _p(qg), _p(sg), _p(qu), _p(su), _p(qd), _p(sd), _p(g3),
+                          _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_unpack")
+    return qg, sg, qu, su, qd, sd, g3[:3]
+
+
+class PackedLayer:
+    """Device-resident packed weights of one layer plus the expert pointer
+    table that the C ABI takes (a device array of device pointers)."""
+
+    def __init__(self, dims, packed: torch.Tensor, router_w: torch.Tensor, router_b: Optional[torch.Tensor]):
+        self.dims = dims
+        self.packed = packed  # uint8 [E + S][packed_bytes]
+        self.router_w = router_w.contiguous()
+        self.router_b = None if router_b is None else router_b.contiguous()
+        pb = packed.shape[1]
+        base = packed.data_ptr()
+        E = dims.n_experts
+        self.table = torch.tensor([base + e * pb for e in range(E)], dtype=torch.int64, device=packed.device)
+        self.shared_ptr = base + E * pb if dims.has_shared else None
+
+    @classmethod
+    def from_layer(cls, layer, device="cuda", stream=None):
+        """Pack a canonical synth.Layer (weights on any device) onto `device`."""
+        d = layer.dims
+        pb = moe_packed_bytes(d)
+        n = layer.q_gate.shape[0]
+        packed = torch.empty((n, pb), dtype=torch.uint8, device=device)
+        for e in range(n):
+            t = [getattr(layer, a)[e].to(device).contiguous() for a in
+                 ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down")]
+            g3 = layer.g3[e].to(device).contiguous()
+            moe_pack(d, *t, g3=g3, out=packed[e], stream=stream)
+        rb = None if layer.router_b is None else layer.router_b.to(device)
+        return cls(d, packed, layer.router_w.to(device), rb)
+
+    def clone(self):
+        """Same weights at new device addresses."""
+        return PackedLayer(self.dims, self.packed.clone(), self.router_w.clone(),
+                           None if self.router_b is None else self.router_b.clone())
+
+    def weights(self) -> MoeWeights:
+        return MoeWeights(self.table.data_ptr(), self.shared_ptr, self.router_w.data_ptr(),
+                          None if self.router_b is None else self.router_b.data_ptr())
+
+
+def moe_route(layer: PackedLayer, x: torch.Tensor, ws: Optional[torch.Tensor] = None, stream=None):
+    d = _dims(layer.dims)
+    T = x.shape[0]
+    k, E = d.top_k, d.n_experts
+    dev = x.device
+    cap = max(1, min(E, T * k))
+    out = dict(topk_idx=torch.empty((T, k), dtype=torch.int32, device=dev),
+               topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+               n_unique=torch.zeros(4, dtype=torch.int32, device=dev),
+               uniq_ids=torch.full((cap,), -1, dtype=torch.int32, device=dev),
+               uniq_off=torch.full((cap + 4,), -1, dtype=torch.int32, device=dev),
+               pairs=torch.full((max(1, T * k),), -1, dtype=torch.int32, device=dev))
+    if ws is None:
+        ws = workspace(d, T, dev)
+    w = layer.weights()
+    rc = lib().moe_route(ctypes.byref(d), ctypes.byref(w), _p(x), T, _p(out["topk_idx"]), _p(out["topk_w"]),
+                         _p(out["n_unique"]), _p(out["uniq_ids"]), _p(out["uniq_off"]), _p(out["pairs"]),
+                         _p(ws), ws.numel(), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_route")
+    return out
+
+
+def moe_w4a16_forward(layer: PackedLayer, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                      ws: Optional[torch.Tensor] = None, topk_idx: Optional[torch.Tensor] = None,
+                      topk_w: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    d = _dims(layer.dims)
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, d.hidden), dtype=torch.float16, device=x.device)
+    if ws is None:
+        ws = workspace(d, T, x.device)
+    w = layer.weights()
+    rc = lib().moe_w4a16_forward(ctypes.byref(d), ctypes.byref(w), _p(x), T, _p(y), _p(topk_idx), _p(topk_w),
+                                 _p(ws), ws.numel(), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w4a16_forward")
+    return y

@@ -1,0 +1,236 @@
+// Host side of the C ABI declared in include/moe_w4a16.h: argument
+// validation, workspace planning and kernel launches.  Nothing here
+// allocates, copies or synchronises.
+#include <string.h>
+
+#include "common.h"
+
+namespace moe {
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline size_t up256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Largest f <= fmax with (K/128) % f == 0, so every K-segment is a whole
+// number of 128-column groups.
+int split_factor(int K, int fmax) {
+  const int g = K / 128;
+  for (int f = fmax; f > 1; --f)
+    if (g % f == 0) return f;
+  return 1;
+}
+
+int check_dims(const moe_dims_t* d) {
+  if (!d) return MOE_E_INVAL;
+  if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts || d->hidden <= 0 || d->inter <= 0)
+    return MOE_E_INVAL;
+  if (d->has_shared != 0 && d->has_shared != 1) return MOE_E_INVAL;
+  if (d->wfmt != MOE_W_INT4_ROW && d->wfmt != MOE_W_E2M1_B16) return MOE_E_UNSUPPORTED;
+  if (d->hidden % 128 || d->inter % 128) return MOE_E_UNSUPPORTED;
+  if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_E_UNSUPPORTED;
+  if ((int64_t)d->hidden * d->inter > (int64_t)1 << 30) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+constexpr int32_t kMaxTokens = 1 << 20;
+
+}  // namespace
+
+bool make_plan(const moe_dims_t& d, int T, Plan* p) {
+  Plan q{};
+  q.T = T;
+  q.H = d.hidden;
+  q.I = d.inter;
+  q.E = d.n_experts;
+  q.k = d.top_k;
+  q.S = d.has_shared;
+  q.decode = T <= kDecodeMaxTokens;
+  q.slots_max = q.S + (int)std::min<int64_t>(q.E, (int64_t)T * q.k);
+  q.rows_total = T * q.k + T;
+  q.ks_gu = split_factor(q.H, 8);
+  q.ks_dn = split_factor(q.I, 4);
+  // Counters: one for the router, one per (slot, gate/up row block) for the
+  // largest decode batch, one per down row block.
+  const int slots_decode = q.S + std::min(q.E, kDecodeMaxTokens * q.k);
+  q.c_route = 0;
+  q.c_gu = 64;  // keep the router counter on its own cache line
+  q.c_dn = q.c_gu + (size_t)slots_decode * (q.I / 64);
+  q.n_counters = q.c_dn + q.H / 64;
+  q.sync_bytes = up256(q.n_counters * 4);
+  size_t off = q.sync_bytes;
+  const size_t Tk = (size_t)T * q.k;
+  const size_t cap = std::max<size_t>(1, std::min<size_t>(q.E, Tk));
+  q.z_off = off; off = up256(off + (size_t)T * q.E * 8);
+  q.idx_off = off; off = up256(off + Tk * 4);
+  q.w_off = off; off = up256(off + Tk * 4);
+  q.nu_off = off; off = up256(off + 4);
+  q.ids_off = off; off = up256(off + cap * 4);
+  q.off_off = off; off = up256(off + (cap + 1) * 4);
+  q.pairs_off = off; off = up256(off + std::max<size_t>(1, Tk) * 4);
+  const size_t nch = ((size_t)T + 31) / 32;
+  q.ucnt_off = off; off = up256(off + nch * q.E * 4);
+  q.ubase_off = off; off = up256(off + nch * q.E * 4);
+  q.tiles_off = off; off = up256(off + (Tk / 16 + q.E + T / 16 + 4) * 8);
+  q.h_off = off; off = up256(off + (size_t)q.rows_total * q.I * 2);
+  if (q.decode) {
+    q.p_gu_off = off; off = up256(off + (size_t)q.ks_gu * q.rows_total * 2 * q.I * 4);
+    q.p_dn_off = off; off = up256(off + (size_t)q.ks_dn * q.rows_total * q.H * 4);
+  } else {
+    q.p_gu_off = 0;
+    q.p_dn_off = off; off = up256(off + (size_t)q.rows_total * q.H * 4);
+  }
+  q.total = off;
+  *p = q;
+  return true;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+namespace {
+
+Route route_ptrs(const Plan& p, void* ws) {
+  char* b = (char*)ws;
+  Route r{};
+  r.z = (double*)(b + p.z_off);
+  r.topk_idx = (int32_t*)(b + p.idx_off);
+  r.topk_w = (float*)(b + p.w_off);
+  r.n_unique = (int32_t*)(b + p.nu_off);
+  r.uniq_ids = (int32_t*)(b + p.ids_off);
+  r.uniq_off = (int32_t*)(b + p.off_off);
+  r.pairs = (int32_t*)(b + p.pairs_off);
+  r.ucnt = (int32_t*)(b + p.ucnt_off);
+  r.ubase = (int32_t*)(b + p.ubase_off);
+  r.counter = (uint32_t*)ws + p.c_route;
+  return r;
+}
+
+int check_weights(const moe_dims_t* d, const moe_weights_t* w) {
+  if (!w || !w->experts || !w->router_w) return MOE_E_INVAL;
+  if (!aligned16(w->experts) || !aligned16(w->router_w) || (w->router_b && !aligned16(w->router_b)))
+    return MOE_E_INVAL;
+  if (d->has_shared ? (!w->shared || ((uintptr_t)w->shared & 255u)) : (w->shared != nullptr)) return MOE_E_INVAL;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_packed_bytes(const moe_dims_t* d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  return layout_of(*d).total;
+}
+
+size_t moe_workspace_sync_bytes(const moe_dims_t* d) {
+  if (check_dims(d) != MOE_OK) return 0;
+  Plan p;
+  make_plan(*d, 1, &p);
+  return p.sync_bytes;
+}
+
+size_t moe_workspace_bytes(const moe_dims_t* d, int32_t T) {
+  if (check_dims(d) != MOE_OK || T < 0 || T > kMaxTokens) return 0;
+  Plan p;
+  make_plan(*d, T, &p);
+  return p.total;
+}
+
+int32_t moe_decode_max_tokens(void) { return kDecodeMaxTokens; }
+
+int moe_pack(const moe_dims_t* d, const void* q_gate, const void* s_gate, const void* q_up, const void* s_up,
+             const void* q_down, const void* s_down, const float* g3, void* packed_out, void* stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  const void* ps[] = {q_gate, s_gate, q_up, s_up, q_down, s_down, packed_out};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return MOE_E_INVAL;
+  if (((uintptr_t)packed_out & 255u) || (g3 && ((uintptr_t)g3 & 3u))) return MOE_E_INVAL;
+  if (launch_pack(*d, q_gate, s_gate, q_up, s_up, q_down, s_down, g3, packed_out, (hipStream_t)stream) !=
+      hipSuccess)
+    return MOE_E_HIP;
+  return MOE_OK;
+}
+
+int moe_unpack(const moe_dims_t* d, const void* packed, void* q_gate, void* s_gate, void* q_up, void* s_up,
+               void* q_down, void* s_down, float* g3, void* stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  const void* ps[] = {packed, q_gate, s_gate, q_up, s_up, q_down, s_down};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return MOE_E_INVAL;
+  if (((uintptr_t)packed & 255u) || (g3 && ((uintptr_t)g3 & 3u))) return MOE_E_INVAL;
+  if (launch_unpack(*d, packed, q_gate, s_gate, q_up, s_up, q_down, s_down, g3, (hipStream_t)stream) != hipSuccess)
+    return MOE_E_HIP;
+  return MOE_OK;
+}
+
+int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, int32_t* topk_idx,
+              float* topk_w, int32_t* n_unique, int32_t* uniq_ids, int32_t* uniq_off, int32_t* pairs, void* ws,
+              size_t ws_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_E_INVAL;
+  if (T > kMaxTokens) return MOE_E_UNSUPPORTED;
+  if (!w || !w->router_w || !aligned16(w->router_w) || (w->router_b && !aligned16(w->router_b)))
+    return MOE_E_INVAL;
+  if (T == 0) return MOE_OK;
+  const void* ps[] = {x, topk_idx, topk_w, n_unique, uniq_ids, uniq_off, pairs, ws};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return MOE_E_INVAL;
+  Plan p;
+  make_plan(*d, T, &p);
+  if (ws_bytes < p.total) return MOE_E_WORKSPACE;
+  Route r = route_ptrs(p, ws);
+  r.topk_idx = topk_idx;
+  r.topk_w = topk_w;
+  r.n_unique = n_unique;
+  r.uniq_ids = uniq_ids;
+  r.uniq_off = uniq_off;
+  r.pairs = pairs;
+  if (launch_route(*d, p, *w, x, r, nullptr, 0, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  return MOE_OK;
+}
+
+int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
+                      int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  int st = check_dims(d);
+  if (st != MOE_OK) return st;
+  if (T < 0) return MOE_E_INVAL;
+  if (T > kMaxTokens) return MOE_E_UNSUPPORTED;
+  st = check_weights(d, w);
+  if (st != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  const void* ps[] = {x, y, ws};
+  for (const void* p : ps)
+    if (!p || !aligned16(p)) return MOE_E_INVAL;
+  if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out))) return MOE_E_INVAL;
+  Plan p;
+  make_plan(*d, T, &p);
+  if (ws_bytes < p.total) return MOE_E_WORKSPACE;
+  Route r = route_ptrs(p, ws);
+  if (topk_idx_out) r.topk_idx = topk_idx_out;
+  if (topk_w_out) r.topk_w = topk_w_out;
+  hipStream_t s = (hipStream_t)stream;
+  uint32_t* zero_from = (uint32_t*)ws + p.c_gu;
+  const size_t zero_count = p.n_counters - p.c_gu;
+  if (launch_route(*d, p, *w, x, r, zero_from, zero_count, s) != hipSuccess) return MOE_E_HIP;
+  hipError_t e = p.decode ? launch_decode_experts(*d, p, *w, x, r, ws, y, s)
+                          : launch_prefill_experts(*d, p, *w, x, r, ws, y, s);
+  return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "MOE_OK: success";
+    case MOE_E_INVAL: return "MOE_E_INVAL: invalid argument (null or misaligned pointer, bad size or T)";
+    case MOE_E_UNSUPPORTED: return "MOE_E_UNSUPPORTED: shape or format outside the supported set";
+    case MOE_E_WORKSPACE: return "MOE_E_WORKSPACE: workspace smaller than moe_workspace_bytes()";
+    case MOE_E_HIP: return "MOE_E_HIP: a kernel launch failed";
+    default: return "unknown moe status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,119 @@
+// Internal declarations shared by the HIP translation units of the library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe_w4a16.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Packed device layout of one expert (written by moe_pack).
+//
+// Weights are stored in 1 KiB blocks of 64 rows x 32 columns: lane l of a
+// wavefront reads the 16 bytes at offset 16*l, which hold row l's 32
+// consecutive columns, so one 128-bit load per lane pulls one contiguous KiB.
+//   GU region:  for rb in [0, I/64), c in [0, H/32): [gate block][up block]
+//               (2 KiB per step, so gate row i and up row i sit in one lane)
+//   D region:   for rb in [0, H/64), c in [0, I/32): [down block]
+// Inside a lane's 16 bytes, dword m holds columns 32c + 8m + (0..7).
+//   INT4_ROW: nibble position p (bits 4p..4p+3) of that dword holds column
+//     offset 2p (p < 4) or 2(p-4)+1 (p >= 4), stored offset-binary (q + 8),
+//     so that (d & 0x000F000F) and (d & 0x00F000F0) each yield a pair of
+//     adjacent columns.
+//   E2M1_B16: byte b of the dword holds columns 2b (low nibble) and 2b+1
+//     (high nibble), codes unchanged.
+// Scales:
+//   INT4_ROW: binary16 gate[I], up[I], down[H].
+//   E2M1_B16: e4m3 block scales grouped per 4 chunks (128 columns): for the
+//     GU region [rb][H/128][gate: 64 lanes x 8 B][up: 64 lanes x 8 B], for
+//     the D region [rb][I/128][64 lanes x 8 B]; byte 2j / 2j+1 of a lane's
+//     8 bytes scale columns 32j..32j+15 / 32j+16..32j+31 of the group;
+//     then fp32 g[3] (gate, up, down).
+// Every region starts on a 256-byte boundary.
+// ---------------------------------------------------------------------------
+struct Layout {
+  size_t gu_off, d_off;        // weight regions
+  size_t sg_off, su_off, sd_off;  // INT4_ROW scales
+  size_t sgu_off, sdd_off;     // E2M1 block scales
+  size_t g3_off;               // E2M1 tensor scales
+  size_t total;
+};
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+inline Layout layout_of(const moe_dims_t& d) {
+  Layout L{};
+  const size_t H = (size_t)d.hidden, I = (size_t)d.inter;
+  size_t off = 0;
+  L.gu_off = off; off = align256(off + I * H);        // gate + up, 4 bits each
+  L.d_off = off;  off = align256(off + H * I / 2);
+  if (d.wfmt == MOE_W_INT4_ROW) {
+    L.sg_off = off; off = align256(off + I * 2);
+    L.su_off = off; off = align256(off + I * 2);
+    L.sd_off = off; off = align256(off + H * 2);
+  } else {
+    L.sgu_off = off; off = align256(off + 2 * I * (H / 16));
+    L.sdd_off = off; off = align256(off + H * (I / 16));
+    L.g3_off = off;  off = align256(off + 3 * 4);
+  }
+  L.total = off;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Workspace layout.  The first `sync` bytes hold completion counters that
+// every kernel leaves at zero.
+// ---------------------------------------------------------------------------
+constexpr int kDecodeMaxTokens = 16;   // GEMV path for T <= this
+constexpr int kMaxTopK = 32;
+constexpr int kMaxExperts = 1024;
+constexpr int kRouteSmallMaxTokens = 16;
+
+struct Plan {
+  int T, H, I, E, k, S;      // S = has_shared
+  int slots_max;             // S + min(E, T*k)
+  int rows_total;            // T*k + T: h / partial rows (pair rows then shared rows)
+  int ks_gu, ks_dn;          // split-K factors of the GEMV path
+  bool decode;               // GEMV path
+  // counters (uint32), offsets in elements from ws base
+  size_t c_route, c_gu, c_dn, n_counters;
+  size_t sync_bytes;
+  // byte offsets
+  size_t z_off, idx_off, w_off, nu_off, ids_off, off_off, pairs_off;
+  size_t ucnt_off, ubase_off, tiles_off;
+  size_t h_off, p_gu_off, p_dn_off;
+  size_t total;
+};
+
+bool make_plan(const moe_dims_t& d, int T, Plan* p);
+
+// Device pointers resolved for one call.
+struct Route {
+  double* z;
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* n_unique;
+  int32_t* uniq_ids;
+  int32_t* uniq_off;
+  int32_t* pairs;
+  int32_t* ucnt;    // union: per-chunk counts
+  int32_t* ubase;   // union: per-chunk bases
+  uint32_t* counter;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_pack(const moe_dims_t& d, const void* qg, const void* sg, const void* qu, const void* su,
+                       const void* qd, const void* sd, const float* g3, void* out, hipStream_t s);
+hipError_t launch_unpack(const moe_dims_t& d, const void* packed, void* qg, void* sg, void* qu, void* su,
+                         void* qd, void* sd, float* g3, hipStream_t s);
+hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
+                        const Route& r, uint32_t* zero_from, size_t zero_count, hipStream_t s);
+hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
+                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s);
+hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
+                                  const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,12 @@
+// Prefill path (large batches): grouped GEMMs on the matrix cores.
+#include "common.h"
+
+namespace moe {
+
+hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
+                                  const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s) {
+  (void)d; (void)p; (void)w; (void)x; (void)r; (void)ws; (void)y; (void)s;
+  return hipErrorNotSupported;
+}
+
+}  // namespace moe

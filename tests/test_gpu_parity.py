@@ -1,0 +1,181 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Indices and union arrays must match bit-exactly; routing
+weights to 1e-6 relative; y to rel-L2 <= 1e-3 and max-abs <= 1e-2."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_moe_expert_02_amd as moe
+from quantized_moe_expert_02_amd import synth
+from helpers import assert_close, min_topk_gap, oracle_route, oracle_y
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _log(*a):
+    print(*a, flush=True)
+
+
+def _check_route(out, r, T, k):
+    assert np.array_equal(out["topk_idx"].cpu().numpy(), r.topk_idx), "topk_idx"
+    np.testing.assert_allclose(out["topk_w"].cpu().numpy(), r.topk_w, rtol=1e-6, atol=0)
+    nu = int(out["n_unique"][0])
+    assert nu == r.n_unique
+    assert np.array_equal(out["uniq_ids"][:nu].cpu().numpy(), r.uniq_ids)
+    assert np.array_equal(out["uniq_off"][:nu + 1].cpu().numpy(), r.uniq_off)
+    assert np.array_equal(out["pairs"][:T * k].cpu().numpy(), r.pairs)
+
+
+# ---- pack / unpack ---------------------------------------------------------
+@pytest.mark.parametrize("dims", [synth.Dims(256, 128, 2, 1, 1, 0), synth.Dims(384, 256, 2, 1, 1, 1),
+                                  synth.Dims(6144, 2048, 1, 1, 1, 0), synth.Dims(2048, 512, 1, 1, 1, 1)])
+def test_pack_unpack_round_trip(dims):
+    _log("pack", dims)
+    layer = synth.make_layer(dims, ("pack", dims.as_tuple()), device=DEV)
+    for e in range(layer.n_stored):
+        t = [getattr(layer, n)[e].contiguous() for n in ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down")]
+        packed = moe.moe_pack(dims, *t, g3=layer.g3[e].contiguous())
+        torch.cuda.synchronize()
+        back = moe.moe_unpack(dims, packed)
+        for a, b in zip(t, back[:6]):
+            assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+        if dims.wfmt == 1:
+            assert torch.equal(back[6], layer.g3[e])
+
+
+# ---- routing ---------------------------------------------------------------
+ROUTE_CASES = [
+    (synth.Dims(256, 128, 8, 2, 1, 0), 4),
+    (synth.Dims(256, 128, 8, 2, 1, 0), 1),
+    (synth.Dims(512, 128, 100, 6, 0, 0), 16),
+    (synth.Dims(6144, 2048, 256, 8, 1, 0), 1),
+    (synth.Dims(6144, 2048, 256, 8, 1, 0), 8),
+    (synth.Dims(2048, 512, 256, 8, 1, 1), 4),
+    (synth.Dims(1024, 128, 64, 1, 0, 0), 3),
+    (synth.Dims(1024, 128, 1000, 32, 1, 0), 5),
+    # large-batch route path
+    (synth.Dims(256, 128, 8, 2, 1, 0), 17),
+    (synth.Dims(512, 128, 100, 6, 0, 0), 333),
+    (synth.Dims(1024, 128, 256, 8, 1, 0), 2048),
+]
+
+
+@pytest.mark.parametrize("dims,T", ROUTE_CASES)
+def test_route_matches_oracle(dims, T):
+    _log("route", dims, T)
+    rw, rb = synth.make_router(dims, ("route", dims.as_tuple(), T), zipf=1.1 if T == 2048 else 0.0)
+    x = synth.make_tokens(dims, T, ("route", dims.as_tuple(), T))
+    r = oracle.route(dims, x, rw, rb)
+    assert min_topk_gap(r, dims.top_k) > 1e-9
+    layer = moe.PackedLayer(dims, torch.zeros((dims.n_experts + dims.has_shared, 256), dtype=torch.uint8,
+                                              device=DEV), rw.to(DEV), None if rb is None else rb.to(DEV))
+    out = moe.moe_route(layer, x.to(DEV))
+    torch.cuda.synchronize()
+    _check_route(out, r, T, dims.top_k)
+
+
+def test_route_crafted_ties_lower_index():
+    dims = synth.Dims(256, 128, 16, 4, 0, 0)
+    rw, _ = synth.make_router(dims, "ties")
+    x = synth.make_tokens(dims, 6, "ties")
+    r0 = oracle.route(dims, x, rw, None)
+    rw = rw.clone()
+    for t in range(2):
+        a = int(r0.topk_idx[t, 0])
+        rw[(a + 5) % 16] = rw[a]  # an exact twin of a top expert
+    r = oracle.route(dims, x, rw, None)
+    layer = moe.PackedLayer(dims, torch.zeros((16, 256), dtype=torch.uint8, device=DEV), rw.to(DEV), None)
+    out = moe.moe_route(layer, x.to(DEV))
+    torch.cuda.synchronize()
+    _check_route(out, r, 6, 4)
+
+
+# ---- whole layer -----------------------------------------------------------
+def _small_cases():
+    return [
+        ("tiny", synth.WORKLOADS["tiny"]["dims"], 4),
+        ("tiny_t1", synth.Dims(256, 128, 8, 2, 1, 0), 1),
+        ("no_shared_k1", synth.Dims(256, 128, 8, 1, 0, 0), 5),
+        ("ragged", synth.Dims(384, 256, 100, 6, 1, 0), 16),
+        ("e2m1_small", synth.Dims(256, 256, 8, 2, 1, 1), 4),
+        ("e2m1_ragged", synth.Dims(384, 384, 33, 3, 0, 1), 7),
+        ("dense_e1k1", synth.Dims(128, 128, 1, 1, 0, 0), 3),
+    ]
+
+
+@pytest.mark.parametrize("name,dims,T", _small_cases())
+def test_forward_small_matches_oracle(name, dims, T):
+    _log("forward", name, dims, T)
+    layer = synth.make_layer(dims, ("fwd", name))
+    x = synth.make_tokens(dims, T, ("fwd", name))
+    r = oracle_route(layer, x)
+    assert min_topk_gap(r, dims.top_k) > 1e-9
+    y_ref = oracle.forward(layer, x)
+    pl = moe.PackedLayer.from_layer(layer)
+    ti = torch.empty((T, dims.top_k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((T, dims.top_k), dtype=torch.float32, device=DEV)
+    y = moe.moe_w4a16_forward(pl, x.to(DEV), topk_idx=ti, topk_w=tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
+    np.testing.assert_allclose(tw.cpu().numpy(), r.topk_w, rtol=1e-6)
+    assert_close(y, y_ref, name)
+
+
+@pytest.mark.parametrize("name", ["decode_b1", "decode_b8", "e2m1_b1", "e2m1_b4"])
+def test_forward_full_size_matches_oracle(name):
+    """Full-size decode layers (all 256 + 1 experts resident), every output
+    element checked against the oracle."""
+    _log("full", name)
+    layer, x = synth.workload(name, device=DEV)
+    r = oracle_route(layer, x)
+    assert min_topk_gap(r, layer.dims.top_k) > 1e-9
+    pl = moe.PackedLayer.from_layer(layer)
+    y = moe.moe_w4a16_forward(pl, x)
+    torch.cuda.synchronize()
+    y_ref = oracle_y(layer, x)
+    rel, mx = assert_close(y, y_ref, name)
+    _log(f"  {name}: U={r.n_unique} rel_l2={rel:.2e} max_abs={mx:.2e}")
+
+
+def test_forward_deterministic_and_batch_invariant():
+    dims = synth.Dims(1024, 256, 64, 4, 1, 0)
+    layer = synth.make_layer(dims, "det")
+    x = synth.make_tokens(dims, 12, "det").to(DEV)
+    pl = moe.PackedLayer.from_layer(layer)
+    y1 = moe.moe_w4a16_forward(pl, x)
+    y2 = moe.moe_w4a16_forward(pl, x)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    for t in range(12):
+        yt = moe.moe_w4a16_forward(pl, x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(yt[0], y1[t]), t
+
+
+def test_forward_zero_input_and_empty_batch():
+    layer, x = synth.workload("tiny")
+    pl = moe.PackedLayer.from_layer(layer)
+    y = moe.moe_w4a16_forward(pl, torch.zeros_like(x).to(DEV))
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(y) == 0
+    y0 = torch.full((0, layer.dims.hidden), 7, dtype=torch.float16, device=DEV)
+    moe.moe_w4a16_forward(pl, x[:0].to(DEV), y=y0)
+    torch.cuda.synchronize()
+
+
+def test_workspace_reuse_across_T():
+    """One zero-filled workspace, sized for the largest T, serves calls of any
+    smaller T back to back (completion counters are left at zero)."""
+    dims = synth.Dims(512, 256, 32, 4, 1, 0)
+    layer = synth.make_layer(dims, "wsreuse")
+    pl = moe.PackedLayer.from_layer(layer)
+    ws = moe.workspace(dims, 16, DEV)
+    for T in (16, 3, 1, 9, 16):
+        x = synth.make_tokens(dims, T, ("wsreuse", T))
+        y = moe.moe_w4a16_forward(pl, x.to(DEV), ws=ws)
+        torch.cuda.synchronize()
+        assert_close(y, oracle.forward(layer, x), f"T={T}")
+    assert torch.count_nonzero(ws[: moe.moe_workspace_sync_bytes(dims)]) == 0
