@@ -1,0 +1,376 @@
+"""Benchmark of the 4-bit MoE FFN layer on one MI355X.
+
+A step is one call of moe_w4a16_forward (route, union, experts, combine) on
+one batch.  Steps cycle over L independent layer instances (each with all
+E + 1 experts resident and its own router and input) captured in a HIP
+graph, so the touched weights per graph replay far exceed the 256 MB
+Infinity Cache and every step streams its experts from HBM.
+
+Prints one JSON line: the headline workload (decode, batch 1, 6144 x 2048,
+256 experts top-8 + shared, int4 per-row scales) with a roofline object for
+its dominant kernel and the CPU oracle timed on a bounded sample.  Other
+workloads are reported under "secondary".
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import quantized_moe_expert_02_amd as moe  # noqa: E402
+from quantized_moe_expert_02_amd import synth  # noqa: E402
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+FP16_MFMA_PEAK_TFLOPS = 2500.0
+PROFILES = os.path.join(ROOT, "profiles")
+
+# stage index of the dominant kernel per path, and its name in rocprofv3 output
+DOMINANT = {"decode": (1, "k_gu_gemv"), "prefill": (1, "k_gu_gemm")}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---- algorithmic work -------------------------------------------------------
+def scale_bytes(d, rows, cols):
+    return rows * 2 if d.wfmt == synth.INT4_ROW else rows * (cols // 16)
+
+
+def expert_gu_bytes(d):
+    return d.inter * d.hidden + 2 * scale_bytes(d, d.inter, d.hidden)
+
+
+def expert_dn_bytes(d):
+    return d.hidden * d.inter // 2 + scale_bytes(d, d.hidden, d.inter)
+
+
+def layer_bytes(d, T, n_touched):
+    """Bytes the layer must move: each touched expert once (plus the shared
+    expert), the router, x in and y out."""
+    n = n_touched + d.has_shared
+    return n * (expert_gu_bytes(d) + expert_dn_bytes(d)) + d.n_experts * d.hidden * 4 + 2 * T * d.hidden * 2
+
+
+def gu_kernel_bytes(d, T, n_touched):
+    """Algorithmic bytes of the gate/up kernel: touched gate/up weights and
+    scales, x read, h written."""
+    n = n_touched + d.has_shared
+    return n * expert_gu_bytes(d) + T * d.hidden * 2 + (T * d.top_k + T * d.has_shared) * d.inter * 2
+
+
+def layer_flops(d, T):
+    return 2 * 3 * d.hidden * d.inter * T * (d.top_k + d.has_shared)
+
+
+# ---- layer chain -------------------------------------------------------------
+class Chain:
+    def __init__(self, workload: str, L: int, seed: int = 0):
+        w = synth.WORKLOADS[workload]
+        self.name = workload
+        self.dims = w["dims"]
+        self.T = w["tokens"]
+        t0 = time.time()
+        base = synth.make_layer(self.dims, (workload if "e2m1" not in workload else "e2m1", seed, 0),
+                                device="cuda", zipf=w.get("zipf", 0.0))
+        self.canon0 = base
+        pl0 = moe.PackedLayer.from_layer(base)
+        self.layers = [pl0]
+        for l in range(1, L):
+            rw, rb = synth.make_router(self.dims, (workload, seed, l, "r"), device="cuda", zipf=w.get("zipf", 0.0))
+            p = moe.PackedLayer(self.dims, pl0.packed.clone(), rw, rb)
+            self.layers.append(p)
+        self.x = [synth.make_tokens(self.dims, self.T, (workload, seed, l, "x"), device="cuda") for l in range(L)]
+        self.y = [torch.empty((self.T, self.dims.hidden), dtype=torch.float16, device="cuda") for _ in range(L)]
+        self.ws = moe.workspace(self.dims, self.T)
+        torch.cuda.synchronize()
+        log(f"[bench] {workload}: {L} layers x {self.packed_gb():.2f} GB built in {time.time() - t0:.1f}s")
+
+    def packed_gb(self):
+        return self.layers[0].packed.numel() / 1e9
+
+    def call(self, l, stream=None):
+        moe.moe_w4a16_forward(self.layers[l], self.x[l], y=self.y[l], ws=self.ws, stream=stream)
+
+    def touched(self):
+        """Realised union size per layer (read back once, outside timing)."""
+        out = []
+        for l, pl in enumerate(self.layers):
+            r = moe.moe_route(pl, self.x[l])
+            out.append(int(r["n_unique"][0]))
+        torch.cuda.synchronize()
+        return out
+
+
+def time_chain(ch: Chain, steps: int, warmup: int):
+    L = len(ch.layers)
+    graphs = []
+    full, rem = divmod(steps, L)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for l in range(L):  # eager warm-up of every layer before capture
+            ch.call(l)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g_full = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_full):
+        for l in range(L):
+            ch.call(l)
+    g_rem = None
+    if rem:
+        g_rem = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_rem):
+            for l in range(rem):
+                ch.call(l)
+    for _ in range(max(1, -(-warmup // L))):
+        g_full.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    e0.record()
+    for _ in range(full):
+        g_full.replay()
+    if g_rem is not None:
+        g_rem.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1)
+    return ms, wall
+
+
+class _Hip:
+    """A few HIP runtime calls through ctypes (raw events the library can
+    record; torch creates its own event handles lazily)."""
+
+    def __init__(self):
+        import ctypes
+        self.c = ctypes
+        L = ctypes.CDLL("libamdhip64.so")
+        L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.L = L
+
+    def event(self):
+        h = self.c.c_void_p()
+        if self.L.hipEventCreate(self.c.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return h.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = self.c.c_float(0)
+        rc = self.L.hipEventElapsedTime(self.c.byref(ms), self.c.c_void_p(a), self.c.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, h):
+        self.L.hipEventDestroy(self.c.c_void_p(h))
+
+
+def time_stages(ch: Chain, reps: int):
+    """Mean duration (ms) of each stage of a forward call, from HIP events
+    recorded by the library on its stream between stage launches."""
+    hip = _Hip()
+    L = len(ch.layers)
+    evs = [[hip.event() for _ in range(4)] for _ in range(reps * L)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(50_000_000)  # let the host queue every call before the GPU starts them
+    i = 0
+    for r in range(reps):
+        for l in range(L):
+            moe.moe_w4a16_forward_profiled(ch.layers[l], ch.x[l], ch.y[l], ch.ws, evs[i])
+            i += 1
+    torch.cuda.synchronize()
+    n = len(evs)
+    out = [sum(hip.elapsed_ms(e[j], e[j + 1]) for e in evs) / n for j in range(3)]
+    for e in evs:
+        for h in e:
+            hip.destroy(h)
+    return out
+
+
+def traffic_record(kernel: str, workload: str):
+    """Counter-measured HBM bytes per launch of `kernel` (FETCH_SIZE +
+    WRITE_SIZE, calibrated against a plain copy) if the committed record
+    matches the current kernel source; else None."""
+    path = os.path.join(PROFILES, f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    src = kv.get("source")
+    if not src or hashlib.sha256(open(os.path.join(ROOT, src), "rb").read()).hexdigest() != kv.get("source_sha256"):
+        return None
+    return float(kv["bytes_per_launch"])
+
+
+# ---- CPU baseline (the oracle, test infrastructure) ------------------------
+class _Indexable:
+    """Host copies of some experts' tensors, indexed by expert id."""
+
+    def __init__(self, d, n):
+        self.d, self.shape = d, (n,)
+
+    def __getitem__(self, e):
+        return self.d[int(e)]
+
+
+class _HostExperts:
+    """Host copies of the experts a sample needs, indexable like a Layer."""
+
+    def __init__(self, layer, experts):
+        self.dims = layer.dims
+        n = layer.q_gate.shape[0]
+        for name in ("q_gate", "s_gate", "q_up", "s_up", "q_down", "s_down"):
+            src = getattr(layer, name)
+            setattr(self, name, _Indexable({int(e): src[int(e)].cpu() for e in experts}, n))
+        self.g3 = layer.g3.cpu()
+        self.router_w = layer.router_w.cpu()
+        self.router_b = None if layer.router_b is None else layer.router_b.cpu()
+
+
+def cpu_baseline(ch: Chain, budget_s: float = 12.0, max_tokens: int = 64):
+    import numpy as np
+    import oracle
+
+    layer = ch.canon0
+    d = layer.dims
+    n_cand = max_tokens
+    xs = synth.make_tokens(d, n_cand, (ch.name, "cpu-sample"), device="cpu")
+    r = oracle.route(d, xs, layer.router_w.cpu(), None if layer.router_b is None else layer.router_b.cpu())
+    need = set(np.unique(r.topk_idx).tolist()) | ({d.n_experts} if d.has_shared else set())
+    host = _HostExperts(layer, need)
+    threads = oracle.max_threads()
+    done, t0 = 0, time.perf_counter()
+    while done < n_cand and (time.perf_counter() - t0) < budget_s:
+        oracle.forward(host, xs, tokens=[done], experts_needed=[int(e) for e in r.topk_idx[done]])
+        done += 1
+    el = time.perf_counter() - t0
+    # parity of the GPU path (one call per token, as timed) on the same sample
+    pl = moe.PackedLayer(d, ch.layers[0].packed, layer.router_w, layer.router_b)
+    xg = xs[:done].to("cuda")
+    y = torch.cat([moe.moe_w4a16_forward(pl, xg[t:t + 1].contiguous()) for t in range(done)])
+    torch.cuda.synchronize()
+    y_ref = oracle.forward(host, xs, tokens=list(range(done)), experts_needed=sorted(need - {d.n_experts}))
+    err = y.double().cpu().numpy() - y_ref
+    rel = float(np.linalg.norm(err) / np.linalg.norm(y_ref))
+    return {"value": done / el, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{done} single-token decode calls of the {ch.name} layer (seeded tokens), {el:.1f}s, "
+                      f"fp64 C++ oracle with OpenMP over output rows",
+            "parity_rel_l2_on_sample": rel}
+
+
+# ---- main ----------------------------------------------------------------------
+def run_workload(name, L, steps, warmup, stage_reps=4):
+    ch = Chain(name, L)
+    touched = ch.touched()
+    ms, wall = time_chain(ch, steps, warmup)
+    stages = time_stages(ch, stage_reps)
+    d, T = ch.dims, ch.T
+    ms_step = ms / steps
+    U = sum(touched) / len(touched)
+    lb = sum(layer_bytes(d, T, u) for u in touched) / len(touched)
+    res = {
+        "workload": name, "tokens": T, "layers_chained": L, "steps": steps,
+        "ms_per_step": ms_step, "tokens_per_s": T * steps / (ms / 1e3),
+        "mean_unique_experts": U, "layer_bytes": lb,
+        "layer_hbm_gbps": lb / (ms_step / 1e3) / 1e9,
+        "stage_ms": {"route": stages[0], "gate_up": stages[1], "down": stages[2]},
+        "wall_s": wall,
+    }
+    if T > moe.moe_decode_max_tokens():
+        res["mfma_util"] = layer_flops(d, T) / (ms_step / 1e3) / (FP16_MFMA_PEAK_TFLOPS * 1e12)
+    return ch, res, touched
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=512)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--layers", type=int, default=8)
+    ap.add_argument("--workload", default="decode_b1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's EP/TP sharding "
+              "is described in DESIGN.md but not built). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.init()
+    moe.lib()
+
+    ch, res, touched = run_workload(args.workload, args.layers, args.steps, args.warmup)
+    d, T = ch.dims, ch.T
+    path = "decode" if T <= moe.moe_decode_max_tokens() else "prefill"
+    st_idx, kname = DOMINANT[path]
+    k_ms = res["stage_ms"]["gate_up"]
+    U = res["mean_unique_experts"]
+    alg = sum(gu_kernel_bytes(d, T, u) for u in touched) / len(touched)
+    achieved = alg / (k_ms / 1e3) / 1e9
+    roofline = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(kname, args.workload),
+                "algorithmic_bytes_per_launch": alg, "avg_launch_ms": k_ms}
+    cpu = None
+    if not args.no_cpu_baseline:
+        try:
+            cpu = cpu_baseline(ch)
+        except Exception as e:  # the baseline is context, never the headline
+            cpu = {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle", "sample": f"failed: {e}"}
+    secondary = []
+    del ch
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        for name, L, steps in (("decode_b8", 8, 128), ("e2m1_b1", 32, 512), ("e2m1_b4", 32, 256)):
+            try:
+                c2, r2, _ = run_workload(name, L, steps, 32, stage_reps=2)
+                secondary.append(r2)
+                del c2
+                torch.cuda.empty_cache()
+            except Exception as e:
+                secondary.append({"workload": name, "error": str(e)})
+    out = {
+        "metric": METRIC,
+        "value": res["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": res["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "hidden": d.hidden, "inter": d.inter, "experts": d.n_experts,
+                   "shared_experts": d.has_shared, "top_k": d.top_k, "tokens": T,
+                   "weights": "int4_row" if d.wfmt == 0 else "e2m1_b16", "layers_chained": args.layers},
+        "layer_hbm_gbps": res["layer_hbm_gbps"],
+        "layer_hbm_frac": res["layer_hbm_gbps"] / HBM_PEAK_GBPS,
+        "mean_unique_experts": U,
+        "stage_ms": res["stage_ms"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -153,6 +153,17 @@ int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_
                       uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                       void* stream);
 
+/* moe_w4a16_forward with stage timing for benchmarks: `events` is a host
+ * array of n_events hipEvent_t handles (passed as void*; entries may be
+ * NULL).  events[i] is recorded on `stream` right before stage i is
+ * launched and events[n_stages] right after the last stage, where the
+ * stages are 0: routing and union, 1: gate/up projections + SwiGLU,
+ * 2: down projections + combine (n_stages = 3).  Recording adds no
+ * synchronisation.  Same arguments and results as moe_w4a16_forward. */
+int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
+                               uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws,
+                               size_t ws_bytes, void* stream, void* const* events, int32_t n_events);
+
 /* Largest T served by the GEMV path of moe_w4a16_forward. */
 int32_t moe_decode_max_tokens(void);
 

@@ -21,7 +21,8 @@ MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, 
 MOE_W_INT4_ROW, MOE_W_E2M1_B16 = 0, 1
 
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
-           "moe_route", "moe_w4a16_forward", "moe_decode_max_tokens", "moe_status_string")
+           "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_decode_max_tokens",
+           "moe_status_string")
 
 
 class MoeDims(ctypes.Structure):
@@ -67,6 +68,8 @@ def lib():
         L.moe_route.restype = ctypes.c_int
         L.moe_w4a16_forward.argtypes = [D, W, P, i32, P, P, P, P, sz, P]
         L.moe_w4a16_forward.restype = ctypes.c_int
+        L.moe_w4a16_forward_profiled.argtypes = [D, W, P, i32, P, P, P, P, sz, P, P, i32]
+        L.moe_w4a16_forward_profiled.restype = ctypes.c_int
         L.moe_decode_max_tokens.restype = i32
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
@@ -230,4 +233,20 @@ def moe_w4a16_forward(layer: PackedLayer, x: torch.Tensor, y: Optional[torch.Ten
                                  _p(ws), ws.numel(), _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w4a16_forward")
+    return y
+
+
+def moe_w4a16_forward_profiled(layer: PackedLayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor, events,
+                               stream=None) -> torch.Tensor:
+    """moe_w4a16_forward that records `events` (raw hipEvent_t handles as
+    ints, or None) before each stage and after the last: [route, gate/up,
+    down, end]."""
+    d = _dims(layer.dims)
+    T = x.shape[0]
+    handles = (ctypes.c_void_p * len(events))(*events)
+    w = layer.weights()
+    rc = lib().moe_w4a16_forward_profiled(ctypes.byref(d), ctypes.byref(w), _p(x), T, _p(y), None, None, _p(ws),
+                                          ws.numel(), _stream(stream), handles, len(events))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w4a16_forward_profiled")
     return y

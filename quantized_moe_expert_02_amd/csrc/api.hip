@@ -72,6 +72,7 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.ucnt_off = off; off = up256(off + nch * q.E * 4);
   q.ubase_off = off; off = up256(off + nch * q.E * 4);
   q.tiles_off = off; off = up256(off + (Tk / 16 + q.E + T / 16 + 4) * 8);
+  q.slots_off = off; off = up256(off + (size_t)q.slots_max * sizeof(SlotEntry));
   q.h_off = off; off = up256(off + (size_t)q.rows_total * q.I * 2);
   if (q.decode) {
     q.p_gu_off = off; off = up256(off + (size_t)q.ks_gu * q.rows_total * 2 * q.I * 4);
@@ -103,6 +104,7 @@ Route route_ptrs(const Plan& p, void* ws) {
   r.pairs = (int32_t*)(b + p.pairs_off);
   r.ucnt = (int32_t*)(b + p.ucnt_off);
   r.ubase = (int32_t*)(b + p.ubase_off);
+  r.slots = (SlotEntry*)(b + p.slots_off);
   r.counter = (uint32_t*)ws + p.c_route;
   return r;
 }
@@ -190,12 +192,13 @@ int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, in
   r.uniq_ids = uniq_ids;
   r.uniq_off = uniq_off;
   r.pairs = pairs;
-  if (launch_route(*d, p, *w, x, r, nullptr, 0, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  if (launch_route(*d, p, *w, x, r, false, nullptr, 0, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
 }
 
-int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
-                      int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
+                        int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream,
+                        const StageEvents& se) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_E_INVAL;
@@ -216,10 +219,24 @@ int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_
   hipStream_t s = (hipStream_t)stream;
   uint32_t* zero_from = (uint32_t*)ws + p.c_gu;
   const size_t zero_count = p.n_counters - p.c_gu;
-  if (launch_route(*d, p, *w, x, r, zero_from, zero_count, s) != hipSuccess) return MOE_E_HIP;
-  hipError_t e = p.decode ? launch_decode_experts(*d, p, *w, x, r, ws, y, s)
-                          : launch_prefill_experts(*d, p, *w, x, r, ws, y, s);
+  se.record(0, s);
+  if (launch_route(*d, p, *w, x, r, true, zero_from, zero_count, s) != hipSuccess) return MOE_E_HIP;
+  hipError_t e = p.decode ? launch_decode_experts(*d, p, *w, x, r, ws, y, s, se)
+                          : launch_prefill_experts(*d, p, *w, x, r, ws, y, s, se);
   return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
+                      int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream) {
+  return forward_impl(d, w, x, T, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream, StageEvents{nullptr, 0});
+}
+
+int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
+                               uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
+                               void* stream, void* const* events, int32_t n_events) {
+  if (n_events < 0 || (n_events > 0 && !events)) return MOE_E_INVAL;
+  return forward_impl(d, w, x, T, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream,
+                      StageEvents{events, n_events});
 }
 
 const char* moe_status_string(int status) {

@@ -83,12 +83,21 @@ struct Plan {
   size_t sync_bytes;
   // byte offsets
   size_t z_off, idx_off, w_off, nu_off, ids_off, off_off, pairs_off;
-  size_t ucnt_off, ubase_off, tiles_off;
+  size_t ucnt_off, ubase_off, tiles_off, slots_off;
   size_t h_off, p_gu_off, p_dn_off;
   size_t total;
 };
 
 bool make_plan(const moe_dims_t& d, int T, Plan* p);
+
+// One expert slot of a call, written by the union step.  Slot 0 is the
+// shared expert when there is one; the routed union follows in ascending
+// expert order; slots past the realised union have n == 0.
+struct SlotEntry {
+  const uint8_t* base;  // packed expert
+  int32_t n;            // tokens using it
+  int32_t p0;           // first index into pairs, or -1 for the shared expert
+};
 
 // Device pointers resolved for one call.
 struct Route {
@@ -101,6 +110,7 @@ struct Route {
   int32_t* pairs;
   int32_t* ucnt;    // union: per-chunk counts
   int32_t* ubase;   // union: per-chunk bases
+  SlotEntry* slots; // [slots_max]
   uint32_t* counter;
 };
 
@@ -109,11 +119,56 @@ hipError_t launch_pack(const moe_dims_t& d, const void* qg, const void* sg, cons
                        const void* qd, const void* sd, const float* g3, void* out, hipStream_t s);
 hipError_t launch_unpack(const moe_dims_t& d, const void* packed, void* qg, void* sg, void* qu, void* su,
                          void* qd, void* sd, float* g3, hipStream_t s);
+// Routing and union.  With `with_slots`, also fills r.slots from w.experts
+// and w.shared (moe_w4a16_forward); moe_route passes false.
 hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
-                        const Route& r, uint32_t* zero_from, size_t zero_count, hipStream_t s);
+                        const Route& r, bool with_slots, uint32_t* zero_from, size_t zero_count, hipStream_t s);
+// Optional stage events (benchmark timing): ev[i] is recorded before stage
+// i and ev[n-1] after the last; null entries are skipped.
+struct StageEvents {
+  void* const* ev;
+  int n;
+  void record(int i, hipStream_t s) const {
+    if (ev && i < n && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
+  }
+};
+
 hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
-                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s);
+                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s,
+                                 const StageEvents& se);
 hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
-                                  const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s);
+                                  const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s,
+                                  const StageEvents& se);
+
+// ---------------------------------------------------------------------------
+// Cross-workgroup hand-off without L2 maintenance.  The per-XCD L2 caches are
+// not coherent with each other for ordinary stores, and a device-scope fence
+// writes back and invalidates the whole L2.  Data handed between workgroups
+// is therefore written and read with device-scope relaxed atomic accesses
+// (which the hardware keeps coherent), and a unit publishes its arrival only
+// after all of its stores have completed (s_waitcnt 0).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ void st_dev(T* p, T v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ T ld_dev(const T* p) {
+  return __hip_atomic_load(const_cast<T*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Called by every lane of a wavefront after its st_dev stores: returns the
+// counter value before this wavefront's increment (same on all lanes).
+__device__ __forceinline__ uint32_t publish_arrival(uint32_t* counter) {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0): our stores are done
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t prev = 0;
+  if ((threadIdx.x & 63) == 0)
+    prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  prev = __shfl(prev, 0, 64);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  return prev;
+}
 
 }  // namespace moe

@@ -26,6 +26,7 @@ namespace moe {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+constexpr int kMaxSplit = 8;  // largest split-K factor of the GEMV kernels
 // Global-address-space views, so weight loads compile to global_load (not
 // flat_load, which also occupies the LDS/scalar wait counter).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -34,8 +35,7 @@ typedef __attribute__((address_space(1))) const u32x4 guint4;
 typedef __attribute__((address_space(1))) const u32x2 guint2;
 
 struct GemvArgs {
-  const void* const* experts;
-  const void* shared;
+  const SlotEntry* slots;
   const int32_t* n_unique;
   const int32_t* uniq_ids;
   const int32_t* uniq_off;
@@ -119,6 +119,58 @@ __device__ __forceinline__ float dot8(half2_t p0, half2_t p1, half2_t p2, half2_
 //   sc: E2M1 only: this lane's 8 scale bytes of the first 4-chunk group of
 //      matrix 0; matrix m of group g is at sc + (g*NM + m)*64 (uint2 units).
 //   act[t]: wave-uniform activation rows, already offset to column 32*c0.
+template <int FMT, int NM, int U>
+__device__ __forceinline__ void load_batch(const guint4* __restrict__ w, const guint2* __restrict__ sc, int c,
+                                           u32x4 (&wv)[U][NM], u32x2 (&sv)[NM]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) wv[u][m] = __builtin_nontemporal_load(w + ((c + u) * NM + m) * 64);
+  if (FMT == MOE_W_E2M1_B16) {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) sv[m] = sc[((c / U) * NM + m) * 64];
+  }
+}
+
+template <int FMT, int NM, int NT, int U>
+__device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u32x2 (&sv)[NM], int c,
+                                              const uint4* const* act, const Int4Masks& mk, float (&acc)[NM][NT]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    uint4 xv[NT][4];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[t][i] = act[t][(c + u) * 4 + i];
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const uint32_t dw[4] = {wv[u][m].x, wv[u][m].y, wv[u][m].z, wv[u][m].w};
+      half2_t s0, s1;
+      if (FMT == MOE_W_E2M1_B16) {
+        const uint32_t sb = (u < 2) ? sv[m].x : sv[m].y;
+        s0 = e4m3_pair(sb, (u & 1) * 2);
+        s1 = e4m3_pair(sb, (u & 1) * 2 + 1);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        half2_t p0, p1, p2, p3;
+        if (FMT == MOE_W_INT4_ROW) dec_int4(dw[i], mk, p0, p1, p2, p3);
+        else dec_e2m1(dw[i], i < 2 ? s0 : s1, p0, p1, p2, p3);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[m][t] = dot8(p0, p1, p2, p3, xv[t][i], acc[m][t]);
+      }
+    }
+  }
+}
+
+// Streams `nch` chunks (a multiple of 4) for NM matrices (gate+up: NM=2) and
+// NT activation rows, keeping the next 4-chunk batch of weights in flight
+// while the current one is decoded and multiplied.
+//   w: this lane's 16 bytes in the first chunk of matrix 0; matrix m of
+//      chunk c is at w + (c*NM + m)*64 (uint4 units).
+//   sc: E2M1 only: this lane's 8 scale bytes of the first 4-chunk group of
+//      matrix 0; matrix m of group g is at sc + (g*NM + m)*64 (uint2 units).
+//   act[t]: wave-uniform activation rows, already offset to column 32*c0.
 template <int FMT, int NM, int NT>
 __device__ __forceinline__ void stream_chunks(const guint4* __restrict__ w, const guint2* __restrict__ sc,
                                               const uint4* const* act, int nch, float (&acc)[NM][NT]) {
@@ -127,50 +179,22 @@ __device__ __forceinline__ void stream_chunks(const guint4* __restrict__ w, cons
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
-  constexpr int U = 4;  // chunks per step (one E2M1 scale group)
-  for (int c = 0; c < nch; c += U) {
-    u32x4 wv[U][NM];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int m = 0; m < NM; ++m) wv[u][m] = w[((c + u) * NM + m) * 64];
-    u32x2 sv[NM];
-    if (FMT == MOE_W_E2M1_B16) {
-#pragma unroll
-      for (int m = 0; m < NM; ++m) sv[m] = sc[((c / U) * NM + m) * 64];
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      uint4 xv[NT][4];
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) xv[t][i] = act[t][(c + u) * 4 + i];
-#pragma unroll
-      for (int m = 0; m < NM; ++m) {
-        const uint32_t dw[4] = {wv[u][m].x, wv[u][m].y, wv[u][m].z, wv[u][m].w};
-        half2_t s0, s1;
-        if (FMT == MOE_W_E2M1_B16) {
-          const uint32_t sb = (u < 2) ? sv[m].x : sv[m].y;
-          s0 = e4m3_pair(sb, (u & 1) * 2);
-          s1 = e4m3_pair(sb, (u & 1) * 2 + 1);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          half2_t p0, p1, p2, p3;
-          if (FMT == MOE_W_INT4_ROW) dec_int4(dw[i], mk, p0, p1, p2, p3);
-          else dec_e2m1(dw[i], i < 2 ? s0 : s1, p0, p1, p2, p3);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) acc[m][t] = dot8(p0, p1, p2, p3, xv[t][i], acc[m][t]);
-        }
-      }
-    }
+  constexpr int U = 4;  // chunks per batch (one E2M1 scale group)
+  u32x4 wa[U][NM], wb[U][NM];
+  u32x2 sa[NM], sb[NM];
+  load_batch<FMT, NM, U>(w, sc, 0, wa, sa);
+  for (int c = 0; c < nch; c += 2 * U) {
+    const bool has_b = c + U < nch;
+    if (has_b) load_batch<FMT, NM, U>(w, sc, c + U, wb, sb);
+    compute_batch<FMT, NM, NT, U>(wa, sa, c, act, mk, acc);
+    if (!has_b) break;
+    if (c + 2 * U < nch) load_batch<FMT, NM, U>(w, sc, c + 2 * U, wa, sa);
+    compute_batch<FMT, NM, NT, U>(wb, sb, c + U, act, mk, acc);
   }
 }
 
-// Resolves the expert and token list of a slot.  Slot 0 is the shared
-// expert when S == 1; the others are the union slots in ascending expert
-// order.  Returns false when the slot is past the realised union.
+// Expert and token list of a slot, from the slot table the union step
+// wrote: one 16-byte wave-uniform load.  Returns false for unused slots.
 struct SlotInfo {
   const uint8_t* base;
   int n;            // tokens
@@ -178,18 +202,11 @@ struct SlotInfo {
 };
 
 __device__ __forceinline__ bool resolve_slot(const GemvArgs& a, int slot, SlotInfo& si) {
-  if (a.S && slot == 0) {
-    si.base = (const uint8_t*)a.shared;
-    si.n = a.T;
-    si.p0 = -1;
-    return true;
-  }
-  const int u = slot - a.S;
-  if (u >= *a.n_unique) return false;
-  si.base = (const uint8_t*)a.experts[a.uniq_ids[u]];
-  si.p0 = a.uniq_off[u];
-  si.n = a.uniq_off[u + 1] - si.p0;
-  return true;
+  const SlotEntry e = a.slots[slot];
+  si.base = e.base;
+  si.n = e.n;
+  si.p0 = e.p0;
+  return si.n > 0;
 }
 
 // Token index and output row (pair id, or T*k + t for the shared expert) of
@@ -207,16 +224,12 @@ __device__ __forceinline__ void slot_token(const GemvArgs& a, const SlotInfo& si
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
-// Releases this unit's partial stores and reports whether it is the last of
-// `total` units of its group.
+// Publishes this unit's partial stores and reports whether it is the last of
+// `total` units of its group; the last one resets the counter for the next
+// call.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total) {
-  __threadfence();
-  uint32_t prev = 0;
-  if ((threadIdx.x & 63) == 0) prev = atomicAdd(counter, 1u);
-  prev = __shfl(prev, 0, 64);
-  if (prev != total - 1) return false;
-  __threadfence();
-  if ((threadIdx.x & 63) == 0) *counter = 0;  // leave it zero for the next call
+  if (publish_arrival(counter) != total - 1) return false;
+  if ((threadIdx.x & 63) == 0) st_dev(counter, 0u);
   return true;
 }
 
@@ -243,8 +256,8 @@ __device__ void gu_tile(const GemvArgs& a, const SlotInfo& si, int rb, int c0, i
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     float* pr = a.part + (((size_t)ks * a.rows_total + rows[t]) * 2) * a.I + 64 * rb + lane;
-    pr[0] = acc[0][t];
-    pr[a.I] = acc[1][t];
+    st_dev(pr, acc[0][t]);
+    st_dev(pr + a.I, acc[1][t]);
   }
 }
 
@@ -268,7 +281,7 @@ __device__ void dn_tile(const GemvArgs& a, const SlotInfo& si, int rb, int c0, i
   stream_chunks<FMT, 1, NT>(w, sc, act, a.cpu, acc);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
-    a.part[((size_t)ks * a.rows_total + rows[t]) * a.H + 64 * rb + lane] = acc[0][t] * scale;
+    st_dev(a.part + ((size_t)ks * a.rows_total + rows[t]) * a.H + 64 * rb + lane, acc[0][t] * scale);
 }
 
 // Grid: x = (I/64) * ks units of (row block, K-segment); y = expert slots.
@@ -305,11 +318,23 @@ __global__ __launch_bounds__(64) void k_gu_gemv(GemvArgs a, const uint16_t* __re
   for (int i = 0; i < si.n; ++i) {
     int tok, row;
     slot_token(a, si, i, tok, row);
+    // issue every partial load before summing (they are independent)
+    float pg[kMaxSplit], pu[kMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      if (s < a.ks) {
+        const float* pr = a.part + (((size_t)s * a.rows_total + row) * 2) * a.I + r;
+        pg[s] = ld_dev(pr);
+        pu[s] = ld_dev(pr + a.I);
+      }
+    }
     float g = 0.f, u = 0.f;
-    for (int s = 0; s < a.ks; ++s) {
-      const float* pr = a.part + (((size_t)s * a.rows_total + row) * 2) * a.I + r;
-      g += pr[0];
-      u += pr[a.I];
+#pragma unroll
+    for (int s = 0; s < kMaxSplit; ++s) {
+      if (s < a.ks) {
+        g += pg[s];
+        u += pu[s];
+      }
     }
     g *= sg;
     u *= su;
@@ -347,17 +372,27 @@ __global__ __launch_bounds__(64) void k_dn_gemv(GemvArgs a) {
   // slot order, each o summed over K-segments in order.
   for (int t = 0; t < a.T; ++t) {
     float acc = 0.f;
-    for (int j = 0; j < a.k; ++j) {
-      const int row = t * a.k + j;
-      float o = 0.f;
-      for (int s = 0; s < a.ks; ++s) o += a.part[((size_t)s * a.rows_total + row) * a.H + r];
-      acc += a.topk_w[row] * o;
-    }
-    if (a.S) {
-      const int row = a.T * a.k + t;
-      float o = 0.f;
-      for (int s = 0; s < a.ks; ++s) o += a.part[((size_t)s * a.rows_total + row) * a.H + r];
-      acc += o;
+    for (int j0 = 0; j0 < a.k + a.S; j0 += 8) {
+      // up to 8 slots' partials in flight at once, summed in slot order
+      float o[8][kMaxSplit];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const int row = (j < a.k) ? t * a.k + j : a.T * a.k + t;
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+          if (j < a.k + a.S && s < a.ks) o[jj][s] = ld_dev(a.part + ((size_t)s * a.rows_total + row) * a.H + r);
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        if (j >= a.k + a.S) break;
+        float v = 0.f;
+#pragma unroll
+        for (int s = 0; s < kMaxSplit; ++s)
+          if (s < a.ks) v += o[jj][s];
+        acc += (j < a.k) ? a.topk_w[t * a.k + j] * v : v;
+      }
     }
     a.y[(size_t)t * a.H + r] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
@@ -366,10 +401,10 @@ __global__ __launch_bounds__(64) void k_dn_gemv(GemvArgs a) {
 }  // namespace
 
 hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
-                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s) {
+                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s,
+                                 const StageEvents& se) {
   GemvArgs a{};
-  a.experts = w.experts;
-  a.shared = w.shared;
+  a.slots = r.slots;
   a.n_unique = r.n_unique;
   a.uniq_ids = r.uniq_ids;
   a.uniq_off = r.uniq_off;
@@ -391,6 +426,7 @@ hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_w
   a.ks = p.ks_gu;
   a.cpu = (p.H / 32) / p.ks_gu;
   dim3 g1((unsigned)((p.I / 64) * p.ks_gu), (unsigned)p.slots_max);
+  se.record(1, s);
   if (d.wfmt == MOE_W_INT4_ROW) hipLaunchKernelGGL(k_gu_gemv<MOE_W_INT4_ROW>, g1, dim3(64), 0, s, a, x);
   else hipLaunchKernelGGL(k_gu_gemv<MOE_W_E2M1_B16>, g1, dim3(64), 0, s, a, x);
   hipError_t e = hipGetLastError();
@@ -401,9 +437,12 @@ hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_w
   a.ks = p.ks_dn;
   a.cpu = (p.I / 32) / p.ks_dn;
   dim3 g2((unsigned)((p.H / 64) * p.ks_dn), (unsigned)p.slots_max);
+  se.record(2, s);
   if (d.wfmt == MOE_W_INT4_ROW) hipLaunchKernelGGL(k_dn_gemv<MOE_W_INT4_ROW>, g2, dim3(64), 0, s, a);
   else hipLaunchKernelGGL(k_dn_gemv<MOE_W_E2M1_B16>, g2, dim3(64), 0, s, a);
-  return hipGetLastError();
+  e = hipGetLastError();
+  se.record(3, s);
+  return e;
 }
 
 }  // namespace moe

@@ -179,3 +179,31 @@ def test_workspace_reuse_across_T():
         torch.cuda.synchronize()
         assert_close(y, oracle.forward(layer, x), f"T={T}")
     assert torch.count_nonzero(ws[: moe.moe_workspace_sync_bytes(dims)]) == 0
+
+
+def test_graph_replays_match_eager():
+    """The forward call captured in a HIP graph: every replay (with eager
+    work and synchronisation in between) equals the eager result bitwise."""
+    dims = synth.Dims(1024, 256, 64, 4, 1, 0)
+    layer = synth.make_layer(dims, "graph")
+    pl = moe.PackedLayer.from_layer(layer)
+    x = synth.make_tokens(dims, 3, "graph").to(DEV)
+    ws = moe.workspace(dims, 3, DEV)
+    y_eager = moe.moe_w4a16_forward(pl, x, ws=ws).clone()
+    y = torch.empty_like(y_eager)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.moe_w4a16_forward(pl, x, y=y, ws=ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_w4a16_forward(pl, x, y=y, ws=ws)
+    for i in range(5):
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), f"replay {i}"
+        moe.moe_w4a16_forward(pl, x[:1].contiguous(), ws=ws)  # eager work in between
+        torch.cuda.synchronize()
