@@ -71,7 +71,8 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   const size_t nch = ((size_t)T + 31) / 32;
   q.ucnt_off = off; off = up256(off + nch * q.E * 4);
   q.ubase_off = off; off = up256(off + nch * q.E * 4);
-  q.tiles_off = off; off = up256(off + (Tk / 16 + q.E + T / 16 + 4) * 8);
+  q.tiles_off = off; off = up256(off + (size_t)prefill_max_tiles(T, q.k, q.E, q.S) * 8);
+  q.ntiles_off = off; off = up256(off + 4);
   q.slots_off = off; off = up256(off + (size_t)q.slots_max * sizeof(SlotEntry));
   q.h_off = off; off = up256(off + (size_t)q.rows_total * q.I * 2);
   if (q.decode) {
@@ -105,6 +106,8 @@ Route route_ptrs(const Plan& p, void* ws) {
   r.ucnt = (int32_t*)(b + p.ucnt_off);
   r.ubase = (int32_t*)(b + p.ubase_off);
   r.slots = (SlotEntry*)(b + p.slots_off);
+  r.tiles = (int32_t*)(b + p.tiles_off);
+  r.n_tiles = (int32_t*)(b + p.ntiles_off);
   r.counter = (uint32_t*)ws + p.c_route;
   return r;
 }

@@ -71,6 +71,15 @@ constexpr int kDecodeMaxTokens = 16;   // GEMV path for T <= this
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 constexpr int kRouteSmallMaxTokens = 16;
+constexpr int kPrefillTileRows = 64;   // tokens per grouped-GEMM tile
+
+// Upper bound on grouped-GEMM tiles (slot, first token) for T tokens.
+inline int prefill_max_tiles(int T, int k, int E, int S) {
+  const long P = (long)T * k;
+  const long U = P < E ? P : E;
+  const long B = kPrefillTileRows;
+  return (int)((S ? (T + B - 1) / B : 0) + (P + B - 1) / B + U);
+}
 
 struct Plan {
   int T, H, I, E, k, S;      // S = has_shared
@@ -83,7 +92,7 @@ struct Plan {
   size_t sync_bytes;
   // byte offsets
   size_t z_off, idx_off, w_off, nu_off, ids_off, off_off, pairs_off;
-  size_t ucnt_off, ubase_off, tiles_off, slots_off;
+  size_t ucnt_off, ubase_off, tiles_off, ntiles_off, slots_off;
   size_t h_off, p_gu_off, p_dn_off;
   size_t total;
 };
@@ -111,6 +120,8 @@ struct Route {
   int32_t* ucnt;    // union: per-chunk counts
   int32_t* ubase;   // union: per-chunk bases
   SlotEntry* slots; // [slots_max]
+  int32_t* tiles;   // [max tiles][2]: (slot, first token) of each grouped-GEMM tile
+  int32_t* n_tiles; // [1]
   uint32_t* counter;
 };
 

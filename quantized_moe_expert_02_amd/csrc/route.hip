@@ -39,8 +39,10 @@ struct RouteArgs {
   uint32_t* zero_from;
   int zero_count;
   int n_chunks;
-  // slot table (forward only)
+  // slot table and grouped-GEMM tile list (forward only)
   SlotEntry* slots;
+  int32_t* tiles;
+  int32_t* n_tiles;
   int slots_max;
   const void* const* experts;
   const void* shared;
@@ -475,6 +477,27 @@ __global__ __launch_bounds__(1024) void k_union_scan(RouteArgs a) {
     a.uniq_off[nu] = off;
     s_prs[0] = nu;
     if (a.slots && a.S) write_slot(a, 0, -1, a.T, -1);
+    if (a.tiles) {
+      // grouped-GEMM tiles: shared expert first, then the union in order
+      int nt = 0;
+      if (a.S)
+        for (int m0 = 0; m0 < a.T; m0 += kPrefillTileRows) {
+          a.tiles[2 * nt] = 0;
+          a.tiles[2 * nt + 1] = m0;
+          ++nt;
+        }
+      int u = 0;
+      for (int e = 0; e < a.E; ++e) {
+        if (s_tot[e] == 0) continue;
+        for (int m0 = 0; m0 < s_tot[e]; m0 += kPrefillTileRows) {
+          a.tiles[2 * nt] = a.S + u;
+          a.tiles[2 * nt + 1] = m0;
+          ++nt;
+        }
+        ++u;
+      }
+      *a.n_tiles = nt;
+    }
   }
   __syncthreads();
   if (a.slots)
@@ -542,6 +565,8 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
   a.n_chunks = (p.T + 31) / 32;
   a.S = p.S;
   a.slots = with_slots ? r.slots : nullptr;
+  a.tiles = with_slots ? r.tiles : nullptr;
+  a.n_tiles = r.n_tiles;
   a.slots_max = p.slots_max;
   a.experts = w.experts;
   a.shared = w.shared;
