@@ -61,7 +61,8 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   size_t off = q.sync_bytes;
   const size_t Tk = (size_t)T * q.k;
   const size_t cap = std::max<size_t>(1, std::min<size_t>(q.E, Tk));
-  q.z_off = off; off = up256(off + (size_t)T * q.E * 8);
+  // z plus, for large batches, the K-split partial logits
+  q.z_off = off; off = up256(off + (size_t)T * q.E * 8 * (q.decode ? 1 : 5));
   q.idx_off = off; off = up256(off + Tk * 4);
   q.w_off = off; off = up256(off + Tk * 4);
   q.nu_off = off; off = up256(off + 4);

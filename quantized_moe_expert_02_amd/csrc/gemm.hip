@@ -3,16 +3,18 @@
 //
 // Each unique expert is applied to all of its tokens at once (the batch-wise
 // MoE union, "Show HN: 低速のコンピュータでGLM 5.2を動かす方法", hakusoku.com,
-// section 実装済み機能); its 4-bit weights are decoded once per tile into LDS
-// as exact binary16 values (int4 codes are small integers; e2m1 x e4m3 has at
-// most 6 significant bits) and multiplied on v_mfma_f32_16x16x32_f16 with
-// fp32 accumulation.  Row scales (int4) or the tensor scale (e2m1) are applied
+// section 実装済み機能); its 4-bit weights are decoded in registers, straight
+// into matrix-core operands, as exact binary16 values (int4 codes are small
+// integers; e2m1 x e4m3 has at most 6 significant bits) -- the in-register
+// decode of the Ornith engine ("GTX 1070向け35BパラメータMoEモデル推論エンジン公開",
+// section "VRAMとシステムメモリで重みを分割する設計") -- and multiplied on
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  Row scales (int4) or the tensor scale (e2m1) are applied
 // in the epilogue, as is the SwiGLU.
 //
-//   k_gu_gemm:  tile = 64 tokens of one expert x 64 gate rows + 64 up rows
-//               -> h (binary16, one row per (token, slot) pair)
-//   k_dn_gemm:  tile = 64 tokens x 128 down rows -> per-pair fp32 outputs,
-//               already multiplied by the pair's routing weight
+//   k_expert_gemm<.., 2>:  tile = 64 tokens of one expert x 512 gate rows +
+//                          512 up rows -> h (binary16, one row per pair)
+//   k_expert_gemm<.., 1>:  tile = 64 tokens x 512 down rows -> per-pair fp32
+//                          outputs, already multiplied by the routing weight
 //   k_combine:  y[t] = sum over slots j (in slot order) + shared -> binary16
 #include "common.h"
 
@@ -26,8 +28,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 guint4;
 
 constexpr int BM = kPrefillTileRows;  // tokens per tile
-constexpr int BK = 64;    // columns per K step (two 32-column chunks)
-constexpr int LDS_PITCH = BK + 8;  // halves per LDS row (16-byte pad against bank conflicts)
+constexpr int XP = 40;                // halves per LDS token row (32 + 8 pad)
 
 struct GemmArgs {
   const SlotEntry* slots;
@@ -47,7 +48,7 @@ struct GemmArgs {
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
 // int4 (device order, offset binary) -> 8 consecutive binary16 values.
-__device__ __forceinline__ u32x4 dequant_int4(uint32_t d) {
+__device__ __forceinline__ half8_t dequant_int4(uint32_t d) {
   const half2_t k1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t d8 = d >> 8;
@@ -55,18 +56,16 @@ __device__ __forceinline__ u32x4 dequant_int4(uint32_t d) {
   const half2_t p1 = as_h2((d & 0x00F000F0u) | 0x54005400u) + k72;
   const half2_t p2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + k1032;
   const half2_t p3 = as_h2((d8 & 0x00F000F0u) | 0x54005400u) + k72;
-  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
-               __builtin_bit_cast(uint32_t, p3)};
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
-// e2m1 codes (byte b = columns 2b, 2b+1) times the block scale -> 8 binary16.
-__device__ __forceinline__ u32x4 dequant_e2m1(uint32_t d, half2_t s) {
+// e2m1 codes (byte b = columns 2b, 2b+1) times a block scale -> 8 binary16.
+__device__ __forceinline__ half8_t dequant_e2m1(uint32_t d, half2_t s) {
   const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 0) * s;
   const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 1) * s;
   const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 2) * s;
   const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(d, 1.0f, 3) * s;
-  return u32x4{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1), __builtin_bit_cast(uint32_t, p2),
-               __builtin_bit_cast(uint32_t, p3)};
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 __device__ __forceinline__ half2_t e4m3_half2(uint32_t byte) {
@@ -74,34 +73,47 @@ __device__ __forceinline__ half2_t e4m3_half2(uint32_t byte) {
   return half2_t{h, h};
 }
 
-// Decodes this lane's 16 bytes of a 64-row x 32-column block (row `lane`) and
-// stores the 32 binary16 values to LDS row `lane` at column offset `col`.
-// E2M1: `sbytes` holds the row's two block scales of this chunk.
-template <int FMT>
-__device__ __forceinline__ void decode_to_lds(u32x4 w, uint32_t sbytes, _Float16* lds_row, int col) {
-  u32x4 o[4];
-  if (FMT == MOE_W_INT4_ROW) {
-    o[0] = dequant_int4(w.x);
-    o[1] = dequant_int4(w.y);
-    o[2] = dequant_int4(w.z);
-    o[3] = dequant_int4(w.w);
-  } else {
-    const half2_t s0 = e4m3_half2(sbytes & 0xFF), s1 = e4m3_half2((sbytes >> 8) & 0xFF);
-    o[0] = dequant_e2m1(w.x, s0);
-    o[1] = dequant_e2m1(w.y, s0);
-    o[2] = dequant_e2m1(w.z, s1);
-    o[3] = dequant_e2m1(w.w, s1);
-  }
-  u32x4* dst = reinterpret_cast<u32x4*>(lds_row + col);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = o[i];
+// 4x4 transpose across the lane groups {n, 16+n, 32+n, 48+n} and the four
+// dwords: afterwards lane 16a+n dword b holds what lane 16b+n dword a held.
+// Two v_permlane32_swap (exchange of the upper half's first operand with the
+// lower half's second) then two v_permlane16_swap (odd rows' first operand
+// with even rows' second).
+__device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t& d2, uint32_t& d3) {
+  auto r02 = __builtin_amdgcn_permlane32_swap(d0, d2, false, false);
+  auto r13 = __builtin_amdgcn_permlane32_swap(d1, d3, false, false);
+  d0 = r02[0];
+  d2 = r02[1];
+  d1 = r13[0];
+  d3 = r13[1];
+  auto r01 = __builtin_amdgcn_permlane16_swap(d0, d1, false, false);
+  auto r23 = __builtin_amdgcn_permlane16_swap(d2, d3, false, false);
+  d0 = r01[0];
+  d1 = r01[1];
+  d2 = r23[0];
+  d3 = r23[1];
 }
 
-// E2M1 block-scale bytes of chunk c for row `lane`: two bytes of the lane's
-// 8-byte group (see the packed layout).
-__device__ __forceinline__ uint32_t e2m1_scale_pair(const uint8_t* sregion, size_t group_idx, int lane, int c) {
-  const uint8_t* p = sregion + (group_idx * 64 + lane) * 8 + 2 * (c & 3);
-  return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+// One packed 64-row x 32-column block in a wavefront (lane l: row l, dword b =
+// columns 8b..8b+7) -> the B operands of four v_mfma_f32_16x16x32_f16, one per
+// 16-row group q: lane 16g+n receives row 16q+n, columns 8g..8g+7.
+// E2M1: `sc` holds this lane's two block-scale bytes (columns 0-15, 16-31).
+template <int FMT>
+__device__ __forceinline__ void block_to_operands(u32x4 w, uint32_t sc, half8_t (&b)[4]) {
+  uint32_t d0 = w.x, d1 = w.y, d2 = w.z, d3 = w.w;
+  transpose4(d0, d1, d2, d3);
+  if (FMT == MOE_W_INT4_ROW) {
+    b[0] = dequant_int4(d0);
+    b[1] = dequant_int4(d1);
+    b[2] = dequant_int4(d2);
+    b[3] = dequant_int4(d3);
+  } else {
+    uint32_t t0 = sc & 0xFF, t1 = sc & 0xFF, t2 = (sc >> 8) & 0xFF, t3 = (sc >> 8) & 0xFF;
+    transpose4(t0, t1, t2, t3);
+    b[0] = dequant_e2m1(d0, e4m3_half2(t0));
+    b[1] = dequant_e2m1(d1, e4m3_half2(t1));
+    b[2] = dequant_e2m1(d2, e4m3_half2(t2));
+    b[3] = dequant_e2m1(d3, e4m3_half2(t3));
+  }
 }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
@@ -121,173 +133,183 @@ __device__ __forceinline__ bool tile_token(const GemmArgs& a, const SlotEntry& s
   return true;
 }
 
-// Gate/up: grid (I/64, max tiles); 256 threads = 4 waves; wave w owns gate
-// and up rows 16w..16w+15 of the row block, all 64 tokens of the tile.
-template <int FMT>
-__global__ __launch_bounds__(256) void k_gu_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 sx[BM][LDS_PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 sw[2][64][LDS_PITCH];
-  __shared__ int s_act[BM], s_out[BM];
-  const int tile = blockIdx.y;
-  if (tile >= *a.n_tiles) return;
-  const int slot = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
-  const SlotEntry se = a.slots[slot];
-  const int rb = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid & 63;
-  if (tid < BM) {
-    int ar = -1, orow = -1;
-    if (!tile_token(a, se, m0 + tid, ar, orow)) ar = -1;
-    s_act[tid] = ar;
-    s_out[tid] = orow;
-  }
-  __syncthreads();
-  const int n_ch = a.H / 32;
-  const guint4* wbase = (const guint4*)(se.base + a.L.gu_off) + (size_t)rb * n_ch * 2 * 64 + lane;
-  const uint8_t* sregion = se.base + a.L.sgu_off;
-  f32x4 acc_g[4], acc_u[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc_g[i] = acc_u[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.H; k0 += BK) {
-    // weights: wave w decodes chunk (k0/32 + w/2) of matrix w%2 (gate 0, up 1)
-    {
-      const int c = k0 / 32 + (wave >> 1), m = wave & 1;
-      const u32x4 wv = __builtin_nontemporal_load(wbase + ((size_t)c * 2 + m) * 64);
-      uint32_t sb = 0;
-      if (FMT == MOE_W_E2M1_B16)
-        sb = e2m1_scale_pair(sregion, ((size_t)rb * (a.H / 128) + c / 4) * 2 + m, lane, c);
-      decode_to_lds<FMT>(wv, sb, &sw[m][lane][0], 32 * (wave >> 1));
-    }
-    // activations: 64 tokens x 64 columns, 16 bytes per thread x 2
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int idx = tid + 256 * r;  // 0..511
-      const int m = idx >> 3, q = idx & 7;
-      const int ar = s_act[m];
-      u32x4 v = {0, 0, 0, 0};
-      if (ar >= 0) v = *reinterpret_cast<const u32x4*>(a.x + (size_t)ar * a.H + k0 + 8 * q);
-      *reinterpret_cast<u32x4*>(&sx[m][8 * q]) = v;
-    }
-    __syncthreads();
-    const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      const half8_t bg = *reinterpret_cast<const half8_t*>(&sw[0][16 * wave + n][kk + 8 * g]);
-      const half8_t bu = *reinterpret_cast<const half8_t*>(&sw[1][16 * wave + n][kk + 8 * g]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const half8_t av = *reinterpret_cast<const half8_t*>(&sx[16 * mt + n][kk + 8 * g]);
-        acc_g[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bg, acc_g[mt], 0, 0, 0);
-        acc_u[mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bu, acc_u[mt], 0, 0, 0);
-      }
-    }
-    __syncthreads();
-  }
-  // epilogue: lane holds tokens 16 mt + 4 g + i for weight row 16 wave + n
-  const int n = lane & 15, g = lane >> 4;
-  const int row = rb * 64 + 16 * wave + n;
-  float sgv, suv;
-  if (FMT == MOE_W_INT4_ROW) {
-    sgv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sg_off)[row]);
-    suv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.su_off)[row]);
-  } else {
-    const float* g3 = reinterpret_cast<const float*>(se.base + a.L.g3_off);
-    sgv = g3[0];
-    suv = g3[1];
-  }
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int m = 16 * mt + 4 * g + i;
-      const int orow = s_out[m];
-      if (s_act[m] < 0) continue;
-      const float gv = acc_g[mt][i] * sgv, uv = acc_u[mt][i] * suv;
-      a.h[(size_t)orow * a.I + row] = __builtin_bit_cast(uint16_t, (_Float16)(silu(gv) * uv));
-    }
-  }
-}
+// Grouped GEMM over one tile of BM tokens of one expert.  512 threads = 8
+// wavefronts; wavefront w owns the 64-row block rb = 8*group + w of each
+// of the NM matrices (gate and up for NM = 2, down for NM = 1) and all BM
+// tokens.  Per 32-column slice: each wavefront streams its NM weight blocks
+// (one 128-bit load per lane each) and decodes them into MFMA operands in
+// registers; the tile's activation rows (gathered by token) pass through a
+// double-buffered LDS slice shared by the eight wavefronts.
+//   NM == 2: K = H, activations x, epilogue: row scales, SwiGLU -> h.
+//   NM == 1: K = I, activations h, epilogue: row scale, routing weight -> part.
+constexpr int kGemmWaves = 8;  // wavefronts per workgroup, 64 rows each
 
-// Down: grid (H/128, max tiles); 256 threads = 4 waves; wave w owns down rows
-// 32w..32w+31 of the 128-row tile (two 64-row blocks), all 64 tokens.
-template <int FMT>
-__global__ __launch_bounds__(256) void k_dn_gemm(GemmArgs a) {
-  __shared__ __attribute__((aligned(16))) _Float16 sx[BM][LDS_PITCH];
-  __shared__ __attribute__((aligned(16))) _Float16 sw[128][LDS_PITCH];
-  __shared__ int s_out[BM];
+template <int FMT, int NM>
+__global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int nx) {
+  __shared__ __attribute__((aligned(16))) _Float16 sx[2][BM][XP];
+  __shared__ int s_act[BM], s_out[BM];
   __shared__ float s_w[BM];
-  const int tile = blockIdx.y;
+  // XCD-aware order: workgroups are spread round-robin over the 8 XCDs, so
+  // map block b to tile 8*(l/nx) + b%8 and row group l%nx with l = b/8: all
+  // row groups of one token tile run on one XCD and share its L2 copy of the
+  // tile's activations.
+  const int bid = blockIdx.x, xcd = bid & 7, loc = bid >> 3;
+  const int tile = 8 * (loc / nx) + xcd;
+  const int ngrp = loc % nx;
   if (tile >= *a.n_tiles) return;
   const int slot = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
   const SlotEntry se = a.slots[slot];
-  const int nb = blockIdx.x;  // 128-row tile
-  const int tid = threadIdx.x, wave = tid / 64, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int K = (NM == 2) ? a.H : a.I;
+  const int R = (NM == 2) ? a.I : a.H;  // rows per matrix
+  const int rb = ngrp * kGemmWaves + wave;
+  const bool active = rb * 64 < R;
   if (tid < BM) {
     int ar = -1, orow = -1;
     const bool ok = tile_token(a, se, m0 + tid, ar, orow);
+    s_act[tid] = ok ? (NM == 2 ? ar : orow) : -1;  // activation row (x row, or h row = output row of GU)
     s_out[tid] = ok ? orow : -1;
     s_w[tid] = ok ? (se.p0 < 0 ? 1.0f : a.topk_w[orow]) : 0.0f;
   }
   __syncthreads();
-  const int n_ch = a.I / 32;
-  const guint4* wbase = (const guint4*)(se.base + a.L.d_off) + lane;
-  const uint8_t* sregion = se.base + a.L.sdd_off;
-  f32x4 acc[2][4];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[j][i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k0 = 0; k0 < a.I; k0 += BK) {
-    // weights: wave w decodes row block (2 nb + w/2), chunk (k0/32 + w%2)
-    {
-      const int rb = 2 * nb + (wave >> 1), c = k0 / 32 + (wave & 1);
-      const u32x4 wv = __builtin_nontemporal_load(wbase + ((size_t)rb * n_ch + c) * 64);
-      uint32_t sb = 0;
-      if (FMT == MOE_W_E2M1_B16) sb = e2m1_scale_pair(sregion, (size_t)rb * (a.I / 128) + c / 4, lane, c);
-      decode_to_lds<FMT>(wv, sb, &sw[64 * (wave >> 1) + lane][0], 32 * (wave & 1));
-    }
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-      const int idx = tid + 256 * r;
-      const int m = idx >> 3, q = idx & 7;
-      const int orow = s_out[m];
-      u32x4 v = {0, 0, 0, 0};
-      if (orow >= 0) v = *reinterpret_cast<const u32x4*>(a.h + (size_t)orow * a.I + k0 + 8 * q);
-      *reinterpret_cast<u32x4*>(&sx[m][8 * q]) = v;
-    }
-    __syncthreads();
-    const int n = lane & 15, g = lane >> 4;
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
-      half8_t b[2];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = *reinterpret_cast<const half8_t*>(&sw[32 * wave + 16 * j + n][kk + 8 * g]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const half8_t av = *reinterpret_cast<const half8_t*>(&sx[16 * mt + n][kk + 8 * g]);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, b[j], acc[j][mt], 0, 0, 0);
-      }
-    }
-    __syncthreads();
+  const uint16_t* act = (NM == 2) ? a.x : a.h;
+  const int nch = K / 32;
+  // this thread's 16-byte share of an activation slice: token tid/4, columns
+  // 8*(tid%4) (threads 0..255; the others only compute)
+  const bool xload = tid < 4 * BM;
+  const int xm = (tid >> 2) & (BM - 1), xq = tid & 3;
+  const int xrow = xload ? s_act[xm] : -1;
+  const uint16_t* xsrc = act + (size_t)(xrow < 0 ? 0 : xrow) * K + 8 * xq;
+  // weights: lane's 16 bytes of block (rb, chunk c) of matrix m
+  const guint4* wsrc;
+  const uint8_t* ssrc = nullptr;
+  if (NM == 2) {
+    wsrc = (const guint4*)(se.base + a.L.gu_off) + (size_t)rb * nch * 2 * 64 + lane;
+    if (FMT == MOE_W_E2M1_B16) ssrc = se.base + a.L.sgu_off + ((size_t)rb * (K / 128) * 2 * 64 + lane) * 8;
+  } else {
+    wsrc = (const guint4*)(se.base + a.L.d_off) + (size_t)rb * nch * 64 + lane;
+    if (FMT == MOE_W_E2M1_B16) ssrc = se.base + a.L.sdd_off + ((size_t)rb * (K / 128) * 64 + lane) * 8;
   }
-  const int n = lane & 15, g = lane >> 4;
+  auto load_w = [&](int c, int m) -> u32x4 {
+    return __builtin_nontemporal_load(wsrc + ((size_t)c * NM + m) * 64);
+  };
+  auto load_s = [&](int c, int m) -> uint32_t {
+    const uint8_t* p = ssrc + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3);
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
+  };
+  auto load_x = [&](int c) -> u32x4 {
+    return xrow < 0 ? u32x4{0, 0, 0, 0} : *reinterpret_cast<const u32x4*>(xsrc + 32 * c);
+  };
+
+  f32x4 acc[NM][4][4];  // [matrix][row group q][token group mt]
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int row = nb * 128 + 32 * wave + 16 * j + n;
-    float sd;
-    if (FMT == MOE_W_INT4_ROW)
-      sd = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sd_off)[row]);
-    else
-      sd = reinterpret_cast<const float*>(se.base + a.L.g3_off)[2];
+  for (int m = 0; m < NM; ++m)
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int m = 16 * mt + 4 * g + i;
-        const int orow = s_out[m];
-        if (orow < 0) continue;
-        a.part[(size_t)orow * a.H + row] = s_w[m] * (sd * acc[j][mt][i]);
+      for (int mt = 0; mt < 4; ++mt) acc[m][q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Weights stream through a ring of kDepth register slices (loads issued
+  // kDepth slices ahead); activations through a double-buffered LDS slice.
+  constexpr int kDepth = 6;
+  u32x4 ring[kDepth][NM];
+  uint32_t sring[kDepth][NM];
+#pragma unroll
+  for (int j = 0; j < kDepth; ++j)
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      sring[j][m] = 0;
+      if (active && j < nch) {
+        ring[j][m] = load_w(j, m);
+        if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(j, m);
       }
+    }
+  // activation slices: register ring kXDepth deep feeding the LDS double buffer
+  constexpr int kXDepth = 2;
+  u32x4 xring[kXDepth];
+#pragma unroll
+  for (int j = 0; j < kXDepth; ++j) xring[j] = (j + 1 < nch) ? load_x(j + 1) : u32x4{0, 0, 0, 0};
+  if (xload) *reinterpret_cast<u32x4*>(&sx[0][xm][8 * xq]) = load_x(0);
+  __syncthreads();
+  const int n = lane & 15, g = lane >> 4;
+  for (int c0 = 0; c0 < nch; c0 += kDepth) {
+#pragma unroll
+    for (int j = 0; j < kDepth; ++j) {
+      const int c = c0 + j;
+      if (c >= nch) break;
+      // slice c+1 sits in xring[j % kXDepth]; refill it with slice c+1+kXDepth
+      const u32x4 xn = xring[j % kXDepth];
+      if (c + 1 + kXDepth < nch) xring[j % kXDepth] = load_x(c + 1 + kXDepth);
+      if (active) {
+        u32x4 wv[NM];
+        uint32_t sv[NM];
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          wv[m] = ring[j][m];
+          sv[m] = sring[j][m];
+          if (c + kDepth < nch) {
+            ring[j][m] = load_w(c + kDepth, m);
+            if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(c + kDepth, m);
+          }
+        }
+        half8_t av[4];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) av[mt] = *reinterpret_cast<const half8_t*>(&sx[c & 1][16 * mt + n][8 * g]);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+          half8_t b[4];
+          block_to_operands<FMT>(wv[m], sv[m], b);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int mt = 0; mt < 4; ++mt)
+              acc[m][q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], b[q], acc[m][q][mt], 0, 0, 0);
+        }
+      }
+      if (xload && c + 1 < nch) *reinterpret_cast<u32x4*>(&sx[(c + 1) & 1][xm][8 * xq]) = xn;
+      __syncthreads();
+    }
+  }
+  if (!active) return;
+  // epilogue: lane (n, g) holds tokens 16 mt + 4 g + i of row 64 rb + 16 q + n
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int row = rb * 64 + 16 * q + n;
+    if (NM == 2) {
+      float sgv, suv;
+      if (FMT == MOE_W_INT4_ROW) {
+        sgv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sg_off)[row]);
+        suv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.su_off)[row]);
+      } else {
+        const float* g3 = reinterpret_cast<const float*>(se.base + a.L.g3_off);
+        sgv = g3[0];
+        suv = g3[1];
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mm = 16 * mt + 4 * g + i;
+          const int orow = s_out[mm];
+          if (orow < 0) continue;
+          const float gv = acc[0][q][mt][i] * sgv, uv = acc[NM - 1][q][mt][i] * suv;
+          a.h[(size_t)orow * a.I + row] = __builtin_bit_cast(uint16_t, (_Float16)(silu(gv) * uv));
+        }
+    } else {
+      float sd;
+      if (FMT == MOE_W_INT4_ROW)
+        sd = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sd_off)[row]);
+      else
+        sd = reinterpret_cast<const float*>(se.base + a.L.g3_off)[2];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int mm = 16 * mt + 4 * g + i;
+          const int orow = s_out[mm];
+          if (orow < 0) continue;
+          a.part[(size_t)orow * a.H + row] = s_w[mm] * (sd * acc[0][q][mt][i]);
+        }
     }
   }
 }
@@ -326,19 +348,22 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   a.S = p.S;
   a.rows_total = p.rows_total;
   a.L = layout_of(d);
-  const unsigned mt = (unsigned)prefill_max_tiles(p.T, p.k, p.E, p.S);
+  const int mt8 = (prefill_max_tiles(p.T, p.k, p.E, p.S) + 7) / 8 * 8;
+  const int rows_per_wg = 64 * kGemmWaves;
+  const int nx_gu = (p.I + rows_per_wg - 1) / rows_per_wg, nx_dn = (p.H + rows_per_wg - 1) / rows_per_wg;
   se.record(1, s);
+  const dim3 blk(64 * kGemmWaves);
   if (d.wfmt == MOE_W_INT4_ROW)
-    hipLaunchKernelGGL(k_gu_gemm<MOE_W_INT4_ROW>, dim3(p.I / 64, mt), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_expert_gemm<MOE_W_INT4_ROW, 2>), dim3(mt8 * nx_gu), blk, 0, s, a, nx_gu);
   else
-    hipLaunchKernelGGL(k_gu_gemm<MOE_W_E2M1_B16>, dim3(p.I / 64, mt), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_expert_gemm<MOE_W_E2M1_B16, 2>), dim3(mt8 * nx_gu), blk, 0, s, a, nx_gu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   se.record(2, s);
   if (d.wfmt == MOE_W_INT4_ROW)
-    hipLaunchKernelGGL(k_dn_gemm<MOE_W_INT4_ROW>, dim3(p.H / 128, mt), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_expert_gemm<MOE_W_INT4_ROW, 1>), dim3(mt8 * nx_dn), blk, 0, s, a, nx_dn);
   else
-    hipLaunchKernelGGL(k_dn_gemm<MOE_W_E2M1_B16>, dim3(p.H / 128, mt), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_expert_gemm<MOE_W_E2M1_B16, 1>), dim3(mt8 * nx_dn), blk, 0, s, a, nx_dn);
   hipLaunchKernelGGL(k_combine, dim3((p.H + 255) / 256, p.T), dim3(256), 0, s, a);
   e = hipGetLastError();
   se.record(3, s);

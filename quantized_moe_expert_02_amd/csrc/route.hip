@@ -365,56 +365,84 @@ __global__ __launch_bounds__(256) void k_route_small(RouteArgs a) {
 
 // ---- large batches -------------------------------------------------------
 
-// fp64 logits, tiled: 32 tokens x 64 experts per 256-thread block; each
-// thread owns 2 tokens x 4 experts.  Operands are staged in LDS as fp32
+// fp64 logits for large batches: block (tile of 64 tokens, tile of 64
+// experts, K-split ks) accumulates columns [ks*Kc, (ks+1)*Kc) into a partial
+// sum per (token, expert); partials are added in K-split order by k_topk.
+// Each thread owns 4 tokens x 4 experts; operands are staged in LDS as fp32
 // (binary16 -> fp32 is exact) and widened to fp64 for the FMA.
-constexpr int LT = 32, LE = 64, LK = 32;
+constexpr int LT = 64, LE = 64, LK = 32;
+constexpr int kLogitSplit = 4;
 __global__ __launch_bounds__(256) void k_logits_tiled(RouteArgs a) {
-  __shared__ float sx[LK][LT + 4];
-  __shared__ float sw[LK][LE + 4];
+  __shared__ __attribute__((aligned(16))) float sx[LK][LT];
+  __shared__ __attribute__((aligned(16))) float sw[LK][LE];
   const int t0 = blockIdx.x * LT, e0 = blockIdx.y * LE;
+  const int kc = a.H / kLogitSplit;
+  const int kbeg = blockIdx.z * kc;
   const int tid = threadIdx.x;
-  const int tt = (tid & 15) * 2;   // token offset in tile
-  const int te = (tid >> 4) * 4;   // expert offset in tile
-  double acc[2][4] = {};
-  for (int k0 = 0; k0 < a.H; k0 += LK) {
-    // x tile: 32 tokens x 32 columns = 1024 values, 4 per thread
-    for (int i = tid; i < LT * LK; i += 256) {
-      const int r = i / LK, c = i % LK;
-      const int t = t0 + r;
-      float v = 0.f;
-      if (t < a.T) v = (float)__builtin_bit_cast(_Float16, a.x[(size_t)t * a.H + k0 + c]);
-      sx[c][r] = v;
-    }
-    for (int i = tid; i < LE * LK; i += 256) {
-      const int r = i / LK, c = i % LK;
-      const int e = e0 + r;
-      sw[c][r] = (e < a.E) ? a.Wr[(size_t)e * a.H + k0 + c] : 0.f;
+  const int tt = (tid & 15) * 4;  // token offset in tile
+  const int te = (tid >> 4) * 4;  // expert offset in tile
+  double acc[4][4] = {};
+  // staging: thread loads 8 consecutive columns of one row (x: 64 rows; w: 64 rows)
+  const int sr = tid >> 2, sc8 = (tid & 3) * 8;
+  for (int k0 = kbeg; k0 < kbeg + kc; k0 += LK) {
+    {
+      const int t = t0 + sr;
+      float v[8] = {};
+      if (t < a.T) {
+        const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H + k0 + sc8);
+        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[i] & 0xFFFF));
+          v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[i] >> 16));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sx[sc8 + i][sr] = v[i];
+      const int e = e0 + sr;
+      float u[8] = {};
+      if (e < a.E) {
+        const float4 w0 = *reinterpret_cast<const float4*>(a.Wr + (size_t)e * a.H + k0 + sc8);
+        const float4 w1 = *reinterpret_cast<const float4*>(a.Wr + (size_t)e * a.H + k0 + sc8 + 4);
+        u[0] = w0.x; u[1] = w0.y; u[2] = w0.z; u[3] = w0.w;
+        u[4] = w1.x; u[5] = w1.y; u[6] = w1.z; u[7] = w1.w;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) sw[sc8 + i][sr] = u[i];
     }
     __syncthreads();
-#pragma unroll 8
+#pragma unroll 4
     for (int c = 0; c < LK; ++c) {
-      const double x0 = sx[c][tt], x1 = sx[c][tt + 1];
-      const double w0 = sw[c][te], w1 = sw[c][te + 1], w2 = sw[c][te + 2], w3 = sw[c][te + 3];
-      acc[0][0] = fma(x0, w0, acc[0][0]);
-      acc[0][1] = fma(x0, w1, acc[0][1]);
-      acc[0][2] = fma(x0, w2, acc[0][2]);
-      acc[0][3] = fma(x0, w3, acc[0][3]);
-      acc[1][0] = fma(x1, w0, acc[1][0]);
-      acc[1][1] = fma(x1, w1, acc[1][1]);
-      acc[1][2] = fma(x1, w2, acc[1][2]);
-      acc[1][3] = fma(x1, w3, acc[1][3]);
+      const float4 xv = *reinterpret_cast<const float4*>(&sx[c][tt]);
+      const float4 wv = *reinterpret_cast<const float4*>(&sw[c][te]);
+      const double xd[4] = {xv.x, xv.y, xv.z, xv.w};
+      const double wd[4] = {wv.x, wv.y, wv.z, wv.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fma(xd[i], wd[j], acc[i][j]);
     }
     __syncthreads();
   }
-  for (int i = 0; i < 2; ++i) {
+  double* zp = a.z + (size_t)blockIdx.z * a.T * a.E;
+  for (int i = 0; i < 4; ++i) {
     const int t = t0 + tt + i;
     if (t >= a.T) continue;
     for (int j = 0; j < 4; ++j) {
       const int e = e0 + te + j;
-      if (e < a.E) a.z[(size_t)t * a.E + e] = acc[i][j] + (a.b ? (double)a.b[e] : 0.0);
+      if (e < a.E) zp[(size_t)t * a.E + e] = acc[i][j];
     }
   }
+}
+
+// Adds the K-split partial logits (in split order) and the bias: z[t][e].
+__global__ __launch_bounds__(256) void k_logits_sum(RouteArgs a) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t n = (size_t)a.T * a.E;
+  if (i >= n) return;
+  double v = 0.0;
+  for (int s = 0; s < kLogitSplit; ++s) v += a.z[(size_t)(s + 1) * n + i];
+  a.z[i] = v + (a.b ? (double)a.b[i % a.E] : 0.0);
 }
 
 // One wavefront per token.
@@ -449,13 +477,19 @@ __global__ __launch_bounds__(1024) void k_union_scan(RouteArgs a) {
   __shared__ int s_tot[kMaxExperts];
   __shared__ int s_pre[kMaxExperts];
   __shared__ int s_prs[kMaxExperts];
+  __shared__ const uint8_t* s_ptr[kMaxExperts];
   const int tid = threadIdx.x;
+  if (a.slots)
+    for (int e = tid; e < a.E; e += blockDim.x) s_ptr[e] = (const uint8_t*)a.experts[e];
+  // pass 1: per-expert totals (16 independent loads in flight per thread)
   for (int e = tid; e < a.E; e += blockDim.x) {
     int run = 0;
-    for (int c = 0; c < a.n_chunks; ++c) {
-      const int v = a.ucnt[(size_t)c * a.E + e];
-      a.ubase[(size_t)c * a.E + e] = run;
-      run += v;
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (c0 + i < a.n_chunks) ? a.ucnt[(size_t)(c0 + i) * a.E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) run += v[i];
     }
     s_tot[e] = run;
   }
@@ -468,7 +502,13 @@ __global__ __launch_bounds__(1024) void k_union_scan(RouteArgs a) {
       if (s_tot[e] > 0) {
         a.uniq_ids[nu] = e;
         a.uniq_off[nu] = off;
-        if (a.slots) write_slot(a, a.S + nu, e, s_tot[e], off);
+        if (a.slots) {
+          SlotEntry sl;
+          sl.base = s_ptr[e];
+          sl.n = s_tot[e];
+          sl.p0 = off;
+          a.slots[a.S + nu] = sl;
+        }
         ++nu;
       }
       off += s_tot[e];
@@ -503,9 +543,19 @@ __global__ __launch_bounds__(1024) void k_union_scan(RouteArgs a) {
   if (a.slots)
     for (int sl = a.S + s_prs[0] + tid; sl < a.slots_max; sl += blockDim.x) write_slot(a, sl, 0, 0, 0);
   __syncthreads();
+  // pass 2: base of each (chunk, expert) = expert base + earlier chunks' counts
   for (int e = tid; e < a.E; e += blockDim.x) {
-    const int base = s_pre[e];
-    for (int c = 0; c < a.n_chunks; ++c) a.ubase[(size_t)c * a.E + e] += base;
+    int run = s_pre[e];
+    for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
+      int v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = (c0 + i < a.n_chunks) ? a.ucnt[(size_t)(c0 + i) * a.E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (c0 + i < a.n_chunks) a.ubase[(size_t)(c0 + i) * a.E + e] = run;
+        run += v[i];
+      }
+    }
   }
 }
 
@@ -578,7 +628,13 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
     hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((zero_count + 255) / 256)), dim3(256), 0, s, zero_from,
                        (int)zero_count);
   }
-  hipLaunchKernelGGL(k_logits_tiled, dim3((p.T + LT - 1) / LT, (p.E + LE - 1) / LE), dim3(256), 0, s, a);
+  {
+    RouteArgs b = a;
+    b.z = r.z + (size_t)p.T * p.E;  // K-split partials live after z
+    hipLaunchKernelGGL(k_logits_tiled, dim3((p.T + LT - 1) / LT, (p.E + LE - 1) / LE, kLogitSplit), dim3(256), 0, s, b);
+    const size_t n = (size_t)p.T * p.E;
+    hipLaunchKernelGGL(k_logits_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
+  }
   hipLaunchKernelGGL(k_topk, dim3((p.T + 3) / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_union_count, dim3(a.n_chunks), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, s, a);
