@@ -33,8 +33,12 @@ HBM_PEAK_GBPS = 8000.0
 FP16_MFMA_PEAK_TFLOPS = 2500.0
 PROFILES = os.path.join(ROOT, "profiles")
 
-# stage index of the dominant kernel per path, and its name in rocprofv3 output
-DOMINANT = {"decode": (1, "k_gu_gemv"), "prefill": (1, "k_gu_gemm")}
+# Stage names per path (HIP events the library records between launches) and
+# the dominant kernel: (stage index, name in rocprofv3 output).  On the decode
+# path the shared expert's gate/up runs in the routing launch, so the gate/up
+# launch streams the routed experts only.
+STAGES = {"decode": ("route_shared_gate_up", "gate_up", "down"), "prefill": ("route", "gate_up", "down")}
+DOMINANT = {"decode": (1, "k_gu_phase"), "prefill": (1, "k_gu_gemm")}
 
 
 def log(*a):
@@ -277,6 +281,19 @@ def cpu_baseline(ch: Chain, budget_s: float = 12.0, max_tokens: int = 64):
 
 
 # ---- main ----------------------------------------------------------------------
+def path_of(T):
+    return "decode" if T <= moe.moe_decode_max_tokens() else "prefill"
+
+
+def dominant_bytes(d, T, n_touched):
+    """Algorithmic bytes of the dominant (gate/up) kernel: on the decode path
+    the routed experts' gate/up weights and scales, x read and the routed h
+    rows written; on the prefill path the shared expert as well."""
+    if path_of(T) == "decode":
+        return n_touched * expert_gu_bytes(d) + T * d.hidden * 2 + T * d.top_k * d.inter * 2
+    return gu_kernel_bytes(d, T, n_touched)
+
+
 def run_workload(name, L, steps, warmup, stage_reps=4):
     ch = Chain(name, L)
     touched = ch.touched()
@@ -291,7 +308,7 @@ def run_workload(name, L, steps, warmup, stage_reps=4):
         "ms_per_step": ms_step, "tokens_per_s": T * steps / (ms / 1e3),
         "mean_unique_experts": U, "layer_bytes": lb,
         "layer_hbm_gbps": lb / (ms_step / 1e3) / 1e9,
-        "stage_ms": {"route": stages[0], "gate_up": stages[1], "down": stages[2]},
+        "stage_ms": dict(zip(STAGES[path_of(T)], stages)),
         "wall_s": wall,
     }
     if T > moe.moe_decode_max_tokens():
@@ -318,11 +335,11 @@ def main():
 
     ch, res, touched = run_workload(args.workload, args.layers, args.steps, args.warmup)
     d, T = ch.dims, ch.T
-    path = "decode" if T <= moe.moe_decode_max_tokens() else "prefill"
+    path = path_of(T)
     st_idx, kname = DOMINANT[path]
-    k_ms = res["stage_ms"]["gate_up"]
+    k_ms = res["stage_ms"][STAGES[path][st_idx]]
     U = res["mean_unique_experts"]
-    alg = sum(gu_kernel_bytes(d, T, u) for u in touched) / len(touched)
+    alg = sum(dominant_bytes(d, T, u) for u in touched) / len(touched)
     achieved = alg / (k_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(kname, args.workload),

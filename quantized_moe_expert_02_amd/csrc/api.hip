@@ -49,20 +49,21 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.slots_max = q.S + (int)std::min<int64_t>(q.E, (int64_t)T * q.k);
   q.rows_total = T * q.k + T;
   q.ks_gu = split_factor(q.H, 8);
-  q.ks_dn = split_factor(q.I, 4);
-  // Counters: one for the router, one per (slot, gate/up row block) for the
-  // largest decode batch, one per down row block.
+  q.ks_dn = split_factor(q.I, 2);
+  // Counters: the first 256 words for route-stage counters, then one per
+  // (slot, gate/up row block) for the largest decode batch, then one per
+  // down row block.
   const int slots_decode = q.S + std::min(q.E, kDecodeMaxTokens * q.k);
   q.c_route = 0;
-  q.c_gu = 64;  // keep the router counter on its own cache line
+  q.c_gu = 256;
   q.c_dn = q.c_gu + (size_t)slots_decode * (q.I / 64);
   q.n_counters = q.c_dn + q.H / 64;
   q.sync_bytes = up256(q.n_counters * 4);
   size_t off = q.sync_bytes;
   const size_t Tk = (size_t)T * q.k;
   const size_t cap = std::max<size_t>(1, std::min<size_t>(q.E, Tk));
-  // z plus, for large batches, the K-split partial logits
-  q.z_off = off; off = up256(off + (size_t)T * q.E * 8 * (q.decode ? 1 : 5));
+  // z plus the K-split partial logits of the batched router
+  q.z_off = off; off = up256(off + (size_t)T * q.E * 8 * 5);
   q.idx_off = off; off = up256(off + Tk * 4);
   q.w_off = off; off = up256(off + Tk * 4);
   q.nu_off = off; off = up256(off + 4);
@@ -196,7 +197,7 @@ int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, in
   r.uniq_ids = uniq_ids;
   r.uniq_off = uniq_off;
   r.pairs = pairs;
-  if (launch_route(*d, p, *w, x, r, false, nullptr, 0, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
+  if (launch_route(*d, p, *w, x, r, false, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
   return MOE_OK;
 }
 
@@ -221,13 +222,10 @@ static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint1
   if (topk_idx_out) r.topk_idx = topk_idx_out;
   if (topk_w_out) r.topk_w = topk_w_out;
   hipStream_t s = (hipStream_t)stream;
-  uint32_t* zero_from = (uint32_t*)ws + p.c_gu;
-  const size_t zero_count = p.n_counters - p.c_gu;
+  if (p.decode) return launch_decode(*d, p, *w, x, r, ws, y, s, se) == hipSuccess ? MOE_OK : MOE_E_HIP;
   se.record(0, s);
-  if (launch_route(*d, p, *w, x, r, true, zero_from, zero_count, s) != hipSuccess) return MOE_E_HIP;
-  hipError_t e = p.decode ? launch_decode_experts(*d, p, *w, x, r, ws, y, s, se)
-                          : launch_prefill_experts(*d, p, *w, x, r, ws, y, s, se);
-  return e == hipSuccess ? MOE_OK : MOE_E_HIP;
+  if (launch_route(*d, p, *w, x, r, true, s) != hipSuccess) return MOE_E_HIP;
+  return launch_prefill_experts(*d, p, *w, x, r, ws, y, s, se) == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
 int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,

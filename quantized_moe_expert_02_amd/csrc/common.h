@@ -70,7 +70,6 @@ inline Layout layout_of(const moe_dims_t& d) {
 constexpr int kDecodeMaxTokens = 16;   // GEMV path for T <= this
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
-constexpr int kRouteSmallMaxTokens = 16;
 constexpr int kPrefillTileRows = 64;   // tokens per grouped-GEMM tile
 
 // Upper bound on grouped-GEMM tiles (slot, first token) for T tokens.
@@ -133,7 +132,7 @@ hipError_t launch_unpack(const moe_dims_t& d, const void* packed, void* qg, void
 // Routing and union.  With `with_slots`, also fills r.slots from w.experts
 // and w.shared (moe_w4a16_forward); moe_route passes false.
 hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
-                        const Route& r, bool with_slots, uint32_t* zero_from, size_t zero_count, hipStream_t s);
+                        const Route& r, bool with_slots, hipStream_t s);
 // Optional stage events (benchmark timing): ev[i] is recorded before stage
 // i and ev[n-1] after the last; null entries are skipped.
 struct StageEvents {
@@ -144,9 +143,10 @@ struct StageEvents {
   }
 };
 
-hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
-                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s,
-                                 const StageEvents& se);
+// The whole layer for T <= kDecodeMaxTokens in three launches: route +
+// shared gate/up, routed gate/up, down (stage events 0..3 around them).
+hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
+                         const Route& r, void* ws, uint16_t* y, hipStream_t s, const StageEvents& se);
 hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
                                   const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s,
                                   const StageEvents& se);

@@ -20,7 +20,7 @@
 //   k_gu_gemv:  gate and up rows together -> SwiGLU -> h (binary16)
 //   k_dn_gemv:  down rows -> scaled partials -> routing-weighted combine of
 //               the k slots plus the shared expert -> y (binary16)
-#include "common.h"
+#include "wave.h"
 
 namespace moe {
 namespace {
@@ -33,25 +33,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(1))) const u32x4 guint4;
 typedef __attribute__((address_space(1))) const u32x2 guint2;
+typedef __attribute__((address_space(4))) const u32x4 cu32x4;
+typedef __attribute__((address_space(3))) const u32x4 lu32x4;
 
-struct GemvArgs {
-  const SlotEntry* slots;
-  const int32_t* n_unique;
-  const int32_t* uniq_ids;
-  const int32_t* uniq_off;
-  const int32_t* pairs;
-  const float* topk_w;
-  float* part;        // partials
-  uint32_t* counters;
-  uint16_t* h;        // [rows_total][I]
-  uint16_t* y;        // [T][H]
-  int T, H, I, k, S;
-  int ks;             // K-segments per row block
-  int cpu;            // 32-column chunks per unit
-  int rows_total;
-  int fmt;
-  Layout L;
-};
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
@@ -105,7 +89,7 @@ __device__ __forceinline__ half2_t e4m3_pair(uint32_t bytes, int sel) {
   return half2_t{h, h};
 }
 
-__device__ __forceinline__ float dot8(half2_t p0, half2_t p1, half2_t p2, half2_t p3, uint4 xv, float acc) {
+__device__ __forceinline__ float dot8(half2_t p0, half2_t p1, half2_t p2, half2_t p3, u32x4 xv, float acc) {
   acc = __builtin_amdgcn_fdot2(p0, as_h2(xv.x), acc, false);
   acc = __builtin_amdgcn_fdot2(p1, as_h2(xv.y), acc, false);
   acc = __builtin_amdgcn_fdot2(p2, as_h2(xv.z), acc, false);
@@ -113,12 +97,8 @@ __device__ __forceinline__ float dot8(half2_t p0, half2_t p1, half2_t p2, half2_
   return acc;
 }
 
-// Streams `nch` chunks for NM matrices (gate+up: NM=2) and NT activation rows.
-//   w: this lane's 16 bytes in the first chunk of matrix 0; matrix m of
-//      chunk c is at w + (c*NM + m)*64 (uint4 units).
-//   sc: E2M1 only: this lane's 8 scale bytes of the first 4-chunk group of
-//      matrix 0; matrix m of group g is at sc + (g*NM + m)*64 (uint2 units).
-//   act[t]: wave-uniform activation rows, already offset to column 32*c0.
+// Requests chunks c .. c+U-1 of NM matrices (and, for E2M1, their scale
+// group) with non-temporal loads: the weights are read once per call.
 template <int FMT, int NM, int U>
 __device__ __forceinline__ void load_batch(const guint4* __restrict__ w, const guint2* __restrict__ sc, int c,
                                            u32x4 (&wv)[U][NM], u32x2 (&sv)[NM]) {
@@ -132,12 +112,15 @@ __device__ __forceinline__ void load_batch(const guint4* __restrict__ w, const g
   }
 }
 
-template <int FMT, int NM, int NT, int U>
+template <int FMT, int NM, int NT, int U, typename AP>
 __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u32x2 (&sv)[NM], int c,
-                                              const uint4* const* act, const Int4Masks& mk, float (&acc)[NM][NT]) {
+                                              const AP* act, const Int4Masks& mk, float (&acc)[NM][NT]) {
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    uint4 xv[NT][4];
+    // keep each chunk's activation loads next to their use: hoisting them
+    // over the whole batch needs 16*NT registers per chunk at once
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4 xv[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -164,59 +147,126 @@ __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u3
 }
 
 // Streams `nch` chunks (a multiple of 4) for NM matrices (gate+up: NM=2) and
-// NT activation rows, keeping the next 4-chunk batch of weights in flight
-// while the current one is decoded and multiplied.
+// NT activation rows into acc through a ring of D four-chunk batches: the
+// first D batches are requested at once, then `pre()` runs (a caller's own
+// loads, overlapping the weights in flight), and every batch is reloaded with
+// the batch D ahead right after it has been decoded and multiplied.
 //   w: this lane's 16 bytes in the first chunk of matrix 0; matrix m of
 //      chunk c is at w + (c*NM + m)*64 (uint4 units).
 //   sc: E2M1 only: this lane's 8 scale bytes of the first 4-chunk group of
 //      matrix 0; matrix m of group g is at sc + (g*NM + m)*64 (uint2 units).
 //   act[t]: wave-uniform activation rows, already offset to column 32*c0.
-template <int FMT, int NM, int NT>
-__device__ __forceinline__ void stream_chunks(const guint4* __restrict__ w, const guint2* __restrict__ sc,
-                                              const uint4* const* act, int nch, float (&acc)[NM][NT]) {
+//      Rows that stay unchanged for the whole launch are passed as
+//      constant-address-space pointers, which makes their loads scalar.
+template <int FMT, int NM, int NT, int D, typename AP, typename Pre>
+__device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const guint2* __restrict__ sc,
+                                            const AP* act, int nch, float (&acc)[NM][NT], Pre&& pre) {
   const Int4Masks mk = int4_masks();
-#pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[m][t] = 0.f;
   constexpr int U = 4;  // chunks per batch (one E2M1 scale group)
-  u32x4 wa[U][NM], wb[U][NM];
-  u32x2 sa[NM], sb[NM];
-  load_batch<FMT, NM, U>(w, sc, 0, wa, sa);
-  for (int c = 0; c < nch; c += 2 * U) {
-    const bool has_b = c + U < nch;
-    if (has_b) load_batch<FMT, NM, U>(w, sc, c + U, wb, sb);
-    compute_batch<FMT, NM, NT, U>(wa, sa, c, act, mk, acc);
-    if (!has_b) break;
-    if (c + 2 * U < nch) load_batch<FMT, NM, U>(w, sc, c + 2 * U, wa, sa);
-    compute_batch<FMT, NM, NT, U>(wb, sb, c + U, act, mk, acc);
+  u32x4 wv[D][U][NM];
+  u32x2 sv[D][NM];
+  const int nb = nch / U;
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (d < nb) load_batch<FMT, NM, U>(w, sc, d * U, wv[d], sv[d]);
+  pre();
+  for (int b0 = 0; b0 < nb; b0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int b = b0 + d;
+      if (b < nb) {
+        compute_batch<FMT, NM, NT, U>(wv[d], sv[d], b * U, act, mk, acc);
+        if (b + D < nb) load_batch<FMT, NM, U>(w, sc, (b + D) * U, wv[d], sv[d]);
+      }
+    }
   }
 }
 
-// Expert and token list of a slot, from the slot table the union step
-// wrote: one 16-byte wave-uniform load.  Returns false for unused slots.
-struct SlotInfo {
-  const uint8_t* base;
-  int n;            // tokens
-  int p0;           // first entry in pairs (routed) or -1 (shared)
+// ===========================================================================
+// Decode path: three launches per layer, one wavefront per work unit.
+//   k_route_phase  router units (fp64 partial logits of one expert over one
+//                  column segment, for all tokens; the last router unit to
+//                  finish takes every token's top-k and forms the batch union
+//                  and slot table), and the shared expert's gate/up units,
+//                  which need no routing
+//   k_gu_phase     gate/up units of the routed slots
+//   k_dn_phase     down units of every slot (shared expert first)
+// Units: gate/up (slot, 64-row block, K-segment), down (slot, 64-row output
+// block, K-segment).  A gate/up unit writes fp32 partial sums; the last unit
+// of a (slot, row block) forms h for those rows (row scales, SwiGLU).  The
+// last down unit of an output row block combines the slots in a fixed order
+// (routing-weighted, shared expert last) into y.  "Last" is decided by
+// device-scope arrival counters, which that unit returns to zero, so every
+// call starts from zeroed counters.  Data handed to another workgroup of the
+// same launch is written with device-coherent stores and read after the
+// arrival that publishes it (common.h); the launch boundaries order the
+// phases, so no unit ever waits for another.
+// ===========================================================================
+
+constexpr int kStageChunks = 32;  // h columns staged in LDS per step: 32 x 32
+constexpr int kGuDepth = 2;       // gate/up: 4-chunk batches in flight (16 KiB)
+constexpr int kDnDepth = 4;       // down: 4-chunk batches in flight (16 KiB)
+constexpr int kSyRouter = 128;    // router arrival counter (uint32 index in the sync region)
+
+struct DecArgs {
+  const float* Wr;
+  const float* rbias;
+  const uint16_t* x;
+  const void* const* experts;
+  const void* shared;
+  int T, H, I, E, k, S;
+  Layout L;
+  uint16_t* y;
+  int32_t* topk_idx;
+  float* topk_w;
+  double* z;
+  int32_t* n_unique;
+  int32_t* uniq_ids;
+  int32_t* uniq_off;
+  int32_t* pairs;
+  SlotEntry* slots;
+  uint16_t* h;
+  float* p_gu;
+  float* p_dn;
+  uint32_t* sync;
+  uint32_t* gu_cnt;   // [slots][I/64]
+  uint32_t* dn_cnt;   // [H/64]
+  int ks_gu, ks_dn, cpu_gu, cpu_dn;
+  int slots_max, rows_total;
+  int rsplit, seg4;   // router units per expert, 16-byte columns per router unit
+  int n_router;       // E * rsplit
 };
 
-__device__ __forceinline__ bool resolve_slot(const GemvArgs& a, int slot, SlotInfo& si) {
-  const SlotEntry e = a.slots[slot];
+struct SlotInfo {
+  const uint8_t* base;
+  int n;   // tokens
+  int p0;  // first entry in pairs (routed) or -1 (shared)
+};
+
+// Slot s of the call: the shared expert needs no routing; routed slots come
+// from the table the route phase wrote.  Returns false for unused slots.
+__device__ __forceinline__ bool get_slot(const DecArgs& a, int s, SlotInfo& si) {
+  if (a.S && s == 0) {
+    si.base = (const uint8_t*)a.shared;
+    si.n = a.T;
+    si.p0 = -1;
+    return true;
+  }
+  const SlotEntry e = a.slots[s];
   si.base = e.base;
-  si.n = e.n;
-  si.p0 = e.p0;
+  si.n = __builtin_amdgcn_readfirstlane(e.n);
+  si.p0 = __builtin_amdgcn_readfirstlane(e.p0);
   return si.n > 0;
 }
 
-// Token index and output row (pair id, or T*k + t for the shared expert) of
-// the i-th token of a slot.
-__device__ __forceinline__ void slot_token(const GemvArgs& a, const SlotInfo& si, int i, int& t, int& row) {
+// Token index and output row (pair id, or T*k + t for the shared expert)
+// of the i-th token of a slot.
+__device__ __forceinline__ void slot_token(const DecArgs& a, const SlotInfo& si, int i, int& t, int& row) {
   if (si.p0 < 0) {
     t = i;
     row = a.T * a.k + i;
   } else {
-    const int p = a.pairs[si.p0 + i];
+    const int p = __builtin_amdgcn_readfirstlane(a.pairs[si.p0 + i]);
     t = p / a.k;
     row = p;
   }
@@ -224,87 +274,179 @@ __device__ __forceinline__ void slot_token(const GemvArgs& a, const SlotInfo& si
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
-// Publishes this unit's partial stores and reports whether it is the last of
-// `total` units of its group; the last one resets the counter for the next
-// call.
+// Arrival on a counter shared by `total` units: true for the last one, which
+// also returns the counter to zero.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total) {
   if (publish_arrival(counter) != total - 1) return false;
   if ((threadIdx.x & 63) == 0) st_dev(counter, 0u);
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");  // no load moves above the arrival
   return true;
 }
 
+// ---- batch union ----------------------------------------------------------
+// Unique experts in ascending order, their pair lists (pairs of one expert
+// in token order) and the slot table, from per-expert token bitmasks in LDS:
+// the rank of pair (t, j) within its expert is the number of earlier tokens
+// that chose the same expert.  pe[] holds the expert of every pair.
+struct UnionLds {
+  uint32_t mask[kMaxExperts];  // tokens per expert (bit t)
+  int base[kMaxExperts];       // first pair of each expert
+  int pe[kDecodeMaxTokens * kMaxTopK];
+};
+
+__device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
+  const int lane = threadIdx.x & 63;
+  const int P = a.T * a.k;
+  const int per = (a.E + 63) / 64;
+  const int e0 = lane * per, e1 = min(a.E, e0 + per);
+  for (int e = e0; e < e1; ++e) ls.mask[e] = 0;
+  __syncthreads();
+  for (int p = lane; p < P; p += 64) atomicOr(&ls.mask[ls.pe[p]], 1u << (p / a.k));
+  __syncthreads();
+  int cnt = 0, pres = 0;
+  for (int e = e0; e < e1; ++e) {
+    const int c = __popc(ls.mask[e]);
+    cnt += c;
+    pres += c > 0;
+  }
+  // inclusive scan of (present << 16 | count) across the wavefront
+  int v = (pres << 16) | cnt;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(v, off, 64);
+    if (lane >= off) v += o;
+  }
+  const int excl = v - ((pres << 16) | cnt);
+  int up = excl >> 16, uc = excl & 0xFFFF;
+  for (int e = e0; e < e1; ++e) {
+    const int c = __popc(ls.mask[e]);
+    ls.base[e] = uc;
+    if (c > 0) {
+      a.uniq_ids[up] = e;
+      a.uniq_off[up] = uc;
+      SlotEntry se;
+      se.base = (const uint8_t*)a.experts[e];
+      se.n = c;
+      se.p0 = uc;
+      a.slots[a.S + up] = se;
+      ++up;
+    }
+    uc += c;
+  }
+  const int tot = __builtin_amdgcn_readlane(v, 63);
+  const int nu = tot >> 16;
+  if (lane == 0) {
+    *a.n_unique = nu;
+    a.uniq_off[nu] = tot & 0xFFFF;
+  }
+  for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
+  __syncthreads();
+  for (int p = lane; p < P; p += 64) {
+    const int e = ls.pe[p];
+    const int t = p / a.k;
+    a.pairs[ls.base[e] + __popc(ls.mask[e] & ((1u << t) - 1u))] = p;
+  }
+}
+
+// ---- router unit: fp64 partial logits of expert e over one column segment --
+// Segment s of expert e writes plane s of z ([plane][T][E]).  The last unit
+// to finish adds the planes in order and the bias, takes each token's top-k
+// and runs the union.
+constexpr int kLogitsBatch = 12;  // 16-byte router loads in flight per lane
+__device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& ls) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int e = it / a.rsplit, seg = it % a.rsplit;
+  const int lane = threadIdx.x & 63;
+  double acc[kDecodeMaxTokens];
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTokens; ++t) acc[t] = 0.0;
+  const f32x4* wr = reinterpret_cast<const f32x4*>(a.Wr + (size_t)e * a.H);
+  const int n4 = min(a.H / 4, (seg + 1) * a.seg4);
+  for (int base = seg * a.seg4; base < n4; base += 64 * kLogitsBatch) {
+    f32x4 w[kLogitsBatch];
+#pragma unroll
+    for (int i = 0; i < kLogitsBatch; ++i) {
+      const int c4 = base + lane + 64 * i;
+      w[i] = (c4 < n4) ? __builtin_nontemporal_load(wr + c4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int t = 0; t < kDecodeMaxTokens; ++t) {
+      if (t < a.T) {
+        double s0 = acc[t], s1 = 0.0;
+#pragma unroll
+        for (int i = 0; i < kLogitsBatch; ++i) {
+          const int c4 = base + lane + 64 * i;
+          const uint2 xv = (c4 < n4) ? *reinterpret_cast<const uint2*>(a.x + (size_t)t * a.H + 4 * c4) : make_uint2(0, 0);
+          const _Float16 x0 = __builtin_bit_cast(_Float16, (uint16_t)(xv.x & 0xFFFF));
+          const _Float16 x1 = __builtin_bit_cast(_Float16, (uint16_t)(xv.x >> 16));
+          const _Float16 x2 = __builtin_bit_cast(_Float16, (uint16_t)(xv.y & 0xFFFF));
+          const _Float16 x3 = __builtin_bit_cast(_Float16, (uint16_t)(xv.y >> 16));
+          s0 = fma((double)x0, (double)w[i].x, s0);
+          s1 = fma((double)x1, (double)w[i].y, s1);
+          s0 = fma((double)x2, (double)w[i].z, s0);
+          s1 = fma((double)x3, (double)w[i].w, s1);
+        }
+        acc[t] = s0 + s1;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kDecodeMaxTokens; ++t) {
+    if (t < a.T) {
+      const double v = wave_sum(acc[t]);
+      if (lane == 0) st_dev(a.z + ((size_t)seg * a.T + t) * a.E + e, v);
+    }
+  }
+  if (!arrive_last(a.sync + kSyRouter, (uint32_t)a.n_router)) return;
+  for (int t = 0; t < a.T; ++t)
+    topk_any<true>(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k,
+                   a.topk_idx + (size_t)t * a.k, a.topk_w + (size_t)t * a.k, ls.pe + t * a.k);
+  __syncthreads();
+  union_step(a, ls);
+}
+
+// ---- gate/up unit -----------------------------------------------------------
 template <int FMT, int NT>
-__device__ void gu_tile(const GemvArgs& a, const SlotInfo& si, int rb, int c0, int ks, int i0,
-                        const uint16_t* __restrict__ x) {
+__device__ __forceinline__ void gu_tile(const DecArgs& a, const uint16_t* __restrict__ x, const SlotInfo& si,
+                                        int rb, int c0, int ks, int i0) {
   const int lane = threadIdx.x & 63;
   const guint4* w = (const guint4*)(si.base + a.L.gu_off) + ((size_t)rb * (a.H / 32) + c0) * 2 * 64 + lane;
   const guint2* sc = nullptr;
   if (FMT == MOE_W_E2M1_B16)
     sc = (const guint2*)(si.base + a.L.sgu_off) + ((size_t)rb * (a.H / 128) + c0 / 4) * 2 * 64 + lane;
-  const uint4* act[NT];
+  const cu32x4* act[NT];  // x is read-only during the launch
   int rows[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int tok, row;
     slot_token(a, si, i0 + t, tok, row);
-    tok = __builtin_amdgcn_readfirstlane(tok);
-    rows[t] = __builtin_amdgcn_readfirstlane(row);
-    act[t] = reinterpret_cast<const uint4*>(x + (size_t)tok * a.H + 32 * c0);
+    rows[t] = row;
+    act[t] = (const cu32x4*)(x + (size_t)tok * a.H + 32 * c0);
   }
   float acc[2][NT];
-  stream_chunks<FMT, 2, NT>(w, sc, act, a.cpu, acc);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[0][t] = acc[1][t] = 0.f;
+  stream_ring<FMT, 2, NT, kGuDepth>(w, sc, act, a.cpu_gu, acc, [] {});
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    float* pr = a.part + (((size_t)ks * a.rows_total + rows[t]) * 2) * a.I + 64 * rb + lane;
+    float* pr = a.p_gu + (((size_t)ks * a.rows_total + rows[t]) * 2) * a.I + 64 * rb + lane;
     st_dev(pr, acc[0][t]);
     st_dev(pr + a.I, acc[1][t]);
   }
 }
 
-template <int FMT, int NT>
-__device__ void dn_tile(const GemvArgs& a, const SlotInfo& si, int rb, int c0, int ks, int i0, float scale) {
-  const int lane = threadIdx.x & 63;
-  const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / 32) + c0) * 64 + lane;
-  const guint2* sc = nullptr;
-  if (FMT == MOE_W_E2M1_B16)
-    sc = (const guint2*)(si.base + a.L.sdd_off) + ((size_t)rb * (a.I / 128) + c0 / 4) * 64 + lane;
-  const uint4* act[NT];
-  int rows[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int tok, row;
-    slot_token(a, si, i0 + t, tok, row);
-    rows[t] = __builtin_amdgcn_readfirstlane(row);
-    act[t] = reinterpret_cast<const uint4*>(a.h + (size_t)rows[t] * a.I + 32 * c0);
-  }
-  float acc[1][NT];
-  stream_chunks<FMT, 1, NT>(w, sc, act, a.cpu, acc);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    st_dev(a.part + ((size_t)ks * a.rows_total + rows[t]) * a.H + 64 * rb + lane, acc[0][t] * scale);
-}
-
-// Grid: x = (I/64) * ks units of (row block, K-segment); y = expert slots.
-// Block: one wavefront.
-template <int FMT>
-__global__ __launch_bounds__(64) void k_gu_gemv(GemvArgs a, const uint16_t* __restrict__ x) {
+template <int FMT, int KT>
+__device__ __forceinline__ void gu_unit(const DecArgs& a, const uint16_t* __restrict__ x, int s, int rb, int ks) {
   SlotInfo si;
-  const int slot = blockIdx.y;
-  if (!resolve_slot(a, slot, si)) return;
-  const int rb = blockIdx.x / a.ks, ks = blockIdx.x % a.ks;
-  const int c0 = ks * a.cpu;
-  const int lane = threadIdx.x & 63;
-  for (int i0 = 0; i0 < si.n; i0 += 4) {
-    switch (min(4, si.n - i0)) {
-      case 1: gu_tile<FMT, 1>(a, si, rb, c0, ks, i0, x); break;
-      case 2: gu_tile<FMT, 2>(a, si, rb, c0, ks, i0, x); break;
-      case 3: gu_tile<FMT, 3>(a, si, rb, c0, ks, i0, x); break;
-      default: gu_tile<FMT, 4>(a, si, rb, c0, ks, i0, x); break;
-    }
+  if (!get_slot(a, s, si)) return;
+  const int c0 = ks * a.cpu_gu;
+  for (int i0 = 0; i0 < si.n; i0 += KT) {
+    if (KT == 1 || si.n - i0 == 1) gu_tile<FMT, 1>(a, x, si, rb, c0, ks, i0);
+    else gu_tile<FMT, KT>(a, x, si, rb, c0, ks, i0);
   }
-  if (!arrive_last(a.counters + (size_t)slot * (a.I / 64) + rb, a.ks)) return;
-  // Last K-segment of this (slot, row block): reduce in segment order, apply
-  // the row scales, SwiGLU, store h.
+  if (!arrive_last(a.gu_cnt + (size_t)s * (a.I / 64) + rb, (uint32_t)a.ks_gu)) return;
+  // last K-segment of this (slot, row block): reduce in segment order, row
+  // scales, SwiGLU, h
+  const int lane = threadIdx.x & 63;
   const int r = 64 * rb + lane;
   float sg, su;
   if (FMT == MOE_W_INT4_ROW) {
@@ -318,39 +460,80 @@ __global__ __launch_bounds__(64) void k_gu_gemv(GemvArgs a, const uint16_t* __re
   for (int i = 0; i < si.n; ++i) {
     int tok, row;
     slot_token(a, si, i, tok, row);
-    // issue every partial load before summing (they are independent)
     float pg[kMaxSplit], pu[kMaxSplit];
 #pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) {
-      if (s < a.ks) {
-        const float* pr = a.part + (((size_t)s * a.rows_total + row) * 2) * a.I + r;
-        pg[s] = ld_dev(pr);
-        pu[s] = ld_dev(pr + a.I);
+    for (int q = 0; q < kMaxSplit; ++q) {
+      if (q < a.ks_gu) {
+        const float* pr = a.p_gu + (((size_t)q * a.rows_total + row) * 2) * a.I + r;
+        pg[q] = pr[0];
+        pu[q] = pr[a.I];
       }
     }
     float g = 0.f, u = 0.f;
 #pragma unroll
-    for (int s = 0; s < kMaxSplit; ++s) {
-      if (s < a.ks) {
-        g += pg[s];
-        u += pu[s];
+    for (int q = 0; q < kMaxSplit; ++q)
+      if (q < a.ks_gu) {
+        g += pg[q];
+        u += pu[q];
       }
-    }
-    g *= sg;
-    u *= su;
-    const float hv = silu(g) * u;
-    a.h[(size_t)row * a.I + r] = __builtin_bit_cast(uint16_t, (_Float16)hv);
+    const float hv = silu(g * sg) * (u * su);
+    a.h[(size_t)row * a.I + r] = __builtin_bit_cast(uint16_t, (_Float16)hv);  // read by the next launch
   }
 }
 
-// Grid: x = (H/64) * ks, y = expert slots.  Block: one wavefront.
-template <int FMT>
-__global__ __launch_bounds__(64) void k_dn_gemv(GemvArgs a) {
+// ---- down unit ----------------------------------------------------------------
+// h rows come through LDS: vector loads of h mixed into the weight stream
+// would make every weight batch wait for them (the vector memory counter
+// retires in order).  Each step of kStageChunks chunks requests its first
+// weight batches, then stages the NT h row pieces into LDS while those are
+// in flight, then streams.
+template <int KT>
+struct DnLds {
+  u32x4 h[KT * kStageChunks * 4];  // KT tokens x 32 chunks x 64 B
+};
+
+template <int FMT, int NT, int KT>
+__device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, int rb, int c0, int ks, int i0,
+                                        float scale, DnLds<KT>& ls) {
+  const int lane = threadIdx.x & 63;
+  const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / 32) + c0) * 64 + lane;
+  const guint2* sc = nullptr;
+  if (FMT == MOE_W_E2M1_B16)
+    sc = (const guint2*)(si.base + a.L.sdd_off) + ((size_t)rb * (a.I / 128) + c0 / 4) * 64 + lane;
+  const lu32x4* act[NT];  // LDS
+#pragma unroll
+  for (int t = 0; t < NT; ++t) act[t] = (const lu32x4*)(ls.h + t * kStageChunks * 4);
+  int rows[NT];
+  float acc[1][NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[0][t] = 0.f;
+  for (int p0 = 0; p0 < a.cpu_dn; p0 += kStageChunks) {
+    const int np = min(kStageChunks, a.cpu_dn - p0);
+    __syncthreads();  // the previous step's LDS reads are done
+    // the weight batches are requested first; the pair lookups and h loads
+    // follow while they are in flight
+    stream_ring<FMT, 1, NT, kDnDepth>(
+        w + (size_t)p0 * 64, FMT == MOE_W_E2M1_B16 ? sc + (size_t)(p0 / 4) * 64 : sc, act, np, acc, [&] {
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            int tok, row;
+            slot_token(a, si, i0 + t, tok, row);
+            rows[t] = row;
+            const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)row * a.I + 32 * c0);
+            for (int q = lane; q < np * 4; q += 64) ls.h[t * kStageChunks * 4 + q] = src[p0 * 4 + q];
+          }
+          __syncthreads();
+        });
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    st_dev(a.p_dn + ((size_t)ks * a.rows_total + rows[t]) * a.H + 64 * rb + lane, acc[0][t] * scale);
+}
+
+template <int FMT, int KT>
+__device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rb, int ks, DnLds<KT>& ls) {
   SlotInfo si;
-  const int slot = blockIdx.y;
-  if (!resolve_slot(a, slot, si)) return;
-  const int rb = blockIdx.x / a.ks, ks = blockIdx.x % a.ks;
-  const int c0 = ks * a.cpu;
+  if (!get_slot(a, s, si)) return;
   const int lane = threadIdx.x & 63;
   const int r = 64 * rb + lane;
   float scale;
@@ -358,30 +541,27 @@ __global__ __launch_bounds__(64) void k_dn_gemv(GemvArgs a) {
     scale = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sd_off)[r]);
   else
     scale = reinterpret_cast<const float*>(si.base + a.L.g3_off)[2];
-  for (int i0 = 0; i0 < si.n; i0 += 4) {
-    switch (min(4, si.n - i0)) {
-      case 1: dn_tile<FMT, 1>(a, si, rb, c0, ks, i0, scale); break;
-      case 2: dn_tile<FMT, 2>(a, si, rb, c0, ks, i0, scale); break;
-      case 3: dn_tile<FMT, 3>(a, si, rb, c0, ks, i0, scale); break;
-      default: dn_tile<FMT, 4>(a, si, rb, c0, ks, i0, scale); break;
-    }
+  const int c0 = ks * a.cpu_dn;
+  for (int i0 = 0; i0 < si.n; i0 += KT) {
+    if (KT == 1 || si.n - i0 == 1) dn_tile<FMT, 1, KT>(a, si, rb, c0, ks, i0, scale, ls);
+    else dn_tile<FMT, KT, KT>(a, si, rb, c0, ks, i0, scale, ls);
   }
-  const uint32_t total = (uint32_t)a.ks * (uint32_t)(a.S + *a.n_unique);
-  if (!arrive_last(a.counters + rb, total)) return;
-  // Last unit of this row block: y[t] = sum_j w[t][j] * o_j + o_shared, in
-  // slot order, each o summed over K-segments in order.
+  const uint32_t nu = __builtin_amdgcn_readfirstlane(*a.n_unique);
+  if (!arrive_last(a.dn_cnt + rb, (uint32_t)a.ks_dn * ((uint32_t)a.S + nu))) return;
+  // last unit of this row block: y[t] = sum over the token's slots (routed
+  // slots in slot order, each summed over K-segments in order, times its
+  // routing weight) + the shared expert
   for (int t = 0; t < a.T; ++t) {
     float acc = 0.f;
     for (int j0 = 0; j0 < a.k + a.S; j0 += 8) {
-      // up to 8 slots' partials in flight at once, summed in slot order
       float o[8][kMaxSplit];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int row = (j < a.k) ? t * a.k + j : a.T * a.k + t;
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s)
-          if (j < a.k + a.S && s < a.ks) o[jj][s] = ld_dev(a.part + ((size_t)s * a.rows_total + row) * a.H + r);
+        for (int q = 0; q < kMaxSplit; ++q)
+          if (j < a.k + a.S && q < a.ks_dn) o[jj][q] = a.p_dn[((size_t)q * a.rows_total + row) * a.H + r];
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
@@ -389,8 +569,8 @@ __global__ __launch_bounds__(64) void k_dn_gemv(GemvArgs a) {
         if (j >= a.k + a.S) break;
         float v = 0.f;
 #pragma unroll
-        for (int s = 0; s < kMaxSplit; ++s)
-          if (s < a.ks) v += o[jj][s];
+        for (int q = 0; q < kMaxSplit; ++q)
+          if (q < a.ks_dn) v += o[jj][q];
         acc += (j < a.k) ? a.topk_w[t * a.k + j] * v : v;
       }
     }
@@ -398,51 +578,96 @@ __global__ __launch_bounds__(64) void k_dn_gemv(GemvArgs a) {
   }
 }
 
+// ---- kernels (one wavefront per unit) ---------------------------------------
+template <int FMT, int KT>
+__global__ __launch_bounds__(64) void k_route_phase(DecArgs a, const uint16_t* __restrict__ x) {
+  __shared__ UnionLds ls;
+  const int it = blockIdx.x;
+  if (it < a.n_router) {
+    router_unit(a, it, ls);
+  } else {
+    const int j = it - a.n_router;
+    gu_unit<FMT, KT>(a, x, 0, j / a.ks_gu, j % a.ks_gu);
+  }
+}
+
+template <int FMT, int KT>
+__global__ __launch_bounds__(64) void k_gu_phase(DecArgs a, const uint16_t* __restrict__ x) {
+  const int per_slot = (a.I / 64) * a.ks_gu;
+  const int j = blockIdx.x;
+  const int rem = j % per_slot;
+  gu_unit<FMT, KT>(a, x, a.S + j / per_slot, rem / a.ks_gu, rem % a.ks_gu);
+}
+
+template <int FMT, int KT>
+__global__ __launch_bounds__(64) void k_dn_phase(DecArgs a) {
+  __shared__ DnLds<KT> ls;
+  const int per_slot = (a.H / 64) * a.ks_dn;
+  const int j = blockIdx.x;
+  const int rem = j % per_slot;
+  dn_unit<FMT, KT>(a, j / per_slot, rem / a.ks_dn, rem % a.ks_dn, ls);
+}
+
+template <int FMT, int KT>
+hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, const StageEvents& se) {
+  const int gu_per_slot = (a.I / 64) * a.ks_gu, dn_per_slot = (a.H / 64) * a.ks_dn;
+  se.record(0, s);
+  hipLaunchKernelGGL((k_route_phase<FMT, KT>), dim3(a.n_router + a.S * gu_per_slot), dim3(64), 0, s, a, x);
+  se.record(1, s);
+  hipLaunchKernelGGL((k_gu_phase<FMT, KT>), dim3((a.slots_max - a.S) * gu_per_slot), dim3(64), 0, s, a, x);
+  se.record(2, s);
+  hipLaunchKernelGGL((k_dn_phase<FMT, KT>), dim3(a.slots_max * dn_per_slot), dim3(64), 0, s, a);
+  se.record(3, s);
+  return hipGetLastError();
+}
+
 }  // namespace
 
-hipError_t launch_decode_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,
-                                 const uint16_t* x, const Route& r, void* ws, uint16_t* y, hipStream_t s,
-                                 const StageEvents& se) {
-  GemvArgs a{};
-  a.slots = r.slots;
+hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
+                         const Route& r, void* ws, uint16_t* y, hipStream_t s, const StageEvents& se) {
+  DecArgs a{};
+  a.Wr = w.router_w;
+  a.rbias = w.router_b;
+  a.x = x;
+  a.experts = w.experts;
+  a.shared = w.shared;
+  a.T = p.T;
+  a.H = p.H;
+  a.I = p.I;
+  a.E = p.E;
+  a.k = p.k;
+  a.S = p.S;
+  a.L = layout_of(d);
+  a.y = y;
+  a.topk_idx = r.topk_idx;
+  a.topk_w = r.topk_w;
+  a.z = r.z;
   a.n_unique = r.n_unique;
   a.uniq_ids = r.uniq_ids;
   a.uniq_off = r.uniq_off;
   a.pairs = r.pairs;
-  a.topk_w = r.topk_w;
-  a.T = p.T;
-  a.H = p.H;
-  a.I = p.I;
-  a.k = p.k;
-  a.S = p.S;
-  a.rows_total = p.rows_total;
-  a.fmt = d.wfmt;
-  a.L = layout_of(d);
+  a.slots = r.slots;
   a.h = (uint16_t*)((char*)ws + p.h_off);
-  a.y = y;
-  // gate/up
-  a.part = (float*)((char*)ws + p.p_gu_off);
-  a.counters = (uint32_t*)ws + p.c_gu;
-  a.ks = p.ks_gu;
-  a.cpu = (p.H / 32) / p.ks_gu;
-  dim3 g1((unsigned)((p.I / 64) * p.ks_gu), (unsigned)p.slots_max);
-  se.record(1, s);
-  if (d.wfmt == MOE_W_INT4_ROW) hipLaunchKernelGGL(k_gu_gemv<MOE_W_INT4_ROW>, g1, dim3(64), 0, s, a, x);
-  else hipLaunchKernelGGL(k_gu_gemv<MOE_W_E2M1_B16>, g1, dim3(64), 0, s, a, x);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // down + combine
-  a.part = (float*)((char*)ws + p.p_dn_off);
-  a.counters = (uint32_t*)ws + p.c_dn;
-  a.ks = p.ks_dn;
-  a.cpu = (p.I / 32) / p.ks_dn;
-  dim3 g2((unsigned)((p.H / 64) * p.ks_dn), (unsigned)p.slots_max);
-  se.record(2, s);
-  if (d.wfmt == MOE_W_INT4_ROW) hipLaunchKernelGGL(k_dn_gemv<MOE_W_INT4_ROW>, g2, dim3(64), 0, s, a);
-  else hipLaunchKernelGGL(k_dn_gemv<MOE_W_E2M1_B16>, g2, dim3(64), 0, s, a);
-  e = hipGetLastError();
-  se.record(3, s);
-  return e;
+  a.p_gu = (float*)((char*)ws + p.p_gu_off);
+  a.p_dn = (float*)((char*)ws + p.p_dn_off);
+  a.sync = (uint32_t*)ws;
+  a.gu_cnt = a.sync + p.c_gu;
+  a.dn_cnt = a.sync + p.c_dn;
+  a.ks_gu = p.ks_gu;
+  a.ks_dn = p.ks_dn;
+  a.cpu_gu = (p.H / 32) / p.ks_gu;
+  a.cpu_dn = (p.I / 32) / p.ks_dn;
+  a.slots_max = p.slots_max;
+  a.rows_total = p.rows_total;
+  // router units: enough column segments that each needs one batch of loads
+  const int n4 = p.H / 4, per = 64 * kLogitsBatch;
+  a.rsplit = std::min(kMaxLogitParts, (n4 + per - 1) / per);
+  a.seg4 = (n4 + a.rsplit - 1) / a.rsplit;
+  a.n_router = p.E * a.rsplit;
+  // a single token never needs the two-token tiles, which cost registers
+  if (d.wfmt == MOE_W_INT4_ROW)
+    return p.T == 1 ? launch_phases<MOE_W_INT4_ROW, 1>(a, x, s, se) : launch_phases<MOE_W_INT4_ROW, 2>(a, x, s, se);
+  return p.T == 1 ? launch_phases<MOE_W_E2M1_B16, 1>(a, x, s, se) : launch_phases<MOE_W_E2M1_B16, 2>(a, x, s, se);
 }
 
 }  // namespace moe

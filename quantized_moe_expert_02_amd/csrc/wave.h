@@ -1,0 +1,195 @@
+// Wavefront-level helpers shared by the router kernels: DPP / permlane
+// butterflies, order-preserving keys for fp64 logits, and the top-k of one
+// token by one wavefront (k rounds of a wave-wide argmax).
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+constexpr int kWave = 64;
+constexpr int kMaxLogitParts = 5;  // partial-logit planes the workspace holds
+
+// Value held by the partner lane of a butterfly step.  Steps 1 and 2 use
+// quad permutes, 4 and 8 the half-row / row mirrors (which pair lanes of
+// groups that earlier steps already made uniform), 16 and 32 the gfx950
+// row-swap instructions.
+template <int STEP>
+__device__ __forceinline__ int partner(int v) {
+  if constexpr (STEP == 1) return __builtin_amdgcn_mov_dpp(v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  else if constexpr (STEP == 2) return __builtin_amdgcn_mov_dpp(v, 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
+  else if constexpr (STEP == 4) return __builtin_amdgcn_mov_dpp(v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  else if constexpr (STEP == 8) return __builtin_amdgcn_mov_dpp(v, 0x140, 0xF, 0xF, false);  // row_mirror
+  else if constexpr (STEP == 16) {
+    auto r = __builtin_amdgcn_permlane16_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 16) ? r[0] : r[1]);
+  } else {
+    auto r = __builtin_amdgcn_permlane32_swap((unsigned)v, (unsigned)v, false, false);
+    return (int)((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+}
+
+template <int STEP>
+__device__ __forceinline__ double partner_d(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)partner<STEP>((int)(uint32_t)u);
+  const uint32_t hi = (uint32_t)partner<STEP>((int)(uint32_t)(u >> 32));
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)partner<1>((int)v));
+  v = max(v, (uint32_t)partner<2>((int)v));
+  v = max(v, (uint32_t)partner<4>((int)v));
+  v = max(v, (uint32_t)partner<8>((int)v));
+  v = max(v, (uint32_t)partner<16>((int)v));
+  v = max(v, (uint32_t)partner<32>((int)v));
+  return v;
+}
+
+// Order-preserving map of a finite double onto uint64: a > b  <=>  key(a) > key(b).
+__device__ __forceinline__ uint64_t order_key(double v) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double from_order_key(uint64_t k) {
+  const uint64_t u = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+  return __builtin_bit_cast(double, u);
+}
+
+// Every lane ends with the wave-wide best (key, index): the largest key, ties
+// to the lower index.  The high key word is reduced first; only when more than
+// one lane holds that high word are the low word and the index reduced too.
+__device__ __forceinline__ void wave_argmax_key(uint64_t& key, int& idx) {
+  const uint32_t hi = (uint32_t)(key >> 32);
+  const uint32_t hmax = wave_max_u32(hi);
+  const uint64_t cand = __ballot(hi == hmax);
+  if (__popcll(cand) == 1) {
+    const int l = __ffsll((unsigned long long)cand) - 1;  // wave-uniform
+    key = ((uint64_t)hmax << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key, l);
+    idx = __builtin_amdgcn_readlane(idx, l);
+    return;
+  }
+  const uint32_t lo = (uint32_t)key;
+  const uint32_t lmax = wave_max_u32(hi == hmax ? lo : 0u);
+  const bool c2 = (hi == hmax) && (lo == lmax);
+  const uint32_t best_inv = wave_max_u32(c2 ? ~(uint32_t)idx : 0u);
+  key = ((uint64_t)hmax << 32) | lmax;
+  idx = (int)~best_inv;
+}
+
+// Top-k of one token's logits by one wavefront: k rounds of a wave-wide
+// argmax over the experts not yet taken.  Lane l holds experts l + 64 i.
+// Writes idx/w for slots 0..k-1 and the chosen experts to slot_expert.
+// The routing weights are formed in fp32: sigmoid of the fp64 logit, then
+// renormalised over the kept slots.
+// The logit of expert e is zrow[e], or with kCoherent the sum of nz partial
+// logits zrow[s * zstride + e] (s ascending) plus bias[e] when bias is set.
+template <int kPer, bool kCoherent>
+__device__ void topk_wave(const double* zrow, int nz, size_t zstride, const float* bias, int E, int k,
+                          int32_t* idx_out, float* w_out, int* slot_expert) {
+  // kCoherent: zrow holds partial logits written during this kernel by
+  // other workgroups (published before this wavefront waited, and not read
+  // before), and idx_out / w_out are read back by other workgroups of this
+  // kernel, so they are written with device-coherent stores.
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t key[kPer];
+  if (kCoherent) {
+    // planes are loaded PG at a time, so that at most ~20 doubles per lane
+    // are in flight
+    constexpr int PG = kPer >= 20 ? 1 : (20 / kPer < kMaxLogitParts ? 20 / kPer : kMaxLogitParts);
+    double v[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[i] = 0.0;
+    for (int s0 = 0; s0 < nz; s0 += PG) {
+      double zs[kPer][PG];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+#pragma unroll
+        for (int s = 0; s < PG; ++s) {
+          const int e = lane + i * kWave;
+          if (e < E && s0 + s < nz) zs[i][s] = zrow[(s0 + s) * zstride + e];
+        }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+#pragma unroll
+        for (int s = 0; s < PG; ++s)
+          if (s0 + s < nz) v[i] += zs[i][s];
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + i * kWave;
+      if (bias && e < E) v[i] += (double)bias[e];
+      key[i] = (e < E) ? order_key(v[i]) : 0ull;  // 0: below every finite key
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      const int e = lane + i * kWave;
+      key[i] = (e < E) ? order_key(zrow[e]) : 0ull;
+    }
+  }
+  uint64_t my_key = 0;
+  int my_e = -1;
+  for (int j = 0; j < k; ++j) {
+    uint64_t bk = 0;
+    int bi = 0x7FFFFFFF;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {  // ascending index, so '>' keeps the lower index on ties
+      if (key[i] > bk) {
+        bk = key[i];
+        bi = lane + i * kWave;
+      }
+    }
+    wave_argmax_key(bk, bi);
+    if ((bi & (kWave - 1)) == lane) {
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (lane + i * kWave == bi) key[i] = 0;
+    }
+    if (lane == j) {
+      my_key = bk;
+      my_e = bi;
+    }
+  }
+  const double my_z = from_order_key(my_key);
+  const float s = (lane < k) ? 1.0f / (1.0f + expf(-(float)my_z)) : 0.0f;
+  float tot = s;
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) tot += __shfl_xor(tot, m, kWave);
+  if (lane < k) {
+    if (kCoherent) {
+      st_dev(idx_out + lane, (int32_t)my_e);
+      st_dev(w_out + lane, s / tot);
+    } else {
+      idx_out[lane] = my_e;
+      w_out[lane] = s / tot;
+    }
+    if (slot_expert) slot_expert[lane] = my_e;
+  }
+}
+
+template <bool kCoherent>
+__device__ void topk_any(const double* zrow, int nz, size_t zstride, const float* bias, int E, int k,
+                         int32_t* idx_out, float* w_out, int* slot_expert) {
+  if (E <= 64) topk_wave<1, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
+  else if (E <= 128) topk_wave<2, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
+  else if (E <= 256) topk_wave<4, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
+  else if (E <= 512) topk_wave<8, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
+  else topk_wave<16, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
+}
+
+
+// Every lane ends with the wave-wide fp64 sum, added in a fixed butterfly order.
+__device__ __forceinline__ double wave_sum(double v) {
+  v += partner_d<1>(v);
+  v += partner_d<2>(v);
+  v += partner_d<4>(v);
+  v += partner_d<8>(v);
+  v += partner_d<16>(v);
+  v += partner_d<32>(v);
+  return v;
+}
+
+}  // namespace moe
