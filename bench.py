@@ -185,10 +185,11 @@ class _Hip:
 
 def time_stages(ch: Chain, reps: int):
     """Mean duration (ms) of each stage of a forward call, from HIP events
-    recorded by the library on its stream between stage launches."""
+    that the stage's first and last kernel dispatches record (start / end
+    timestamps of the dispatch packets, so launch overhead is excluded)."""
     hip = _Hip()
     L = len(ch.layers)
-    evs = [[hip.event() for _ in range(4)] for _ in range(reps * L)]
+    evs = [[hip.event() for _ in range(6)] for _ in range(reps * L)]
     torch.cuda.synchronize()
     torch.cuda._sleep(50_000_000)  # let the host queue every call before the GPU starts them
     i = 0
@@ -198,7 +199,7 @@ def time_stages(ch: Chain, reps: int):
             i += 1
     torch.cuda.synchronize()
     n = len(evs)
-    out = [sum(hip.elapsed_ms(e[j], e[j + 1]) for e in evs) / n for j in range(3)]
+    out = [sum(hip.elapsed_ms(e[2 * j], e[2 * j + 1]) for e in evs) / n for j in range(3)]
     for e in evs:
         for h in e:
             hip.destroy(h)
@@ -325,6 +326,9 @@ def main():
     ap.add_argument("--workload", default="decode_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--calibrate-copy-mb", type=int, default=0,
+                    help="first run a plain elementwise copy (torch.neg) over this many MB, so that hardware "
+                         "traffic counters taken over the run can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's EP/TP sharding "
@@ -332,6 +336,14 @@ def main():
         sys.exit(2)
     torch.cuda.init()
     moe.lib()
+    if args.calibrate_copy_mb:
+        n = args.calibrate_copy_mb * (1 << 20) // 2
+        src = torch.ones(n, dtype=torch.float16, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(4):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     ch, res, touched = run_workload(args.workload, args.layers, args.steps, args.warmup)
     d, T = ch.dims, ch.T

@@ -154,12 +154,17 @@ int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_
                       void* stream);
 
 /* moe_w4a16_forward with stage timing for benchmarks: `events` is a host
- * array of n_events hipEvent_t handles (passed as void*; entries may be
- * NULL).  events[i] is recorded on `stream` right before stage i is
- * launched and events[n_stages] right after the last stage, where the
- * stages are 0: routing and union, 1: gate/up projections + SwiGLU,
- * 2: down projections + combine (n_stages = 3).  Recording adds no
- * synchronisation.  Same arguments and results as moe_w4a16_forward. */
+ * array of n_events (0..6) hipEvent_t handles (passed as void*; entries may
+ * be NULL).  events[2i] and events[2i+1] take the start and end time of
+ * stage i, recorded by the dispatch of the stage's first and last kernel
+ * (so the interval holds the stage's kernels and the gaps between them, not
+ * the launch overhead around them).  Stages on the decode path (T <=
+ * moe_decode_max_tokens()): 0 routing + union + shared expert gate/up,
+ * 1 routed gate/up + SwiGLU, 2 down projections + combine.  On the
+ * grouped-GEMM path: 0 routing + union, 1 gate/up + SwiGLU, 2 down +
+ * combine.  Adds no synchronisation.  Same arguments and results as
+ * moe_w4a16_forward; n_events outside 0..6 or a NULL array with n_events
+ * > 0 gives MOE_E_INVAL. */
 int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
                                uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws,
                                size_t ws_bytes, void* stream, void* const* events, int32_t n_events);

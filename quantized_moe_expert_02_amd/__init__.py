@@ -238,9 +238,10 @@ def moe_w4a16_forward(layer: PackedLayer, x: torch.Tensor, y: Optional[torch.Ten
 
 def moe_w4a16_forward_profiled(layer: PackedLayer, x: torch.Tensor, y: torch.Tensor, ws: torch.Tensor, events,
                                stream=None) -> torch.Tensor:
-    """moe_w4a16_forward that records `events` (raw hipEvent_t handles as
-    ints, or None) before each stage and after the last: [route, gate/up,
-    down, end]."""
+    """moe_w4a16_forward that times its stages: `events` holds up to six raw
+    hipEvent_t handles (ints, or None); events[2i] / events[2i+1] take the
+    start / end of stage i (0 route, 1 gate/up, 2 down), recorded by the
+    stage's first / last kernel dispatch."""
     d = _dims(layer.dims)
     T = x.shape[0]
     handles = (ctypes.c_void_p * len(events))(*events)

@@ -223,8 +223,7 @@ static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint1
   if (topk_w_out) r.topk_w = topk_w_out;
   hipStream_t s = (hipStream_t)stream;
   if (p.decode) return launch_decode(*d, p, *w, x, r, ws, y, s, se) == hipSuccess ? MOE_OK : MOE_E_HIP;
-  se.record(0, s);
-  if (launch_route(*d, p, *w, x, r, true, s) != hipSuccess) return MOE_E_HIP;
+  if (launch_route(*d, p, *w, x, r, true, s, se.start(0), se.stop(0)) != hipSuccess) return MOE_E_HIP;
   return launch_prefill_experts(*d, p, *w, x, r, ws, y, s, se) == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
@@ -236,7 +235,7 @@ int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_
 int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
                                uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes,
                                void* stream, void* const* events, int32_t n_events) {
-  if (n_events < 0 || (n_events > 0 && !events)) return MOE_E_INVAL;
+  if (n_events < 0 || n_events > 6 || (n_events > 0 && !events)) return MOE_E_INVAL;
   return forward_impl(d, w, x, T, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream,
                       StageEvents{events, n_events});
 }

@@ -1,6 +1,7 @@
 // Internal declarations shared by the HIP translation units of the library.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -132,19 +133,29 @@ hipError_t launch_unpack(const moe_dims_t& d, const void* packed, void* qg, void
 // Routing and union.  With `with_slots`, also fills r.slots from w.experts
 // and w.shared (moe_w4a16_forward); moe_route passes false.
 hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
-                        const Route& r, bool with_slots, hipStream_t s);
-// Optional stage events (benchmark timing): ev[i] is recorded before stage
-// i and ev[n-1] after the last; null entries are skipped.
+                        const Route& r, bool with_slots, hipStream_t s, hipEvent_t ev_start = nullptr,
+                        hipEvent_t ev_stop = nullptr);
+// Optional stage events (benchmark timing): ev[2i] / ev[2i+1] take the
+// start / end of stage i, recorded by the dispatch packets of the stage's
+// first / last kernel (hipExtLaunchKernelGGL); null entries are skipped.
 struct StageEvents {
   void* const* ev;
   int n;
-  void record(int i, hipStream_t s) const {
-    if (ev && i < n && ev[i]) (void)hipEventRecord((hipEvent_t)ev[i], s);
-  }
+  hipEvent_t start(int i) const { return (ev && 2 * i < n) ? (hipEvent_t)ev[2 * i] : nullptr; }
+  hipEvent_t stop(int i) const { return (ev && 2 * i + 1 < n) ? (hipEvent_t)ev[2 * i + 1] : nullptr; }
 };
 
+// Kernel launch that optionally records events at the dispatch's start and
+// end.
+template <typename... KArgs, typename... Args>
+inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t s, hipEvent_t start, hipEvent_t stop,
+                     Args... args) {
+  if (start || stop) hipExtLaunchKernelGGL(kernel, grid, block, 0, s, start, stop, 0, args...);
+  else hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
+}
+
 // The whole layer for T <= kDecodeMaxTokens in three launches: route +
-// shared gate/up, routed gate/up, down (stage events 0..3 around them).
+// shared gate/up, routed gate/up, down (stages 0, 1, 2).
 hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
                          const Route& r, void* ws, uint16_t* y, hipStream_t s, const StageEvents& se);
 hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_weights_t& w,

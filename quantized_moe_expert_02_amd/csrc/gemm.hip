@@ -351,23 +351,19 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   const int mt8 = (prefill_max_tiles(p.T, p.k, p.E, p.S) + 7) / 8 * 8;
   const int rows_per_wg = 64 * kGemmWaves;
   const int nx_gu = (p.I + rows_per_wg - 1) / rows_per_wg, nx_dn = (p.H + rows_per_wg - 1) / rows_per_wg;
-  se.record(1, s);
   const dim3 blk(64 * kGemmWaves);
   if (d.wfmt == MOE_W_INT4_ROW)
-    hipLaunchKernelGGL((k_expert_gemm<MOE_W_INT4_ROW, 2>), dim3(mt8 * nx_gu), blk, 0, s, a, nx_gu);
+    launch_k(k_expert_gemm<MOE_W_INT4_ROW, 2>, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
   else
-    hipLaunchKernelGGL((k_expert_gemm<MOE_W_E2M1_B16, 2>), dim3(mt8 * nx_gu), blk, 0, s, a, nx_gu);
+    launch_k(k_expert_gemm<MOE_W_E2M1_B16, 2>, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  se.record(2, s);
   if (d.wfmt == MOE_W_INT4_ROW)
-    hipLaunchKernelGGL((k_expert_gemm<MOE_W_INT4_ROW, 1>), dim3(mt8 * nx_dn), blk, 0, s, a, nx_dn);
+    launch_k(k_expert_gemm<MOE_W_INT4_ROW, 1>, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
   else
-    hipLaunchKernelGGL((k_expert_gemm<MOE_W_E2M1_B16, 1>), dim3(mt8 * nx_dn), blk, 0, s, a, nx_dn);
-  hipLaunchKernelGGL(k_combine, dim3((p.H + 255) / 256, p.T), dim3(256), 0, s, a);
-  e = hipGetLastError();
-  se.record(3, s);
-  return e;
+    launch_k(k_expert_gemm<MOE_W_E2M1_B16, 1>, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
+  launch_k(k_combine, dim3((p.H + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
+  return hipGetLastError();
 }
 
 }  // namespace moe

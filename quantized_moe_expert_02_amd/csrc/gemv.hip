@@ -611,13 +611,9 @@ __global__ __launch_bounds__(64) void k_dn_phase(DecArgs a) {
 template <int FMT, int KT>
 hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, const StageEvents& se) {
   const int gu_per_slot = (a.I / 64) * a.ks_gu, dn_per_slot = (a.H / 64) * a.ks_dn;
-  se.record(0, s);
-  hipLaunchKernelGGL((k_route_phase<FMT, KT>), dim3(a.n_router + a.S * gu_per_slot), dim3(64), 0, s, a, x);
-  se.record(1, s);
-  hipLaunchKernelGGL((k_gu_phase<FMT, KT>), dim3((a.slots_max - a.S) * gu_per_slot), dim3(64), 0, s, a, x);
-  se.record(2, s);
-  hipLaunchKernelGGL((k_dn_phase<FMT, KT>), dim3(a.slots_max * dn_per_slot), dim3(64), 0, s, a);
-  se.record(3, s);
+  launch_k(k_route_phase<FMT, KT>, dim3(a.n_router + a.S * gu_per_slot), dim3(64), s, se.start(0), se.stop(0), a, x);
+  launch_k(k_gu_phase<FMT, KT>, dim3((a.slots_max - a.S) * gu_per_slot), dim3(64), s, se.start(1), se.stop(1), a, x);
+  launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * dn_per_slot), dim3(64), s, se.start(2), se.stop(2), a);
   return hipGetLastError();
 }
 

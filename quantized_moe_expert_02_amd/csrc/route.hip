@@ -274,7 +274,8 @@ __global__ __launch_bounds__(256) void k_union_scatter(RouteArgs a) {
 }  // namespace
 
 hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
-                        const Route& r, bool with_slots, hipStream_t s) {
+                        const Route& r, bool with_slots, hipStream_t s, hipEvent_t ev_start,
+                        hipEvent_t ev_stop) {
   RouteArgs a{};
   a.Wr = w.router_w;
   a.b = w.router_b;
@@ -304,14 +305,15 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
   {
     RouteArgs b = a;
     b.z = r.z + (size_t)p.T * p.E;  // K-split partials live after z
-    hipLaunchKernelGGL(k_logits_tiled, dim3((p.T + LT - 1) / LT, (p.E + LE - 1) / LE, kLogitSplit), dim3(256), 0, s, b);
+    launch_k(k_logits_tiled, dim3((p.T + LT - 1) / LT, (p.E + LE - 1) / LE, kLogitSplit), dim3(256), s, ev_start,
+             nullptr, b);
     const size_t n = (size_t)p.T * p.E;
     hipLaunchKernelGGL(k_logits_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
   }
   hipLaunchKernelGGL(k_topk, dim3((p.T + 3) / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_union_count, dim3(a.n_chunks), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, s, a);
-  hipLaunchKernelGGL(k_union_scatter, dim3(a.n_chunks), dim3(256), 0, s, a);
+  launch_k(k_union_scatter, dim3(a.n_chunks), dim3(256), s, nullptr, ev_stop, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,124 @@
+"""Short text summaries of rocprofv3 output for the profiles/ folder.
+
+  python -m quantized_moe_expert_02_amd.profile_summary stats DB_OR_DIR --title T --command C
+      per-kernel calls and average / min / max duration from a --kernel-trace run
+  python -m quantized_moe_expert_02_amd.profile_summary traffic FETCH_DIR WRITE_DIR --kernel K --copy-mb N
+      --workload W --source FILE --command C
+      HBM traffic per launch of kernel K from a FETCH_SIZE run and a WRITE_SIZE run (rocprofv3 --pmc,
+      --output-format csv), each scaled by what the same counter reads for the plain copy kernel that
+      `bench.py --calibrate-copy-mb N` runs first (N MB read and N MB written per launch)
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import os
+import sqlite3
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+COPY_KERNEL = "neg"  # torch.neg(src, out=dst): one read and one write of the tensor
+
+
+def _short(name: str) -> str:
+    n = name.replace("(anonymous namespace)::", "").replace("void ", "")
+    return n.split("(")[0]
+
+
+def _find(path: str, pattern: str) -> str:
+    if os.path.isfile(path):
+        return path
+    hits = sorted(glob.glob(os.path.join(path, "**", pattern), recursive=True))
+    if not hits:
+        sys.exit(f"no {pattern} under {path}")
+    return hits[0]
+
+
+def stats(args) -> None:
+    db = _find(args.path, "*results.db")
+    con = sqlite3.connect(db)
+    rows = list(con.execute("select name, count(*), avg(end-start), min(end-start), max(end-start), sum(end-start) "
+                            "from kernels group by name order by sum(end-start) desc"))
+    print(f"# {args.title}")
+    print(f"# command: {args.command}")
+    print("# kernel durations from rocprofv3 --kernel-trace, in us; this library's kernels (moe::) only")
+    print(f"{'calls':>6} {'avg_us':>9} {'min_us':>9} {'max_us':>9} {'total_us':>11}  kernel")
+    for n, c, a, mi, ma, s in rows:
+        k = _short(n)
+        if k.startswith("moe::"):
+            print(f"{c:6d} {a / 1e3:9.2f} {mi / 1e3:9.2f} {ma / 1e3:9.2f} {s / 1e3:11.1f}  {k[:110]}")
+
+
+def _counter(path: str, counter: str):
+    """{short kernel name: [values per dispatch]} for one counter (KiB per dispatch as rocprofv3 reports)."""
+    f = _find(path, "*counter_collection.csv")
+    out = {}
+    with open(f) as fh:
+        for row in csv.DictReader(fh):
+            if row.get("Counter_Name") != counter:
+                continue
+            out.setdefault(_short(row["Kernel_Name"]), []).append(float(row["Counter_Value"]))
+    return out
+
+
+def traffic(args) -> None:
+    fetch = _counter(args.fetch_dir, "FETCH_SIZE")
+    write = _counter(args.write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        hits = [v for k, v in d.items() if key in k]
+        if not hits:
+            sys.exit(f"kernel matching {key!r} not found; kernels: {sorted(d)[:20]}")
+        vals = [x for h in hits for x in h]
+        return sum(vals) / len(vals), len(vals)
+
+    copy_bytes = args.copy_mb * (1 << 20)
+    cf, _ = pick(fetch, COPY_KERNEL)
+    cw, _ = pick(write, COPY_KERNEL)
+    f_scale = copy_bytes / (cf * 1024.0)
+    w_scale = copy_bytes / (cw * 1024.0)
+    kf, nf = pick(fetch, args.kernel)
+    kw, nw = pick(write, args.kernel)
+    fetch_b = kf * 1024.0 * f_scale
+    write_b = kw * 1024.0 * w_scale
+    src = os.path.join(ROOT, args.source)
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    print(f"# HBM traffic per launch of {args.kernel} ({args.workload}), rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+    print(f"# command: {args.command}")
+    print(f"# copy calibration: torch.neg over {args.copy_mb} MB reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE "
+          f"{cw:.0f} KiB per launch; scale factors fetch {f_scale:.4f}, write {w_scale:.4f}")
+    print(f"kernel = {args.kernel}")
+    print(f"workload = {args.workload}")
+    print(f"dispatches = {nf} / {nw}")
+    print(f"fetch_kib_per_dispatch = {kf:.1f}")
+    print(f"write_kib_per_dispatch = {kw:.1f}")
+    print(f"fetch_bytes_per_launch = {fetch_b:.0f}")
+    print(f"write_bytes_per_launch = {write_b:.0f}")
+    print(f"bytes_per_launch = {fetch_b + write_b:.0f}")
+    print(f"source = {args.source}")
+    print(f"source_sha256 = {sha}")
+
+
+def main() -> None:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="mode", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("path")
+    a.add_argument("--title", required=True)
+    a.add_argument("--command", required=True)
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_dir")
+    b.add_argument("write_dir")
+    b.add_argument("--kernel", required=True)
+    b.add_argument("--copy-mb", type=int, required=True)
+    b.add_argument("--workload", required=True)
+    b.add_argument("--source", required=True)
+    b.add_argument("--command", required=True)
+    args = ap.parse_args()
+    stats(args) if args.mode == "stats" else traffic(args)
+
+
+if __name__ == "__main__":
+    main()
