@@ -21,6 +21,15 @@ int split_factor(int K, int fmax) {
   return 1;
 }
 
+// Split of the shared expert's gate/up: up to 16 K-segments, in groups of
+// four wavefronts (a split above 4 is a multiple of 4).
+int shared_split(int K) {
+  const int g = K / 128;
+  for (int f = 16; f > 4; f -= 4)
+    if (g % f == 0) return f;
+  return split_factor(K, 4);
+}
+
 int check_dims(const moe_dims_t* d) {
   if (!d) return MOE_E_INVAL;
   if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts || d->hidden <= 0 || d->inter <= 0)
@@ -48,8 +57,10 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.decode = T <= kDecodeMaxTokens;
   q.slots_max = q.S + (int)std::min<int64_t>(q.E, (int64_t)T * q.k);
   q.rows_total = T * q.k + T;
-  q.ks_gu = split_factor(q.H, 8);
-  q.ks_dn = split_factor(q.I, 2);
+  // decode K-splits: one wavefront per K-segment, four per workgroup
+  q.ks_gu = split_factor(q.H, 4);  // routed experts
+  q.ks_sgu = shared_split(q.H);    // shared expert, streamed while routing
+  q.ks_dn = split_factor(q.I, 4);
   // Counters: the first 256 words for route-stage counters, then one per
   // (slot, gate/up row block) for the largest decode batch, then one per
   // down row block.
@@ -78,8 +89,9 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.slots_off = off; off = up256(off + (size_t)q.slots_max * sizeof(SlotEntry));
   q.h_off = off; off = up256(off + (size_t)q.rows_total * q.I * 2);
   if (q.decode) {
-    q.p_gu_off = off; off = up256(off + (size_t)q.ks_gu * q.rows_total * 2 * q.I * 4);
-    q.p_dn_off = off; off = up256(off + (size_t)q.ks_dn * q.rows_total * q.H * 4);
+    const int sgu_groups = q.ks_sgu > 4 ? q.ks_sgu / 4 : 1;
+    q.p_gu_off = off; off = up256(off + (size_t)sgu_groups * q.rows_total * 2 * q.I * 4);
+    q.p_dn_off = off; off = up256(off + (size_t)q.rows_total * q.H * 4);
   } else {
     q.p_gu_off = 0;
     q.p_dn_off = off; off = up256(off + (size_t)q.rows_total * q.H * 4);

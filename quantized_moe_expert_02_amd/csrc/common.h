@@ -85,7 +85,7 @@ struct Plan {
   int T, H, I, E, k, S;      // S = has_shared
   int slots_max;             // S + min(E, T*k)
   int rows_total;            // T*k + T: h / partial rows (pair rows then shared rows)
-  int ks_gu, ks_dn;          // split-K factors of the GEMV path
+  int ks_gu, ks_sgu, ks_dn;  // split-K factors of the GEMV path (routed / shared gate/up, down)
   bool decode;               // GEMV path
   // counters (uint32), offsets in elements from ws base
   size_t c_route, c_gu, c_dn, n_counters;

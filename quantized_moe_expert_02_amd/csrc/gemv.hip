@@ -26,7 +26,7 @@ namespace moe {
 namespace {
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-constexpr int kMaxSplit = 8;  // largest split-K factor of the GEMV kernels
+constexpr int kMaxSplit = 8;  // largest split-K factor of the down projection
 // Global-address-space views, so weight loads compile to global_load (not
 // flat_load, which also occupies the LDS/scalar wait counter).
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -183,29 +183,32 @@ __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const 
 }
 
 // ===========================================================================
-// Decode path: three launches per layer, one wavefront per work unit.
-//   k_route_phase  router units (fp64 partial logits of one expert over one
-//                  column segment, for all tokens; the last router unit to
-//                  finish takes every token's top-k and forms the batch union
-//                  and slot table), and the shared expert's gate/up units,
-//                  which need no routing
-//   k_gu_phase     gate/up units of the routed slots
-//   k_dn_phase     down units of every slot (shared expert first)
-// Units: gate/up (slot, 64-row block, K-segment), down (slot, 64-row output
-// block, K-segment).  A gate/up unit writes fp32 partial sums; the last unit
-// of a (slot, row block) forms h for those rows (row scales, SwiGLU).  The
-// last down unit of an output row block combines the slots in a fixed order
-// (routing-weighted, shared expert last) into y.  "Last" is decided by
-// device-scope arrival counters, which that unit returns to zero, so every
-// call starts from zeroed counters.  Data handed to another workgroup of the
-// same launch is written with device-coherent stores and read after the
-// arrival that publishes it (common.h); the launch boundaries order the
-// phases, so no unit ever waits for another.
+// Decode path: three launches per layer.  Workgroups are four wavefronts
+// (fewer workgroups to dispatch per launch).
+//   k_route_phase  router workgroups: four independent router units each
+//                  (fp64 partial logits of one expert over one column
+//                  segment, for all tokens); the last router unit to finish
+//                  takes every token's top-k and forms the batch union and
+//                  slot table.  Shared-expert workgroups: gate/up of one
+//                  64-row block over four K-segments, which need no routing.
+//   k_gu_phase     one workgroup per (routed slot, 64-row block): its
+//                  wavefronts stream the K-segments, reduce through LDS in a
+//                  fixed order and form h (row scales, SwiGLU)
+//   k_dn_phase     one workgroup per (slot, 64-row output block): K-segments
+//                  reduced through LDS into the slot's scaled partial; the
+//                  last slot of a row block combines all slots in a fixed
+//                  order (routing-weighted, shared expert last) into y
+// "Last" is decided by device-scope arrival counters, which that unit
+// returns to zero, so every call starts from zeroed counters.  Data handed
+// to another workgroup of the same launch is written with device-coherent
+// stores and read after the arrival that publishes it (common.h); the launch
+// boundaries order the phases, so no unit ever waits for another.
 // ===========================================================================
 
+constexpr int kWpg = 4;           // wavefronts per workgroup
 constexpr int kStageChunks = 32;  // h columns staged in LDS per step: 32 x 32
 constexpr int kGuDepth = 2;       // gate/up: 4-chunk batches in flight (16 KiB)
-constexpr int kDnDepth = 4;       // down: 4-chunk batches in flight (16 KiB)
+constexpr int kDnDepth = 2;       // down: 4-chunk batches in flight (8 KiB)
 constexpr int kSyRouter = 128;    // router arrival counter (uint32 index in the sync region)
 
 struct DecArgs {
@@ -226,15 +229,17 @@ struct DecArgs {
   int32_t* pairs;
   SlotEntry* slots;
   uint16_t* h;
-  float* p_gu;
-  float* p_dn;
+  float* p_gu;        // shared expert: one partial plane per group of K-segments
+  float* p_dn;        // [rows_total][H] scaled slot partials
   uint32_t* sync;
-  uint32_t* gu_cnt;   // [slots][I/64]
+  uint32_t* gu_cnt;   // [I/64] shared-expert groups
   uint32_t* dn_cnt;   // [H/64]
-  int ks_gu, ks_dn, cpu_gu, cpu_dn;
+  int ks_gu, ks_sgu, ks_dn;     // K-segments: routed gate/up, shared gate/up, down
+  int cpu_gu, cpu_sgu, cpu_dn;  // 32-column chunks per K-segment
   int slots_max, rows_total;
   int rsplit, seg4;   // router units per expert, 16-byte columns per router unit
   int n_router;       // E * rsplit
+  int n_router_wg;    // workgroups of router units
 };
 
 struct SlotInfo {
@@ -275,7 +280,7 @@ __device__ __forceinline__ void slot_token(const DecArgs& a, const SlotInfo& si,
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 // Arrival on a counter shared by `total` units: true for the last one, which
-// also returns the counter to zero.
+// also returns the counter to zero.  Called by one whole wavefront.
 __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total) {
   if (publish_arrival(counter) != total - 1) return false;
   if ((threadIdx.x & 63) == 0) st_dev(counter, 0u);
@@ -283,26 +288,40 @@ __device__ __forceinline__ bool arrive_last(uint32_t* counter, uint32_t total) {
   return true;
 }
 
+// Orders one wavefront's LDS accesses at this point (the other wavefronts of
+// the workgroup run independent units, so no workgroup barrier is used).
+// A wavefront's LDS operations complete in issue order; this keeps the
+// compiler from moving them across.
+__device__ __forceinline__ void wave_lds_sync() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ---- batch union ----------------------------------------------------------
 // Unique experts in ascending order, their pair lists (pairs of one expert
 // in token order) and the slot table, from per-expert token bitmasks in LDS:
 // the rank of pair (t, j) within its expert is the number of earlier tokens
-// that chose the same expert.  pe[] holds the expert of every pair.
+// that chose the same expert.  pe[] holds the expert of every pair.  Run by
+// one wavefront.
 struct UnionLds {
   uint32_t mask[kMaxExperts];  // tokens per expert (bit t)
   int base[kMaxExperts];       // first pair of each expert
   int pe[kDecodeMaxTokens * kMaxTopK];
 };
 
-__device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
+// Lane l owns experts [l*per, l*per + per); ep[i] is the packed pointer of
+// its i-th expert, loaded ahead by the caller.
+constexpr int kMaxPer = kMaxExperts / 64;
+__device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const uint8_t* const (&ep)[kMaxPer]) {
   const int lane = threadIdx.x & 63;
   const int P = a.T * a.k;
   const int per = (a.E + 63) / 64;
   const int e0 = lane * per, e1 = min(a.E, e0 + per);
   for (int e = e0; e < e1; ++e) ls.mask[e] = 0;
-  __syncthreads();
+  wave_lds_sync();
   for (int p = lane; p < P; p += 64) atomicOr(&ls.mask[ls.pe[p]], 1u << (p / a.k));
-  __syncthreads();
+  wave_lds_sync();
   int cnt = 0, pres = 0;
   for (int e = e0; e < e1; ++e) {
     const int c = __popc(ls.mask[e]);
@@ -317,20 +336,24 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
   }
   const int excl = v - ((pres << 16) | cnt);
   int up = excl >> 16, uc = excl & 0xFFFF;
-  for (int e = e0; e < e1; ++e) {
-    const int c = __popc(ls.mask[e]);
-    ls.base[e] = uc;
-    if (c > 0) {
-      a.uniq_ids[up] = e;
-      a.uniq_off[up] = uc;
-      SlotEntry se;
-      se.base = (const uint8_t*)a.experts[e];
-      se.n = c;
-      se.p0 = uc;
-      a.slots[a.S + up] = se;
-      ++up;
+#pragma unroll
+  for (int i = 0; i < kMaxPer; ++i) {
+    const int e = e0 + i;
+    if (i < per && e < e1) {
+      const int c = __popc(ls.mask[e]);
+      ls.base[e] = uc;
+      if (c > 0) {
+        a.uniq_ids[up] = e;
+        a.uniq_off[up] = uc;
+        SlotEntry se;
+        se.base = ep[i];
+        se.n = c;
+        se.p0 = uc;
+        a.slots[a.S + up] = se;
+        ++up;
+      }
+      uc += c;
     }
-    uc += c;
   }
   const int tot = __builtin_amdgcn_readlane(v, 63);
   const int nu = tot >> 16;
@@ -339,7 +362,7 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
     a.uniq_off[nu] = tot & 0xFFFF;
   }
   for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
-  __syncthreads();
+  wave_lds_sync();
   for (int p = lane; p < P; p += 64) {
     const int e = ls.pe[p];
     const int t = p / a.k;
@@ -350,7 +373,7 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
 // ---- router unit: fp64 partial logits of expert e over one column segment --
 // Segment s of expert e writes plane s of z ([plane][T][E]).  The last unit
 // to finish adds the planes in order and the bias, takes each token's top-k
-// and runs the union.
+// and runs the union.  One wavefront.
 constexpr int kLogitsBatch = 12;  // 16-byte router loads in flight per lane
 __device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& ls) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -397,57 +420,55 @@ __device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& 
     }
   }
   if (!arrive_last(a.sync + kSyRouter, (uint32_t)a.n_router)) return;
+  // the expert pointers the union needs are requested first, so that they
+  // arrive while the logits are loaded and ranked
+  const uint8_t* ep[kMaxPer];
+  {
+    const int per = (a.E + 63) / 64, e0 = lane * per;
+#pragma unroll
+    for (int i = 0; i < kMaxPer; ++i)
+      ep[i] = (i < per && e0 + i < a.E) ? (const uint8_t*)a.experts[e0 + i] : nullptr;
+  }
   for (int t = 0; t < a.T; ++t)
     topk_any<true>(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k,
                    a.topk_idx + (size_t)t * a.k, a.topk_w + (size_t)t * a.k, ls.pe + t * a.k);
-  __syncthreads();
-  union_step(a, ls);
+  wave_lds_sync();
+  union_step(a, ls, ep);
 }
 
-// ---- gate/up unit -----------------------------------------------------------
+// ---- gate/up: one (slot, 64-row block) per workgroup --------------------------
+// Wavefront w streams K-segment q0 + w of the block for a tile of NT tokens;
+// the four results meet in LDS and wavefront 0 adds them in segment order.
+template <int KT>
+struct GuLds {
+  float r[kWpg][2][KT][64];
+};
+
 template <int FMT, int NT>
-__device__ __forceinline__ void gu_tile(const DecArgs& a, const uint16_t* __restrict__ x, const SlotInfo& si,
-                                        int rb, int c0, int ks, int i0) {
+__device__ __forceinline__ void gu_stream(const DecArgs& a, const uint16_t* __restrict__ x, const SlotInfo& si,
+                                          int rb, int ks, int nch, int i0, float (&acc)[2][NT]) {
   const int lane = threadIdx.x & 63;
+  const int c0 = ks * nch;
   const guint4* w = (const guint4*)(si.base + a.L.gu_off) + ((size_t)rb * (a.H / 32) + c0) * 2 * 64 + lane;
   const guint2* sc = nullptr;
   if (FMT == MOE_W_E2M1_B16)
     sc = (const guint2*)(si.base + a.L.sgu_off) + ((size_t)rb * (a.H / 128) + c0 / 4) * 2 * 64 + lane;
   const cu32x4* act[NT];  // x is read-only during the launch
-  int rows[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int tok, row;
     slot_token(a, si, i0 + t, tok, row);
-    rows[t] = row;
     act[t] = (const cu32x4*)(x + (size_t)tok * a.H + 32 * c0);
   }
-  float acc[2][NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[0][t] = acc[1][t] = 0.f;
-  stream_ring<FMT, 2, NT, kGuDepth>(w, sc, act, a.cpu_gu, acc, [] {});
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float* pr = a.p_gu + (((size_t)ks * a.rows_total + rows[t]) * 2) * a.I + 64 * rb + lane;
-    st_dev(pr, acc[0][t]);
-    st_dev(pr + a.I, acc[1][t]);
-  }
+  stream_ring<FMT, 2, NT, kGuDepth>(w, sc, act, nch, acc, [] {});
 }
 
-template <int FMT, int KT>
-__device__ __forceinline__ void gu_unit(const DecArgs& a, const uint16_t* __restrict__ x, int s, int rb, int ks) {
-  SlotInfo si;
-  if (!get_slot(a, s, si)) return;
-  const int c0 = ks * a.cpu_gu;
-  for (int i0 = 0; i0 < si.n; i0 += KT) {
-    if (KT == 1 || si.n - i0 == 1) gu_tile<FMT, 1>(a, x, si, rb, c0, ks, i0);
-    else gu_tile<FMT, KT>(a, x, si, rb, c0, ks, i0);
-  }
-  if (!arrive_last(a.gu_cnt + (size_t)s * (a.I / 64) + rb, (uint32_t)a.ks_gu)) return;
-  // last K-segment of this (slot, row block): reduce in segment order, row
-  // scales, SwiGLU, h
-  const int lane = threadIdx.x & 63;
-  const int r = 64 * rb + lane;
+// h for token row `row` of this block from its gate/up sums (wavefront 0).
+template <int FMT>
+__device__ __forceinline__ void gu_finish(const DecArgs& a, const SlotInfo& si, int rb, int row, float g, float u) {
+  const int r = 64 * rb + (threadIdx.x & 63);
   float sg, su;
   if (FMT == MOE_W_INT4_ROW) {
     sg = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sg_off)[r]);
@@ -457,83 +478,154 @@ __device__ __forceinline__ void gu_unit(const DecArgs& a, const uint16_t* __rest
     sg = g3[0];
     su = g3[1];
   }
-  for (int i = 0; i < si.n; ++i) {
-    int tok, row;
-    slot_token(a, si, i, tok, row);
-    float pg[kMaxSplit], pu[kMaxSplit];
-#pragma unroll
-    for (int q = 0; q < kMaxSplit; ++q) {
-      if (q < a.ks_gu) {
-        const float* pr = a.p_gu + (((size_t)q * a.rows_total + row) * 2) * a.I + r;
-        pg[q] = pr[0];
-        pu[q] = pr[a.I];
-      }
-    }
-    float g = 0.f, u = 0.f;
-#pragma unroll
-    for (int q = 0; q < kMaxSplit; ++q)
-      if (q < a.ks_gu) {
-        g += pg[q];
-        u += pu[q];
-      }
-    const float hv = silu(g * sg) * (u * su);
-    a.h[(size_t)row * a.I + r] = __builtin_bit_cast(uint16_t, (_Float16)hv);  // read by the next launch
-  }
+  const float hv = silu(g * sg) * (u * su);
+  a.h[(size_t)row * a.I + r] = __builtin_bit_cast(uint16_t, (_Float16)hv);  // read by the next launch
 }
 
-// ---- down unit ----------------------------------------------------------------
-// h rows come through LDS: vector loads of h mixed into the weight stream
-// would make every weight batch wait for them (the vector memory counter
-// retires in order).  Each step of kStageChunks chunks requests its first
-// weight batches, then stages the NT h row pieces into LDS while those are
-// in flight, then streams.
-template <int KT>
-struct DnLds {
-  u32x4 h[KT * kStageChunks * 4];  // KT tokens x 32 chunks x 64 B
-};
-
+// K-segments [grp*nw, grp*nw + nw) of (slot s, row block rb), nw <= kWpg
+// wavefronts (the others only join the barriers).  With ngrp == 1 the
+// workgroup forms h; otherwise each group writes its sum as partial plane
+// grp and the last group to arrive adds the planes in order and forms h.
 template <int FMT, int NT, int KT>
-__device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, int rb, int c0, int ks, int i0,
-                                        float scale, DnLds<KT>& ls) {
-  const int lane = threadIdx.x & 63;
-  const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / 32) + c0) * 64 + lane;
-  const guint2* sc = nullptr;
-  if (FMT == MOE_W_E2M1_B16)
-    sc = (const guint2*)(si.base + a.L.sdd_off) + ((size_t)rb * (a.I / 128) + c0 / 4) * 64 + lane;
-  const lu32x4* act[NT];  // LDS
+__device__ __forceinline__ void gu_tile_group(const DecArgs& a, const uint16_t* __restrict__ x, const SlotInfo& si,
+                                              int s, int rb, int grp, int ngrp, int nw, int nch, int i0,
+                                              GuLds<KT>& ls) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave < nw) {
+    float acc[2][NT];
+    gu_stream<FMT, NT>(a, x, si, rb, grp * nw + wave, nch, i0, acc);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) act[t] = (const lu32x4*)(ls.h + t * kStageChunks * 4);
-  int rows[NT];
-  float acc[1][NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) acc[0][t] = 0.f;
-  for (int p0 = 0; p0 < a.cpu_dn; p0 += kStageChunks) {
-    const int np = min(kStageChunks, a.cpu_dn - p0);
-    __syncthreads();  // the previous step's LDS reads are done
-    // the weight batches are requested first; the pair lookups and h loads
-    // follow while they are in flight
-    stream_ring<FMT, 1, NT, kDnDepth>(
-        w + (size_t)p0 * 64, FMT == MOE_W_E2M1_B16 ? sc + (size_t)(p0 / 4) * 64 : sc, act, np, acc, [&] {
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            int tok, row;
-            slot_token(a, si, i0 + t, tok, row);
-            rows[t] = row;
-            const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)row * a.I + 32 * c0);
-            for (int q = lane; q < np * 4; q += 64) ls.h[t * kStageChunks * 4 + q] = src[p0 * 4 + q];
-          }
-          __syncthreads();
-        });
+    for (int t = 0; t < NT; ++t) {
+      ls.r[wave][0][t][lane] = acc[0][t];
+      ls.r[wave][1][t][lane] = acc[1][t];
+    }
   }
+  __syncthreads();
+  if (wave == 0) {
 #pragma unroll
-  for (int t = 0; t < NT; ++t)
-    st_dev(a.p_dn + ((size_t)ks * a.rows_total + rows[t]) * a.H + 64 * rb + lane, acc[0][t] * scale);
+    for (int t = 0; t < NT; ++t) {
+      float g = 0.f, u = 0.f;
+      for (int q = 0; q < nw; ++q) {
+        g += ls.r[q][0][t][lane];
+        u += ls.r[q][1][t][lane];
+      }
+      int tok, row;
+      slot_token(a, si, i0 + t, tok, row);
+      if (ngrp == 1) {
+        gu_finish<FMT>(a, si, rb, row, g, u);
+      } else {
+        float* pr = a.p_gu + (((size_t)grp * a.rows_total + row) * 2) * a.I + 64 * rb + lane;
+        st_dev(pr, g);
+        st_dev(pr + a.I, u);
+      }
+    }
+  }
+  __syncthreads();  // LDS is reused by the next tile
 }
 
 template <int FMT, int KT>
-__device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rb, int ks, DnLds<KT>& ls) {
+__device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __restrict__ x, int s, int rb, int grp,
+                                         int ngrp, int nw, int nch, GuLds<KT>& ls) {
   SlotInfo si;
-  if (!get_slot(a, s, si)) return;
+  if (!get_slot(a, s, si)) return;  // uniform over the workgroup
+  for (int i0 = 0; i0 < si.n; i0 += KT) {
+    if (KT == 1 || si.n - i0 == 1) gu_tile_group<FMT, 1, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, ls);
+    else gu_tile_group<FMT, KT, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, ls);
+  }
+  if (ngrp == 1 || threadIdx.x >= 64) return;
+  if (!arrive_last(a.gu_cnt + rb, (uint32_t)ngrp)) return;
+  const int lane = threadIdx.x & 63;
+  for (int i = 0; i < si.n; ++i) {
+    int tok, row;
+    slot_token(a, si, i, tok, row);
+    float g = 0.f, u = 0.f;
+    for (int q0 = 0; q0 < ngrp; q0 += 8) {  // planes in order, loaded 8 at a time
+      float pg[8], pu[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        if (q0 + q < ngrp) {
+          const float* pr = a.p_gu + (((size_t)(q0 + q) * a.rows_total + row) * 2) * a.I + 64 * rb + lane;
+          pg[q] = pr[0];
+          pu[q] = pr[a.I];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q)
+        if (q0 + q < ngrp) {
+          g += pg[q];
+          u += pu[q];
+        }
+    }
+    gu_finish<FMT>(a, si, rb, row, g, u);
+  }
+}
+
+// ---- down: one (slot, 64-row output block) per workgroup ------------------------
+// Wavefront w streams K-segment w for a tile of NT tokens, with its h row
+// pieces staged in its own LDS region: vector loads of h mixed into the
+// weight stream would make every weight batch wait for them (the vector
+// memory counter retires in order), so each step of kStageChunks chunks
+// requests its first weight batches, then stages h while those are in
+// flight, then streams.
+template <int KT>
+struct DnLds {
+  u32x4 h[kWpg][KT * kStageChunks * 4];  // per wavefront: KT tokens x 32 chunks x 64 B
+  float r[kWpg][KT][64];
+};
+
+template <int FMT, int NT, int KT>
+__device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, int rb, int nw, int i0, float scale,
+                                        DnLds<KT>& ls) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave < nw) {
+    const int c0 = wave * a.cpu_dn;
+    const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / 32) + c0) * 64 + lane;
+    const guint2* sc = nullptr;
+    if (FMT == MOE_W_E2M1_B16)
+      sc = (const guint2*)(si.base + a.L.sdd_off) + ((size_t)rb * (a.I / 128) + c0 / 4) * 64 + lane;
+    u32x4* hl = ls.h[wave];
+    const lu32x4* act[NT];  // LDS
+#pragma unroll
+    for (int t = 0; t < NT; ++t) act[t] = (const lu32x4*)(hl + t * kStageChunks * 4);
+    float acc[1][NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[0][t] = 0.f;
+    for (int p0 = 0; p0 < a.cpu_dn; p0 += kStageChunks) {
+      const int np = min(kStageChunks, a.cpu_dn - p0);
+      wave_lds_sync();  // the previous step's LDS reads are done
+      stream_ring<FMT, 1, NT, kDnDepth>(
+          w + (size_t)p0 * 64, FMT == MOE_W_E2M1_B16 ? sc + (size_t)(p0 / 4) * 64 : sc, act, np, acc, [&] {
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+              int tok, row;
+              slot_token(a, si, i0 + t, tok, row);
+              const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)row * a.I + 32 * c0);
+              for (int q = lane; q < np * 4; q += 64) hl[t * kStageChunks * 4 + q] = src[p0 * 4 + q];
+            }
+            wave_lds_sync();
+          });
+    }
+#pragma unroll
+    for (int t = 0; t < NT; ++t) ls.r[wave][t][lane] = acc[0][t];
+  }
+  __syncthreads();
+  if (wave == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      float v = 0.f;
+      for (int q = 0; q < nw; ++q) v += ls.r[q][t][lane];
+      int tok, row;
+      slot_token(a, si, i0 + t, tok, row);
+      st_dev(a.p_dn + (size_t)row * a.H + 64 * rb + lane, v * scale);
+    }
+  }
+  __syncthreads();  // LDS is reused by the next tile
+}
+
+template <int FMT, int KT>
+__device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rb, DnLds<KT>& ls) {
+  SlotInfo si;
+  if (!get_slot(a, s, si)) return;  // uniform over the workgroup
   const int lane = threadIdx.x & 63;
   const int r = 64 * rb + lane;
   float scale;
@@ -541,79 +633,76 @@ __device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rb, int ks,
     scale = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sd_off)[r]);
   else
     scale = reinterpret_cast<const float*>(si.base + a.L.g3_off)[2];
-  const int c0 = ks * a.cpu_dn;
+  const int nw = a.ks_dn;
   for (int i0 = 0; i0 < si.n; i0 += KT) {
-    if (KT == 1 || si.n - i0 == 1) dn_tile<FMT, 1, KT>(a, si, rb, c0, ks, i0, scale, ls);
-    else dn_tile<FMT, KT, KT>(a, si, rb, c0, ks, i0, scale, ls);
+    if (KT == 1 || si.n - i0 == 1) dn_tile<FMT, 1, KT>(a, si, rb, nw, i0, scale, ls);
+    else dn_tile<FMT, KT, KT>(a, si, rb, nw, i0, scale, ls);
   }
+  if (threadIdx.x >= 64) return;
   const uint32_t nu = __builtin_amdgcn_readfirstlane(*a.n_unique);
-  if (!arrive_last(a.dn_cnt + rb, (uint32_t)a.ks_dn * ((uint32_t)a.S + nu))) return;
-  // last unit of this row block: y[t] = sum over the token's slots (routed
-  // slots in slot order, each summed over K-segments in order, times its
-  // routing weight) + the shared expert
+  if (!arrive_last(a.dn_cnt + rb, (uint32_t)a.S + nu)) return;
+  // last slot of this row block: y[t] = sum over the token's slots in slot
+  // order, routed ones times their routing weight, shared expert last
   for (int t = 0; t < a.T; ++t) {
     float acc = 0.f;
     for (int j0 = 0; j0 < a.k + a.S; j0 += 8) {
-      float o[8][kMaxSplit];
+      float o[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int row = (j < a.k) ? t * a.k + j : a.T * a.k + t;
-#pragma unroll
-        for (int q = 0; q < kMaxSplit; ++q)
-          if (j < a.k + a.S && q < a.ks_dn) o[jj][q] = a.p_dn[((size_t)q * a.rows_total + row) * a.H + r];
+        if (j < a.k + a.S) o[jj] = a.p_dn[(size_t)row * a.H + r];
       }
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         if (j >= a.k + a.S) break;
-        float v = 0.f;
-#pragma unroll
-        for (int q = 0; q < kMaxSplit; ++q)
-          if (q < a.ks_dn) v += o[jj][q];
-        acc += (j < a.k) ? a.topk_w[t * a.k + j] * v : v;
+        acc += (j < a.k) ? a.topk_w[t * a.k + j] * o[jj] : o[jj];
       }
     }
     a.y[(size_t)t * a.H + r] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
 }
 
-// ---- kernels (one wavefront per unit) ---------------------------------------
+// ---- kernels ---------------------------------------------------------------------
 template <int FMT, int KT>
-__global__ __launch_bounds__(64) void k_route_phase(DecArgs a, const uint16_t* __restrict__ x) {
-  __shared__ UnionLds ls;
-  const int it = blockIdx.x;
-  if (it < a.n_router) {
-    router_unit(a, it, ls);
-  } else {
-    const int j = it - a.n_router;
-    gu_unit<FMT, KT>(a, x, 0, j / a.ks_gu, j % a.ks_gu);
+__global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint16_t* __restrict__ x) {
+  __shared__ UnionLds ul;
+  __shared__ GuLds<KT> gl;
+  const int b = blockIdx.x;
+  if (b < a.n_router_wg) {
+    const int it = b * kWpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (it < a.n_router) router_unit(a, it, ul);
+    return;
   }
+  // shared expert: workgroup = (row block, group of kWpg K-segments)
+  const int nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw;
+  const int j = b - a.n_router_wg;
+  gu_group<FMT, KT>(a, x, 0, j / ngrp, j % ngrp, ngrp, nw, a.cpu_sgu, gl);
 }
 
 template <int FMT, int KT>
-__global__ __launch_bounds__(64) void k_gu_phase(DecArgs a, const uint16_t* __restrict__ x) {
-  const int per_slot = (a.I / 64) * a.ks_gu;
-  const int j = blockIdx.x;
-  const int rem = j % per_slot;
-  gu_unit<FMT, KT>(a, x, a.S + j / per_slot, rem / a.ks_gu, rem % a.ks_gu);
+__global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_t* __restrict__ x) {
+  __shared__ GuLds<KT> gl;
+  const int per_slot = a.I / 64;
+  gu_group<FMT, KT>(a, x, a.S + blockIdx.x / per_slot, blockIdx.x % per_slot, 0, 1, a.ks_gu, a.cpu_gu, gl);
 }
 
 template <int FMT, int KT>
-__global__ __launch_bounds__(64) void k_dn_phase(DecArgs a) {
-  __shared__ DnLds<KT> ls;
-  const int per_slot = (a.H / 64) * a.ks_dn;
-  const int j = blockIdx.x;
-  const int rem = j % per_slot;
-  dn_unit<FMT, KT>(a, j / per_slot, rem / a.ks_dn, rem % a.ks_dn, ls);
+__global__ __launch_bounds__(64 * kWpg) void k_dn_phase(DecArgs a) {
+  __shared__ DnLds<KT> dl;
+  const int per_slot = a.H / 64;
+  dn_unit<FMT, KT>(a, blockIdx.x / per_slot, blockIdx.x % per_slot, dl);
 }
 
 template <int FMT, int KT>
 hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, const StageEvents& se) {
-  const int gu_per_slot = (a.I / 64) * a.ks_gu, dn_per_slot = (a.H / 64) * a.ks_dn;
-  launch_k(k_route_phase<FMT, KT>, dim3(a.n_router + a.S * gu_per_slot), dim3(64), s, se.start(0), se.stop(0), a, x);
-  launch_k(k_gu_phase<FMT, KT>, dim3((a.slots_max - a.S) * gu_per_slot), dim3(64), s, se.start(1), se.stop(1), a, x);
-  launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * dn_per_slot), dim3(64), s, se.start(2), se.stop(2), a);
+  const int nw = min(kWpg, a.ks_sgu);
+  const int sgu_wg = a.S * (a.I / 64) * (a.ks_sgu / nw);
+  const dim3 blk(64 * kWpg);
+  launch_k(k_route_phase<FMT, KT>, dim3(a.n_router_wg + sgu_wg), blk, s, se.start(0), se.stop(0), a, x);
+  launch_k(k_gu_phase<FMT, KT>, dim3((a.slots_max - a.S) * (a.I / 64)), blk, s, se.start(1), se.stop(1), a, x);
+  launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * (a.H / 64)), blk, s, se.start(2), se.stop(2), a);
   return hipGetLastError();
 }
 
@@ -650,8 +739,10 @@ hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t
   a.gu_cnt = a.sync + p.c_gu;
   a.dn_cnt = a.sync + p.c_dn;
   a.ks_gu = p.ks_gu;
+  a.ks_sgu = p.ks_sgu;
   a.ks_dn = p.ks_dn;
   a.cpu_gu = (p.H / 32) / p.ks_gu;
+  a.cpu_sgu = (p.H / 32) / p.ks_sgu;
   a.cpu_dn = (p.I / 32) / p.ks_dn;
   a.slots_max = p.slots_max;
   a.rows_total = p.rows_total;
@@ -660,6 +751,7 @@ hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t
   a.rsplit = std::min(kMaxLogitParts, (n4 + per - 1) / per);
   a.seg4 = (n4 + a.rsplit - 1) / a.rsplit;
   a.n_router = p.E * a.rsplit;
+  a.n_router_wg = (a.n_router + kWpg - 1) / kWpg;
   // a single token never needs the two-token tiles, which cost registers
   if (d.wfmt == MOE_W_INT4_ROW)
     return p.T == 1 ? launch_phases<MOE_W_INT4_ROW, 1>(a, x, s, se) : launch_phases<MOE_W_INT4_ROW, 2>(a, x, s, se);
