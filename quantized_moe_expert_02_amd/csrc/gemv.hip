@@ -209,7 +209,8 @@ constexpr int kWpg = 4;           // wavefronts per workgroup
 constexpr int kStageChunks = 32;  // h columns staged in LDS per step: 32 x 32
 constexpr int kGuDepth = 2;       // gate/up: 4-chunk batches in flight (16 KiB)
 constexpr int kDnDepth = 2;       // down: 4-chunk batches in flight (8 KiB)
-constexpr int kSyRouter = 128;    // router arrival counter (uint32 index in the sync region)
+constexpr int kSyRouter = 64;     // router arrival counters (uint32 index in the sync region):
+constexpr int kRouterGroups = 8;  //   top counter, then one per group of router workgroups
 
 struct DecArgs {
   const float* Wr;
@@ -375,7 +376,26 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const
 // to finish adds the planes in order and the bias, takes each token's top-k
 // and runs the union.  One wavefront.
 constexpr int kLogitsBatch = 12;  // 16-byte router loads in flight per lane
-__device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& ls) {
+// Arrival of a router unit.  Five hundred arrivals on one counter queue up
+// behind each other at the memory, so they are counted in three levels: the
+// wavefronts of a workgroup in LDS, then one counter per group of
+// workgroups, then the top counter.  True for the last unit overall.
+__device__ __forceinline__ bool router_arrive(const DecArgs& a, uint32_t* wg_cnt) {
+  const int b = blockIdx.x;
+  const uint32_t units = (uint32_t)min(kWpg, a.n_router - b * kWpg);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this unit's logit stores are done
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint32_t prev = 0;
+  if ((threadIdx.x & 63) == 0) prev = atomicAdd(wg_cnt, 1u);
+  if ((uint32_t)__builtin_amdgcn_readfirstlane(prev) != units - 1) return false;
+  const int ng = min(kRouterGroups, a.n_router_wg), g = b % ng;
+  const uint32_t in_group = (uint32_t)((a.n_router_wg - g + ng - 1) / ng);
+  if (!arrive_last(a.sync + kSyRouter + 16 * (1 + g), in_group)) return false;
+  return arrive_last(a.sync + kSyRouter, (uint32_t)ng);
+}
+
+__device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& ls, uint32_t* wg_cnt) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int e = it / a.rsplit, seg = it % a.rsplit;
   const int lane = threadIdx.x & 63;
@@ -419,7 +439,7 @@ __device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& 
       if (lane == 0) st_dev(a.z + ((size_t)seg * a.T + t) * a.E + e, v);
     }
   }
-  if (!arrive_last(a.sync + kSyRouter, (uint32_t)a.n_router)) return;
+  if (!router_arrive(a, wg_cnt)) return;
   // the expert pointers the union needs are requested first, so that they
   // arrive while the logits are loaded and ranked
   const uint8_t* ep[kMaxPer];
@@ -669,10 +689,13 @@ template <int FMT, int KT>
 __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint16_t* __restrict__ x) {
   __shared__ UnionLds ul;
   __shared__ GuLds<KT> gl;
+  __shared__ uint32_t wg_cnt;
   const int b = blockIdx.x;
   if (b < a.n_router_wg) {
+    if (threadIdx.x == 0) wg_cnt = 0;
+    __syncthreads();  // all four wavefronts are present at the start
     const int it = b * kWpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (it < a.n_router) router_unit(a, it, ul);
+    if (it < a.n_router) router_unit(a, it, ul, &wg_cnt);
     return;
   }
   // shared expert: workgroup = (row block, group of kWpg K-segments)
