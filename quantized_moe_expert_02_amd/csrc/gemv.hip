@@ -372,30 +372,24 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const
 }
 
 // ---- router unit: fp64 partial logits of expert e over one column segment --
-// Segment s of expert e writes plane s of z ([plane][T][E]).  The last unit
-// to finish adds the planes in order and the bias, takes each token's top-k
-// and runs the union.  One wavefront.
+// Segment s of expert e writes plane s of z ([plane][T][E]); the top-k step
+// adds the planes in order and the bias.  One wavefront.
 constexpr int kLogitsBatch = 12;  // 16-byte router loads in flight per lane
-// Arrival of a router unit.  Five hundred arrivals on one counter queue up
-// behind each other at the memory, so they are counted in three levels: the
-// wavefronts of a workgroup in LDS, then one counter per group of
-// workgroups, then the top counter.  True for the last unit overall.
-__device__ __forceinline__ bool router_arrive(const DecArgs& a, uint32_t* wg_cnt) {
+// Arrival of a router workgroup (after all of its units): five hundred
+// arrivals on one counter queue up behind each other at the memory, so the
+// workgroups arrive on one of kRouterGroups group counters and the last of
+// each group on the top counter.  True for the last workgroup overall.
+// Called by wavefront 0 after a workgroup barrier; every wavefront has
+// waited for its own logit stores before that barrier.
+__device__ __forceinline__ bool router_arrive(const DecArgs& a) {
   const int b = blockIdx.x;
-  const uint32_t units = (uint32_t)min(kWpg, a.n_router - b * kWpg);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);  // this unit's logit stores are done
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  uint32_t prev = 0;
-  if ((threadIdx.x & 63) == 0) prev = atomicAdd(wg_cnt, 1u);
-  if ((uint32_t)__builtin_amdgcn_readfirstlane(prev) != units - 1) return false;
   const int ng = min(kRouterGroups, a.n_router_wg), g = b % ng;
   const uint32_t in_group = (uint32_t)((a.n_router_wg - g + ng - 1) / ng);
   if (!arrive_last(a.sync + kSyRouter + 16 * (1 + g), in_group)) return false;
   return arrive_last(a.sync + kSyRouter, (uint32_t)ng);
 }
 
-__device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& ls, uint32_t* wg_cnt) {
+__device__ __forceinline__ void router_unit(const DecArgs& a, int it) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int e = it / a.rsplit, seg = it % a.rsplit;
   const int lane = threadIdx.x & 63;
@@ -439,7 +433,26 @@ __device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& 
       if (lane == 0) st_dev(a.z + ((size_t)seg * a.T + t) * a.E + e, v);
     }
   }
-  if (!router_arrive(a, wg_cnt)) return;
+}
+
+// Router units of one workgroup; the last workgroup then takes the top-k of
+// every token (tokens spread over its wavefronts) and forms the union.
+__device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls) {
+  __shared__ int s_last;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int it = blockIdx.x * kWpg + wave;
+  if (it < a.n_router) router_unit(a, it);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // this wavefront's logit stores are done
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (wave == 0) {
+    const bool last = router_arrive(a);
+    if (lane == 0) s_last = last;
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // the expert pointers the union needs are requested first, so that they
   // arrive while the logits are loaded and ranked
   const uint8_t* ep[kMaxPer];
@@ -447,13 +460,15 @@ __device__ __forceinline__ void router_unit(const DecArgs& a, int it, UnionLds& 
     const int per = (a.E + 63) / 64, e0 = lane * per;
 #pragma unroll
     for (int i = 0; i < kMaxPer; ++i)
-      ep[i] = (i < per && e0 + i < a.E) ? (const uint8_t*)a.experts[e0 + i] : nullptr;
+      ep[i] = (wave == 0 && i < per && e0 + i < a.E) ? (const uint8_t*)a.experts[e0 + i] : nullptr;
   }
-  for (int t = 0; t < a.T; ++t)
-    topk_any<true>(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k,
-                   a.topk_idx + (size_t)t * a.k, a.topk_w + (size_t)t * a.k, ls.pe + t * a.k);
-  wave_lds_sync();
-  union_step(a, ls, ep);
+  const int tpw = (a.T + kWpg - 1) / kWpg;
+  const int t0 = wave * tpw, t1 = min(a.T, t0 + tpw);
+  for (int t = t0; t < t1; ++t)
+    topk_tokens(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k, 1, a.topk_idx + t * a.k,
+                a.topk_w + t * a.k, ls.pe + t * a.k);
+  __syncthreads();
+  if (wave == 0) union_step(a, ls, ep);
 }
 
 // ---- gate/up: one (slot, 64-row block) per workgroup --------------------------
@@ -689,13 +704,9 @@ template <int FMT, int KT>
 __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint16_t* __restrict__ x) {
   __shared__ UnionLds ul;
   __shared__ GuLds<KT> gl;
-  __shared__ uint32_t wg_cnt;
   const int b = blockIdx.x;
   if (b < a.n_router_wg) {
-    if (threadIdx.x == 0) wg_cnt = 0;
-    __syncthreads();  // all four wavefronts are present at the start
-    const int it = b * kWpg + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (it < a.n_router) router_unit(a, it, ul, &wg_cnt);
+    router_workgroup(a, ul);
     return;
   }
   // shared expert: workgroup = (row block, group of kWpg K-segments)

@@ -181,6 +181,150 @@ __device__ void topk_any(const double* zrow, int nz, size_t zstride, const float
 }
 
 
+// Top-k of NT tokens at once by one wavefront (the NT rank searches are
+// independent chains, so interleaving them hides their latency).  Same
+// result as topk_wave per token.  Token t's logit of expert e is the sum of
+// nz partial logits z[s * zstride + t * E + e] (s ascending) plus bias[e]
+// when bias is set; partial logits were written by other workgroups of this
+// kernel and published before this wavefront read them.  Each lane first
+// sorts the kPer logits it holds (descending; equal logits keep ascending
+// expert order), then each of the k rounds takes the wave-wide largest head
+// (ties to the lower expert index) and the winning lane pops it.  Outputs
+// are written with device-coherent stores: idx_out[t * k + j], w_out[...],
+// and slot_expert[t * k + j] (LDS) if set.
+template <int kPer, int NT>
+__device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
+                           int32_t* idx_out, float* w_out, int* slot_expert) {
+  const int lane = threadIdx.x & (kWave - 1);
+  double v[NT][kPer];
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) v[t][i] = 0.0;
+  for (int s = 0; s < nz; ++s) {
+    double zs[NT][kPer];
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int e = lane + i * kWave;
+        zs[t][i] = (e < E) ? z[s * zstride + (size_t)t * E + e] : 0.0;
+      }
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) v[t][i] += zs[t][i];
+  }
+  uint64_t key[NT][kPer];
+  int idx[NT][kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + i * kWave;
+    const double b = (bias && e < E) ? (double)bias[e] : 0.0;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      key[t][i] = (e < E) ? order_key(bias ? v[t][i] + b : v[t][i]) : 0ull;  // 0: below every finite key
+      idx[t][i] = e;
+    }
+  }
+  // per-lane sort, descending; a swap only on a strictly larger key keeps
+  // equal keys in ascending expert order
+#pragma unroll
+  for (int pass = 0; pass < kPer - 1; ++pass)
+#pragma unroll
+    for (int i = 0; i < kPer - 1 - pass; ++i)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const bool sw = key[t][i + 1] > key[t][i];
+        const uint64_t k0 = key[t][i], k1 = key[t][i + 1];
+        const int i0 = idx[t][i], i1 = idx[t][i + 1];
+        key[t][i] = sw ? k1 : k0;
+        key[t][i + 1] = sw ? k0 : k1;
+        idx[t][i] = sw ? i1 : i0;
+        idx[t][i + 1] = sw ? i0 : i1;
+      }
+  uint64_t my_key[NT];
+  int my_e[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    my_key[t] = 0;
+    my_e[t] = -1;
+  }
+  for (int j = 0; j < k; ++j) {
+    uint32_t hmax[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) hmax[t] = wave_max_u32((uint32_t)(key[t][0] >> 32));
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const uint32_t hi = (uint32_t)(key[t][0] >> 32);
+      const uint64_t cand = __ballot(hi == hmax[t]);
+      int win;
+      if (__popcll(cand) == 1) {
+        win = __ffsll((unsigned long long)cand) - 1;
+      } else {  // equal high words: compare the low words, then the expert index
+        const uint32_t lo = (uint32_t)key[t][0];
+        const uint32_t lmax = wave_max_u32(hi == hmax[t] ? lo : 0u);
+        const bool c2 = (hi == hmax[t]) && (lo == lmax);
+        const uint32_t best_inv = wave_max_u32(c2 ? ~(uint32_t)idx[t][0] : 0u);
+        win = (int)(~best_inv) & (kWave - 1);
+      }
+      const uint64_t wk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key[t][0] >> 32), win) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[t][0], win);
+      const int we = __builtin_amdgcn_readlane(idx[t][0], win);
+      if (lane == j) {
+        my_key[t] = wk;
+        my_e[t] = we;
+      }
+      if (lane == win) {
+#pragma unroll
+        for (int i = 0; i < kPer - 1; ++i) {
+          key[t][i] = key[t][i + 1];
+          idx[t][i] = idx[t][i + 1];
+        }
+        key[t][kPer - 1] = 0;
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const double my_z = from_order_key(my_key[t]);
+    const float s = (lane < k) ? 1.0f / (1.0f + expf(-(float)my_z)) : 0.0f;
+    float tot = s;
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1) tot += __shfl_xor(tot, m, kWave);
+    if (lane < k) {
+      st_dev(idx_out + t * k + lane, (int32_t)my_e[t]);
+      st_dev(w_out + t * k + lane, s / tot);
+      if (slot_expert) slot_expert[t * k + lane] = my_e[t];
+    }
+  }
+}
+
+// Top-k of T tokens (z, outputs and slot_expert indexed as in topk_multi),
+// one token at a time (ranking several together gains little: the rounds
+// are bound by instruction issue, not latency).
+template <int kPer>
+__device__ __forceinline__ void topk_tokens_per(const double* z, int nz, size_t zstride, const float* bias, int E, int k, int T,
+                                int32_t* idx_out, float* w_out, int* slot_expert) {
+  constexpr int NT = 1;
+  int t0 = 0;
+  for (; t0 + NT <= T; t0 += NT)
+    topk_multi<kPer, NT>(z + (size_t)t0 * E, nz, zstride, bias, E, k, idx_out + t0 * k, w_out + t0 * k,
+                         slot_expert + t0 * k);
+  for (; t0 < T; ++t0)
+    topk_multi<kPer, 1>(z + (size_t)t0 * E, nz, zstride, bias, E, k, idx_out + t0 * k, w_out + t0 * k,
+                        slot_expert + t0 * k);
+}
+
+__device__ __forceinline__ void topk_tokens(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
+                                            int T, int32_t* idx_out, float* w_out, int* slot_expert) {
+  if (E <= 64) topk_tokens_per<1>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
+  else if (E <= 128) topk_tokens_per<2>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
+  else if (E <= 256) topk_tokens_per<4>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
+  else if (E <= 512) topk_tokens_per<8>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
+  else topk_tokens_per<16>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
+}
+
 // Every lane ends with the wave-wide fp64 sum, added in a fixed butterfly order.
 __device__ __forceinline__ double wave_sum(double v) {
   v += partner_d<1>(v);
