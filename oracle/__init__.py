@@ -46,9 +46,9 @@ def lib():
         L.oracle_e4m3_values.argtypes = [P, i64, P]
         L.oracle_dequant.argtypes = [i32, P, P, ctypes.c_float, i32, i32, P]
         L.oracle_dequant.restype = i32
-        L.oracle_route.argtypes = [P, P, i32, P, P, P, P, P, P, P, P, P]
+        L.oracle_route.argtypes = [P, ctypes.c_double, P, i32, P, P, P, P, P, P, P, P, P]
         L.oracle_route.restype = i32
-        L.oracle_forward.argtypes = [P, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P, i32]
+        L.oracle_forward.argtypes = [P, ctypes.c_double, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P, i32]
         L.oracle_forward.restype = i32
         L.oracle_max_threads.restype = i32
         _lib = L
@@ -126,7 +126,10 @@ class Route:
         self.pairs = pairs
 
 
-def route(dims, x, router_w, router_b, want_z: bool = True) -> Route:
+def route(dims, x, router_w, router_b, want_z: bool = True, top_p: Optional[float] = None) -> Route:
+    """Routing and union; top_p defaults to dims.top_p (0: plain top-k)."""
+    if top_p is None:
+        top_p = float(getattr(dims, "top_p", 0.0))
     d = np.asarray(dims.as_tuple() if hasattr(dims, "as_tuple") else dims, dtype=np.int32)
     H, I, E, k = int(d[0]), int(d[1]), int(d[2]), int(d[3])
     xb = _np(x)
@@ -140,7 +143,7 @@ def route(dims, x, router_w, router_b, want_z: bool = True) -> Route:
     ids = np.full(cap, -1, dtype=np.int32)
     off = np.full(cap + 1, -1, dtype=np.int32)
     pairs = np.full(max(1, T * k), -1, dtype=np.int32)
-    rc = lib().oracle_route(_ptr(d), _ptr(xb), T, _ptr(wr), _ptr(rb), _ptr(idx), _ptr(w),
+    rc = lib().oracle_route(_ptr(d), float(top_p), _ptr(xb), T, _ptr(wr), _ptr(rb), _ptr(idx), _ptr(w),
                             _ptr(z) if z is not None else None, _ptr(nu), _ptr(ids), _ptr(off), _ptr(pairs))
     if rc != 0:
         raise ValueError("oracle_route rejected its arguments")
@@ -185,7 +188,7 @@ def forward(layer, x, tokens: Optional[Sequence[int]] = None, threads: int = 0,
         tl = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32))
         n = tl.size
     y = np.empty((n, d.hidden), dtype=np.float64)
-    rc = lib().oracle_forward(_ptr(dims), ptrs["qg"], ptrs["sg"], ptrs["qu"], ptrs["su"], ptrs["qd"], ptrs["sd"],
+    rc = lib().oracle_forward(_ptr(dims), float(getattr(d, "top_p", 0.0)), ptrs["qg"], ptrs["sg"], ptrs["qu"], ptrs["su"], ptrs["qd"], ptrs["sd"],
                               _ptr(g3), _ptr(wr), _ptr(rb), _ptr(xb), T, _ptr(tl) if tl is not None else None,
                               n, _ptr(y), int(threads))
     if rc == -2:

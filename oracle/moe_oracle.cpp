@@ -147,12 +147,54 @@ void expert_ffn(const Dims& d, const Expert& ex, const double* x, double* hbuf, 
   }
 }
 
+// Adaptive top-p over the k ranked slots ("Show HN: 低速のコンピュータでGLM
+// 5.2を動かす方法", hakusoku.com, section 実装済み機能: the --topp option that
+// keeps experts until their cumulative weight reaches p).  Reading taken:
+// keep the shortest prefix of the k slots whose cumulative renormalised
+// weight reaches p, then renormalise over the kept slots.  The decision
+// (an integer) is taken in the GPU path's precision, binary32: s_j =
+// 1 / (1 + exp(-z_j)) from the logit rounded to binary32, their sum over the
+// slots as a pairwise tree over 64 lanes (slots beyond k are zero), w_j =
+// s_j / sum, then the prefix sums in slot order compared with p rounded to
+// binary32.  Returns the number of kept slots, m (k when p <= 0 or p >= 1).
+int top_p_keep(const double* zk, int k, double top_p) {
+  if (!(top_p > 0.0 && top_p < 1.0)) return k;
+  float v[64];
+  for (int j = 0; j < 64; ++j) {
+    if (j < k) {
+      const float zf = (float)zk[j];
+      v[j] = 1.0f / (1.0f + std::exp(-zf));
+    } else {
+      v[j] = 0.0f;
+    }
+  }
+  float s[64];
+  std::memcpy(s, v, sizeof s);
+  for (int width = 1; width < 64; width *= 2)  // butterfly: every lane holds the same tree sum
+    for (int j = 0; j < 64; j += 2 * width)
+      for (int i = j; i < j + width; ++i) {
+        const float sum = v[i] + v[i + width];
+        v[i] = sum;
+        v[i + width] = sum;
+      }
+  const float tot = v[0];
+  const float p = (float)top_p;
+  float cum = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    cum += s[j] / tot;
+    if (cum >= p) return j + 1;
+  }
+  return k;
+}
+
 // Router for one token.  Reading taken: logits in fp64,
 // z_e = b_e + sum_h x_h * Wr[e][h] in ascending h; all experts sorted by
 // (z descending, expert index ascending) so equal logits go to the lower
 // index; the first k are kept in that order; s_j = sigmoid(z_j) and the kept
-// weights are renormalised to sum to one, w_j = s_j / sum s.
-void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const float* b,
+// weights are renormalised to sum to one, w_j = s_j / sum s.  With adaptive
+// top-p only the first m slots are kept (top_p_keep) and renormalised over
+// those; slots j >= m get index -1 and weight 0.
+void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const float* b, double top_p,
                  int* idx, double* w, double* z) {
   std::vector<double> xd(d.H);
   for (int h = 0; h < d.H; ++h) xd[h] = fp16_value(xrow[h]);
@@ -168,14 +210,21 @@ void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const flo
     if (z[a] != z[c]) return z[a] > z[c];
     return a < c;
   });
+  std::vector<double> zk(d.k);
+  for (int j = 0; j < d.k; ++j) zk[j] = z[order[j]];
+  const int m = top_p_keep(zk.data(), d.k, top_p);
   double ssum = 0.0;
   std::vector<double> s(d.k);
-  for (int j = 0; j < d.k; ++j) {
+  for (int j = 0; j < m; ++j) {
     idx[j] = order[j];
-    s[j] = 1.0 / (1.0 + std::exp(-z[order[j]]));
+    s[j] = 1.0 / (1.0 + std::exp(-zk[j]));
     ssum += s[j];
   }
-  for (int j = 0; j < d.k; ++j) w[j] = s[j] / ssum;
+  for (int j = 0; j < m; ++j) w[j] = s[j] / ssum;
+  for (int j = m; j < d.k; ++j) {
+    idx[j] = -1;
+    w[j] = 0.0;
+  }
 }
 
 bool dims_ok(const Dims& d) {
@@ -217,10 +266,12 @@ int oracle_dequant(int32_t fmt, const uint8_t* q, const void* s, float g, int32_
 // Routing and the batch union.
 //   dims: int32[6] = {H, I, E, k, has_shared, fmt}
 //   x: binary16 bits [T][H]; Wr: fp32 [E][H]; b: fp32 [E] or NULL
+//   top_p: adaptive top-p threshold (0 keeps all k slots)
 //   outputs: topk_idx int32 [T][k], topk_w fp32 [T][k], z fp64 [T][E] (nullable),
 //   n_unique int32[1], uniq_ids int32[min(E,T*k)], uniq_off int32[min(E,T*k)+1],
-//   pairs int32[T*k] (pair id t*k+j, grouped by expert ascending, tokens ascending).
-int oracle_route(const int32_t* dims, const uint16_t* x, int32_t T, const float* Wr, const float* b,
+//   pairs int32[T*k] (pair id t*k+j of the kept slots, grouped by expert
+//   ascending, tokens ascending; uniq_off[n_unique] = number of kept pairs).
+int oracle_route(const int32_t* dims, double top_p, const uint16_t* x, int32_t T, const float* Wr, const float* b,
                  int32_t* topk_idx, float* topk_w, double* z_out, int32_t* n_unique, int32_t* uniq_ids,
                  int32_t* uniq_off, int32_t* pairs) {
   const Dims d = to_dims(dims);
@@ -229,7 +280,7 @@ int oracle_route(const int32_t* dims, const uint16_t* x, int32_t T, const float*
 #pragma omp parallel for schedule(static)
   for (int t = 0; t < T; ++t) {
     std::vector<double> z(d.E), w(d.k);
-    route_token(d, x + (int64_t)t * d.H, Wr, b, &idx[(size_t)t * d.k], w.data(), z.data());
+    route_token(d, x + (int64_t)t * d.H, Wr, b, top_p, &idx[(size_t)t * d.k], w.data(), z.data());
     for (int j = 0; j < d.k; ++j) {
       topk_idx[(int64_t)t * d.k + j] = idx[(size_t)t * d.k + j];
       topk_w[(int64_t)t * d.k + j] = (float)w[j];
@@ -257,13 +308,13 @@ int oracle_route(const int32_t* dims, const uint16_t* x, int32_t T, const float*
 
 // The whole layer for the tokens in token_list (all T tokens when NULL):
 // y[t] = sum_j w_j * FFN_{e_j}(x_t) + FFN_shared(x_t), accumulated in double
-// in slot order, shared expert last, with weight one.
+// in slot order over the kept slots, shared expert last, with weight one.
 //   experts: arrays of E(+1) host pointers per canonical tensor; index E is
 //   the shared expert.  Unselected experts may be NULL.  g3: fp32 [E+1][3]
 //   tensor scales (gate, up, down), or NULL meaning 1.0.
 //   y: fp64 [n_list][H].  Returns 0, or -1 on bad arguments, -2 when a
 //   selected expert pointer is NULL.
-int oracle_forward(const int32_t* dims, const void* const* qg, const void* const* sg, const void* const* qu,
+int oracle_forward(const int32_t* dims, double top_p, const void* const* qg, const void* const* sg, const void* const* qu,
                    const void* const* su, const void* const* qd, const void* const* sd, const float* g3,
                    const float* Wr, const float* b, const uint16_t* x, int32_t T, const int32_t* token_list,
                    int32_t n_list, double* y, int32_t n_threads) {
@@ -289,10 +340,11 @@ int oracle_forward(const int32_t* dims, const void* const* qg, const void* const
     if (t < 0 || t >= T) return -1;
     const uint16_t* xrow = x + (int64_t)t * d.H;
     for (int h = 0; h < d.H; ++h) xd[h] = fp16_value(xrow[h]);
-    route_token(d, xrow, Wr, b, idx.data(), w.data(), z.data());
+    route_token(d, xrow, Wr, b, top_p, idx.data(), w.data(), z.data());
     double* yt = y + (int64_t)ti * d.H;
     for (int c = 0; c < d.H; ++c) yt[c] = 0.0;
     for (int j = 0; j < d.k; ++j) {
+      if (idx[j] < 0) continue;  // slot dropped by adaptive top-p
       if (!present(idx[j])) return -2;
       expert_ffn(d, expert_at(idx[j]), xd.data(), hbuf.data(), o.data());
       for (int c = 0; c < d.H; ++c) yt[c] += w[j] * o[c];

@@ -53,8 +53,10 @@ class Dims:
     top_k: int
     has_shared: int = 1
     wfmt: int = INT4_ROW
+    top_p: float = 0.0  # adaptive top-p threshold; 0 keeps all top_k slots
 
     def as_tuple(self):
+        """The six integer fields (top_p travels separately)."""
         return (self.hidden, self.inter, self.n_experts, self.top_k, self.has_shared, self.wfmt)
 
 

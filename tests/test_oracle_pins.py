@@ -293,3 +293,104 @@ def test_token_permutation_equivariance(orc):
     layer, x = synth.workload("tiny")
     perm = [2, 0, 3, 1]
     np.testing.assert_array_equal(orc.forward(layer, x[perm]), orc.forward(layer, x)[perm])
+
+
+# ---- adaptive top-p (prefix rule) -------------------------------------------
+def _np_keep(z_slots: np.ndarray, k: int, p: float):
+    """Kept-slot count by the rule, in binary32 as the GPU path takes it:
+    sigmoid of the binary32 logit, a pairwise tree sum over 64 lanes, the
+    weights' prefix sums in slot order against p.  Also returns the smallest
+    distance of a prefix sum from p (cases closer than 1e-5 are skipped)."""
+    if not (0.0 < p < 1.0):
+        return k, 1.0
+    s = np.zeros(64, dtype=np.float32)
+    s[:k] = (np.float32(1.0) / (np.float32(1.0) + np.exp(-z_slots.astype(np.float32)))).astype(np.float32)
+    v = s.copy()
+    width = 1
+    while width < 64:
+        v = (v.reshape(-1, 2, width)[:, 0, :] + v.reshape(-1, 2, width)[:, 1, :]).astype(np.float32)
+        v = np.repeat(v[:, None, :], 2, axis=1).reshape(-1)
+        width *= 2
+    tot = v[0]
+    cum = np.float32(0.0)
+    margin = 1.0
+    m = k
+    for j in range(k):
+        cum = np.float32(cum + np.float32(s[j] / tot))
+        margin = min(margin, abs(float(cum) - p))
+        if cum >= np.float32(p) and m == k:
+            m = j + 1
+    return m, margin
+
+
+@pytest.mark.parametrize("E,k,bias,p", [(10, 4, False, 0.5), (10, 4, True, 0.7), (8, 3, False, 0.4),
+                                        (10, 10, False, 0.7), (6, 2, True, 0.55)])
+def test_top_p_keeps_shortest_prefix(orc, E, k, bias, p):
+    dims, x, rw, rb = _tiny_route_layer(E, k, bias=bias)
+    r0 = orc.route(dims, x, rw, rb, top_p=0.0)
+    r = orc.route(dims, x, rw, rb, top_p=p)
+    z_np = x.double().numpy() @ rw.double().numpy().T + (rb.double().numpy() if rb is not None else 0.0)
+    checked = 0
+    for t in range(x.shape[0]):
+        zs = z_np[t, r0.topk_idx[t]]
+        m, margin = _np_keep(zs, k, p)
+        if margin < 1e-5:
+            continue
+        checked += 1
+        # shortest prefix of the plain top-k weights that reaches p
+        cum = np.cumsum(r0.topk_w[t].astype(np.float64))
+        assert cum[m - 1] >= p - 1e-6 and (m == 1 or cum[m - 2] < p + 1e-6)
+        assert list(r.topk_idx[t, :m]) == list(r0.topk_idx[t, :m])
+        assert np.all(r.topk_idx[t, m:] == -1) and np.all(r.topk_w[t, m:] == 0)
+        s = expit(zs[:m])
+        np.testing.assert_allclose(r.topk_w[t, :m], s / s.sum(), rtol=1e-6)
+    assert checked >= 3
+
+
+def test_top_p_equal_logits_exact_counts(orc):
+    """Equal router rows give equal logits, so every weight is exactly 1/k
+    (k = 8: 0.125) and the prefix sums are exact: p picks the count."""
+    E, k = 12, 8
+    dims = synth.Dims(64, 32, E, k, 1, synth.INT4_ROW)
+    rw, _ = synth.make_router(dims, ("eq", E))
+    rw = rw[:1].repeat(E, 1).contiguous()
+    x = synth.make_tokens(dims, 2, ("eq", E))
+    for p, m in [(0.625, 5), (0.626, 6), (0.7, 6), (0.75, 6), (0.7500001, 7), (1e-6, 1), (0.9999, 8)]:
+        r = orc.route(dims, x, rw, None, top_p=p)
+        for t in range(2):
+            assert list(r.topk_idx[t, :m]) == list(range(m)), (p, r.topk_idx[t])
+            assert np.all(r.topk_idx[t, m:] == -1)
+            np.testing.assert_allclose(r.topk_w[t, :m], np.full(m, 1.0 / m), rtol=1e-7)
+
+
+def test_top_p_zero_and_one_keep_all_slots(orc):
+    dims, x, rw, rb = _tiny_route_layer(10, 4, bias=True)
+    r0 = orc.route(dims, x, rw, rb, top_p=0.0)
+    for p in (1.0, 0.0):
+        r = orc.route(dims, x, rw, rb, top_p=p)
+        assert np.array_equal(r.topk_idx, r0.topk_idx) and np.array_equal(r.topk_w, r0.topk_w)
+        assert np.array_equal(r.pairs, r0.pairs)
+
+
+def test_top_p_union_and_layer(orc):
+    """The union holds only the kept pairs, and the layer is the kept
+    experts' dense SwiGLU FFNs (numpy) with the renormalised weights, plus
+    the shared expert."""
+    dims = synth.Dims(128, 64, 8, 4, 1, synth.INT4_ROW, top_p=0.5)
+    layer = synth.make_layer(dims, "topp")
+    x = synth.make_tokens(dims, 5, "topp")
+    r = orc.route(dims, x, layer.router_w, layer.router_b)
+    kept = [(t, j) for t in range(5) for j in range(4) if r.topk_idx[t, j] >= 0]
+    assert len(kept) < 20, "p = 0.5 should drop slots here"
+    assert int(r.uniq_off[-1]) == len(kept)
+    assert sorted(int(p) for p in r.pairs[: len(kept)]) == sorted(t * 4 + j for t, j in kept)
+    assert list(r.uniq_ids) == sorted(set(int(r.topk_idx[t, j]) for t, j in kept))
+    y = orc.forward(layer, x)
+    x64 = x.double().numpy()
+    ref = _dense_swiglu(layer, 8, x64)
+    for t, j in kept:
+        e = int(r.topk_idx[t, j])
+        z = r.z[t, r.topk_idx[t][r.topk_idx[t] >= 0]]
+        w = expit(z) / expit(z).sum()
+        ref[t] += w[j] * _dense_swiglu(layer, e, x64[t:t + 1])[0]
+    np.testing.assert_allclose(y, ref, rtol=1e-9, atol=1e-13)
