@@ -81,6 +81,8 @@ typedef struct {
   int32_t top_k;      /* k: routed experts kept per token                */
   int32_t has_shared; /* 1 if a shared expert is added to every token    */
   int32_t wfmt;       /* moe_wfmt_t                                      */
+  float top_p;        /* adaptive expert top-p: 0 keeps all top_k slots;
+                       * otherwise in (0, 1], see moe_route              */
 } moe_dims_t;
 
 /* Weights of one layer (host struct holding device pointers). */
@@ -128,14 +130,21 @@ int moe_unpack(const moe_dims_t* d, const void* packed, void* q_gate, void* s_ga
  * Logits are accumulated in fp64: z[t][e] = b[e] + sum_h x[t][h]*Wr[e][h].
  * Experts are ranked by (z descending, index ascending); the first k are
  * kept in that order.  w[t][j] = sigmoid(z_j) / sum_j' sigmoid(z_j').
+ * Adaptive top-p ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法",
+ * hakusoku.com, section 実装済み機能, the top-p expert option), when
+ * 0 < d->top_p < 1: only the shortest prefix of the k slots whose
+ * cumulative weight reaches top_p is kept (the decision is taken in
+ * binary32: sigmoid of the binary32 logit, a pairwise sum over the slots,
+ * prefix sums in slot order), and the kept weights are renormalised over
+ * the kept slots; dropped slots get topk_idx = -1 and topk_w = 0.
  * Outputs:
  *   topk_idx int32 [T][k], topk_w fp32 [T][k];
  *   n_unique int32 [1]: distinct experts chosen by the batch;
  *   uniq_ids int32 [min(E, T*k)]: those experts, ascending;
  *   uniq_off int32 [min(E, T*k) + 1]: uniq_off[u]..uniq_off[u+1] is expert
- *     u's range in pairs;
- *   pairs int32 [T*k]: pair ids t*k + j, grouped by expert and in ascending
- *     token order within each group.
+ *     u's range in pairs; uniq_off[n_unique] is the number of kept pairs;
+ *   pairs int32 [T*k]: pair ids t*k + j of the kept slots, grouped by
+ *     expert and in ascending token order within each group.
  * Entries past n_unique are unspecified.  T == 0 launches nothing and
  * returns MOE_OK (outputs untouched). */
 int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,

@@ -27,7 +27,8 @@ EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes"
 
 class MoeDims(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
-                ("top_k", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("wfmt", ctypes.c_int32)]
+                ("top_k", ctypes.c_int32), ("has_shared", ctypes.c_int32), ("wfmt", ctypes.c_int32),
+                ("top_p", ctypes.c_float)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -81,7 +82,7 @@ def _dims(d) -> MoeDims:
     if isinstance(d, MoeDims):
         return d
     t = d.as_tuple() if hasattr(d, "as_tuple") else tuple(d)
-    return MoeDims(*[int(v) for v in t])
+    return MoeDims(*[int(v) for v in t[:6]], float(getattr(d, "top_p", t[6] if len(t) > 6 else 0.0)))
 
 
 def _p(t: Optional[torch.Tensor]):

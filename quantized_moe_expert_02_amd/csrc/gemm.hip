@@ -36,6 +36,7 @@ struct GemmArgs {
   const int32_t* tiles;      // [tile] = (slot, m0) pairs
   const int32_t* n_tiles;    // [1]
   const float* topk_w;
+  const int32_t* topk_idx;
   const uint16_t* x;         // [T][H]
   uint16_t* h;               // [rows_total][I]
   float* part;               // [rows_total][H]
@@ -320,7 +321,8 @@ __global__ __launch_bounds__(256) void k_combine(GemmArgs a) {
   const int c = blockIdx.x * 256 + threadIdx.x;
   if (c >= a.H) return;
   float acc = 0.f;
-  for (int j = 0; j < a.k; ++j) acc += a.part[((size_t)t * a.k + j) * a.H + c];
+  for (int j = 0; j < a.k; ++j)
+    if (a.topk_idx[t * a.k + j] >= 0) acc += a.part[((size_t)t * a.k + j) * a.H + c];  // < 0: dropped by top-p
   if (a.S) acc += a.part[((size_t)a.T * a.k + t) * a.H + c];
   a.y[(size_t)t * a.H + c] = __builtin_bit_cast(uint16_t, (_Float16)acc);
 }
@@ -337,6 +339,7 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   a.tiles = r.tiles;
   a.n_tiles = r.n_tiles;
   a.topk_w = r.topk_w;
+  a.topk_idx = r.topk_idx;
   a.x = x;
   a.h = (uint16_t*)((char*)ws + p.h_off);
   a.part = (float*)((char*)ws + p.p_dn_off);

@@ -219,6 +219,8 @@ struct DecArgs {
   const void* const* experts;
   const void* shared;
   int T, H, I, E, k, S;
+  float top_p;
+  int top_p_on;       // 0 < top_p < 1: slots may be dropped
   Layout L;
   uint16_t* y;
   int32_t* topk_idx;
@@ -321,7 +323,8 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const
   const int e0 = lane * per, e1 = min(a.E, e0 + per);
   for (int e = e0; e < e1; ++e) ls.mask[e] = 0;
   wave_lds_sync();
-  for (int p = lane; p < P; p += 64) atomicOr(&ls.mask[ls.pe[p]], 1u << (p / a.k));
+  for (int p = lane; p < P; p += 64)
+    if (ls.pe[p] >= 0) atomicOr(&ls.mask[ls.pe[p]], 1u << (p / a.k));  // < 0: dropped by top-p
   wave_lds_sync();
   int cnt = 0, pres = 0;
   for (int e = e0; e < e1; ++e) {
@@ -366,6 +369,7 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const
   wave_lds_sync();
   for (int p = lane; p < P; p += 64) {
     const int e = ls.pe[p];
+    if (e < 0) continue;
     const int t = p / a.k;
     a.pairs[ls.base[e] + __popc(ls.mask[e] & ((1u << t) - 1u))] = p;
   }
@@ -465,8 +469,8 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
   const int tpw = (a.T + kWpg - 1) / kWpg;
   const int t0 = wave * tpw, t1 = min(a.T, t0 + tpw);
   for (int t = t0; t < t1; ++t)
-    topk_tokens(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k, 1, a.topk_idx + t * a.k,
-                a.topk_w + t * a.k, ls.pe + t * a.k);
+    topk_tokens(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k, a.top_p, 1,
+                a.topk_idx + t * a.k, a.topk_w + t * a.k, ls.pe + t * a.k);
   __syncthreads();
   if (wave == 0) union_step(a, ls, ep);
 }
@@ -681,19 +685,21 @@ __device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rb, DnLds<K
   for (int t = 0; t < a.T; ++t) {
     float acc = 0.f;
     for (int j0 = 0; j0 < a.k + a.S; j0 += 8) {
-      float o[8];
+      // all loads first (independent); a slot dropped by top-p has no
+      // partial row, so its (unwritten) row is loaded but not used
+      float o[8], wj[8];
+      int ej[8];
 #pragma unroll
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int row = (j < a.k) ? t * a.k + j : a.T * a.k + t;
-        if (j < a.k + a.S) o[jj] = a.p_dn[(size_t)row * a.H + r];
+        o[jj] = (j < a.k + a.S) ? a.p_dn[(size_t)row * a.H + r] : 0.f;
+        ej[jj] = (j < a.k && a.top_p_on) ? a.topk_idx[t * a.k + j] : 0;
+        wj[jj] = (j < a.k) ? a.topk_w[t * a.k + j] : 1.f;
       }
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = j0 + jj;
-        if (j >= a.k + a.S) break;
-        acc += (j < a.k) ? a.topk_w[t * a.k + j] * o[jj] : o[jj];
-      }
+      for (int jj = 0; jj < 8; ++jj)
+        if (j0 + jj < a.k + a.S && ej[jj] >= 0) acc += (j0 + jj < a.k) ? wj[jj] * o[jj] : o[jj];
     }
     a.y[(size_t)t * a.H + r] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
@@ -756,6 +762,8 @@ hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t
   a.E = p.E;
   a.k = p.k;
   a.S = p.S;
+  a.top_p = d.top_p;
+  a.top_p_on = d.top_p > 0.0f && d.top_p < 1.0f;
   a.L = layout_of(d);
   a.y = y;
   a.topk_idx = r.topk_idx;

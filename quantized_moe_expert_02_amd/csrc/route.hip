@@ -24,6 +24,7 @@ struct RouteArgs {
   const float* b;
   const uint16_t* x;
   int T, H, E, k, S;
+  float top_p;
   double* z;
   int32_t* topk_idx;
   float* topk_w;
@@ -139,7 +140,7 @@ __global__ __launch_bounds__(256) void k_logits_sum(RouteArgs a) {
 __global__ __launch_bounds__(256) void k_topk(RouteArgs a) {
   const int t = blockIdx.x * 4 + threadIdx.x / kWave;
   if (t >= a.T) return;
-  topk_any<false>(a.z + (size_t)t * a.E, 1, 0, nullptr, a.E, a.k, a.topk_idx + (size_t)t * a.k, a.topk_w + (size_t)t * a.k,
+  topk_any<false>(a.z + (size_t)t * a.E, 1, 0, nullptr, a.E, a.k, a.top_p, a.topk_idx + (size_t)t * a.k, a.topk_w + (size_t)t * a.k,
                   nullptr);
 }
 
@@ -154,7 +155,8 @@ __global__ __launch_bounds__(256) void k_union_count(RouteArgs a) {
   __syncthreads();
   for (int i = threadIdx.x; i < nt * a.k; i += blockDim.x) {
     const int t = t0 + i / a.k;
-    atomicOr(&s_mask[a.topk_idx[(size_t)t * a.k + i % a.k]], 1u << (i / a.k));
+    const int e = a.topk_idx[(size_t)t * a.k + i % a.k];
+    if (e >= 0) atomicOr(&s_mask[e], 1u << (i / a.k));  // e < 0: slot dropped by top-p
   }
   __syncthreads();
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.ucnt[(size_t)c * a.E + e] = __popc(s_mask[e]);
@@ -259,13 +261,15 @@ __global__ __launch_bounds__(256) void k_union_scatter(RouteArgs a) {
   __syncthreads();
   for (int i = threadIdx.x; i < nt * a.k; i += blockDim.x) {
     const int t = t0 + i / a.k;
-    atomicOr(&s_mask[a.topk_idx[(size_t)t * a.k + i % a.k]], 1u << (i / a.k));
+    const int e = a.topk_idx[(size_t)t * a.k + i % a.k];
+    if (e >= 0) atomicOr(&s_mask[e], 1u << (i / a.k));
   }
   __syncthreads();
   for (int i = threadIdx.x; i < nt * a.k; i += blockDim.x) {
     const int tl = i / a.k;
     const int t = t0 + tl;
     const int e = a.topk_idx[(size_t)t * a.k + i % a.k];
+    if (e < 0) continue;
     const int rank = __popc(s_mask[e] & ((1u << tl) - 1u));
     a.pairs[a.ubase[(size_t)c * a.E + e] + rank] = t * a.k + i % a.k;
   }
@@ -284,6 +288,7 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
   a.H = p.H;
   a.E = p.E;
   a.k = p.k;
+  a.top_p = d.top_p;
   a.z = r.z;
   a.topk_idx = r.topk_idx;
   a.topk_w = r.topk_w;

@@ -58,6 +58,30 @@ __device__ __forceinline__ double from_order_key(uint64_t k) {
   return __builtin_bit_cast(double, u);
 }
 
+// Adaptive top-p over the k ranked slots held by lanes 0..k-1 (s: binary32
+// sigmoid of the slot's logit, 0 on lanes >= k; tot: its wave-wide sum).
+// Returns the number of kept slots: the shortest prefix whose cumulative
+// weight s_j / tot, summed in slot order in binary32, reaches p (k when p
+// is 0 or >= 1).
+__device__ __forceinline__ int top_p_keep(float s, float tot, int k, float p) {
+  if (!(p > 0.0f && p < 1.0f)) return k;
+  const float w = s / tot;
+  float cum = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    cum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
+    if (cum >= p) return j + 1;
+  }
+  return k;
+}
+
+// Every lane ends with the wave-wide fp32 sum, butterfly order (the same on
+// every lane).
+__device__ __forceinline__ float wave_sum_f32(float v) {
+#pragma unroll
+  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  return v;
+}
+
 // Every lane ends with the wave-wide best (key, index): the largest key, ties
 // to the lower index.  The high key word is reduced first; only when more than
 // one lane holds that high word are the low word and the index reduced too.
@@ -87,7 +111,7 @@ __device__ __forceinline__ void wave_argmax_key(uint64_t& key, int& idx) {
 // The logit of expert e is zrow[e], or with kCoherent the sum of nz partial
 // logits zrow[s * zstride + e] (s ascending) plus bias[e] when bias is set.
 template <int kPer, bool kCoherent>
-__device__ void topk_wave(const double* zrow, int nz, size_t zstride, const float* bias, int E, int k,
+__device__ void topk_wave(const double* zrow, int nz, size_t zstride, const float* bias, int E, int k, float top_p,
                           int32_t* idx_out, float* w_out, int* slot_expert) {
   // kCoherent: zrow holds partial logits written during this kernel by
   // other workgroups (published before this wavefront waited, and not read
@@ -155,29 +179,31 @@ __device__ void topk_wave(const double* zrow, int nz, size_t zstride, const floa
   }
   const double my_z = from_order_key(my_key);
   const float s = (lane < k) ? 1.0f / (1.0f + expf(-(float)my_z)) : 0.0f;
-  float tot = s;
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) tot += __shfl_xor(tot, m, kWave);
+  float tot = wave_sum_f32(s);
+  const int m = top_p_keep(s, tot, k, top_p);
+  if (m < k) tot = wave_sum_f32(lane < m ? s : 0.0f);
   if (lane < k) {
+    const int32_t e_out = lane < m ? my_e : -1;
+    const float w = lane < m ? s / tot : 0.0f;
     if (kCoherent) {
-      st_dev(idx_out + lane, (int32_t)my_e);
-      st_dev(w_out + lane, s / tot);
+      st_dev(idx_out + lane, e_out);
+      st_dev(w_out + lane, w);
     } else {
-      idx_out[lane] = my_e;
-      w_out[lane] = s / tot;
+      idx_out[lane] = e_out;
+      w_out[lane] = w;
     }
-    if (slot_expert) slot_expert[lane] = my_e;
+    if (slot_expert) slot_expert[lane] = e_out;
   }
 }
 
 template <bool kCoherent>
-__device__ void topk_any(const double* zrow, int nz, size_t zstride, const float* bias, int E, int k,
+__device__ void topk_any(const double* zrow, int nz, size_t zstride, const float* bias, int E, int k, float top_p,
                          int32_t* idx_out, float* w_out, int* slot_expert) {
-  if (E <= 64) topk_wave<1, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
-  else if (E <= 128) topk_wave<2, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
-  else if (E <= 256) topk_wave<4, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
-  else if (E <= 512) topk_wave<8, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
-  else topk_wave<16, kCoherent>(zrow, nz, zstride, bias, E, k, idx_out, w_out, slot_expert);
+  if (E <= 64) topk_wave<1, kCoherent>(zrow, nz, zstride, bias, E, k, top_p, idx_out, w_out, slot_expert);
+  else if (E <= 128) topk_wave<2, kCoherent>(zrow, nz, zstride, bias, E, k, top_p, idx_out, w_out, slot_expert);
+  else if (E <= 256) topk_wave<4, kCoherent>(zrow, nz, zstride, bias, E, k, top_p, idx_out, w_out, slot_expert);
+  else if (E <= 512) topk_wave<8, kCoherent>(zrow, nz, zstride, bias, E, k, top_p, idx_out, w_out, slot_expert);
+  else topk_wave<16, kCoherent>(zrow, nz, zstride, bias, E, k, top_p, idx_out, w_out, slot_expert);
 }
 
 
@@ -194,7 +220,7 @@ __device__ void topk_any(const double* zrow, int nz, size_t zstride, const float
 // and slot_expert[t * k + j] (LDS) if set.
 template <int kPer, int NT>
 __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
-                           int32_t* idx_out, float* w_out, int* slot_expert) {
+                                           float top_p, int32_t* idx_out, float* w_out, int* slot_expert) {
   const int lane = threadIdx.x & (kWave - 1);
   double v[NT][kPer];
 #pragma unroll
@@ -289,13 +315,14 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
   for (int t = 0; t < NT; ++t) {
     const double my_z = from_order_key(my_key[t]);
     const float s = (lane < k) ? 1.0f / (1.0f + expf(-(float)my_z)) : 0.0f;
-    float tot = s;
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1) tot += __shfl_xor(tot, m, kWave);
+    float tot = wave_sum_f32(s);
+    const int m = top_p_keep(s, tot, k, top_p);
+    if (m < k) tot = wave_sum_f32(lane < m ? s : 0.0f);
     if (lane < k) {
-      st_dev(idx_out + t * k + lane, (int32_t)my_e[t]);
-      st_dev(w_out + t * k + lane, s / tot);
-      if (slot_expert) slot_expert[t * k + lane] = my_e[t];
+      const int32_t e_out = lane < m ? my_e[t] : -1;
+      st_dev(idx_out + t * k + lane, e_out);
+      st_dev(w_out + t * k + lane, lane < m ? s / tot : 0.0f);
+      if (slot_expert) slot_expert[t * k + lane] = e_out;
     }
   }
 }
@@ -304,25 +331,26 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
 // one token at a time (ranking several together gains little: the rounds
 // are bound by instruction issue, not latency).
 template <int kPer>
-__device__ __forceinline__ void topk_tokens_per(const double* z, int nz, size_t zstride, const float* bias, int E, int k, int T,
-                                int32_t* idx_out, float* w_out, int* slot_expert) {
+__device__ __forceinline__ void topk_tokens_per(const double* z, int nz, size_t zstride, const float* bias, int E,
+                                                int k, float top_p, int T, int32_t* idx_out, float* w_out,
+                                                int* slot_expert) {
   constexpr int NT = 1;
   int t0 = 0;
   for (; t0 + NT <= T; t0 += NT)
-    topk_multi<kPer, NT>(z + (size_t)t0 * E, nz, zstride, bias, E, k, idx_out + t0 * k, w_out + t0 * k,
+    topk_multi<kPer, NT>(z + (size_t)t0 * E, nz, zstride, bias, E, k, top_p, idx_out + t0 * k, w_out + t0 * k,
                          slot_expert + t0 * k);
   for (; t0 < T; ++t0)
-    topk_multi<kPer, 1>(z + (size_t)t0 * E, nz, zstride, bias, E, k, idx_out + t0 * k, w_out + t0 * k,
+    topk_multi<kPer, 1>(z + (size_t)t0 * E, nz, zstride, bias, E, k, top_p, idx_out + t0 * k, w_out + t0 * k,
                         slot_expert + t0 * k);
 }
 
 __device__ __forceinline__ void topk_tokens(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
-                                            int T, int32_t* idx_out, float* w_out, int* slot_expert) {
-  if (E <= 64) topk_tokens_per<1>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
-  else if (E <= 128) topk_tokens_per<2>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
-  else if (E <= 256) topk_tokens_per<4>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
-  else if (E <= 512) topk_tokens_per<8>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
-  else topk_tokens_per<16>(z, nz, zstride, bias, E, k, T, idx_out, w_out, slot_expert);
+                                            float top_p, int T, int32_t* idx_out, float* w_out, int* slot_expert) {
+  if (E <= 64) topk_tokens_per<1>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
+  else if (E <= 128) topk_tokens_per<2>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
+  else if (E <= 256) topk_tokens_per<4>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
+  else if (E <= 512) topk_tokens_per<8>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
+  else topk_tokens_per<16>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
 }
 
 // Every lane ends with the wave-wide fp64 sum, added in a fixed butterfly order.

@@ -22,6 +22,7 @@ def oracle_y(layer, x, tokens=None):
         need = r.uniq_ids
     else:
         need = np.unique(r.topk_idx[np.asarray(tokens)])
+        need = need[need >= 0]  # -1: slots dropped by adaptive top-p
     return oracle.forward(layer, x.cpu(), tokens=tokens, experts_needed=need)
 
 
@@ -42,3 +43,18 @@ def min_topk_gap(r, k):
     if z.shape[1] <= k:
         return np.inf
     return float(np.min(z[:, k - 1] - z[:, k]))
+
+
+def top_p_margin(r, k, p):
+    """Smallest distance, over tokens and slots, between p and a prefix sum
+    of the binary32 slot weights that adaptive top-p compares with it (the
+    GPU and the oracle may round the sigmoid differently by an ulp, so cases
+    must keep clear of the threshold).  r: a plain top-k oracle route (z set)."""
+    margin = np.inf
+    for t in range(r.topk_idx.shape[0]):
+        zs = r.z[t, r.topk_idx[t]].astype(np.float32)
+        s = (np.float32(1.0) / (np.float32(1.0) + np.exp(-zs))).astype(np.float32)
+        tot = np.float32(s.astype(np.float64).sum())
+        cum = np.cumsum((s / tot).astype(np.float64))
+        margin = min(margin, float(np.min(np.abs(cum - p))))
+    return margin

@@ -60,9 +60,10 @@ def test_sizes(L, d):
     (dict(hidden=100), moe.MOE_E_UNSUPPORTED), (dict(inter=96), moe.MOE_E_UNSUPPORTED),
     (dict(top_k=0), moe.MOE_E_INVAL), (dict(top_k=9, n_experts=8), moe.MOE_E_INVAL),
     (dict(n_experts=2048), moe.MOE_E_UNSUPPORTED), (dict(top_k=40, n_experts=64), moe.MOE_E_UNSUPPORTED),
-    (dict(wfmt=5), moe.MOE_E_UNSUPPORTED), (dict(has_shared=2), moe.MOE_E_INVAL)])
+    (dict(wfmt=5), moe.MOE_E_UNSUPPORTED), (dict(has_shared=2), moe.MOE_E_INVAL),
+    (dict(top_p=-0.1), moe.MOE_E_INVAL), (dict(top_p=1.5), moe.MOE_E_INVAL), (dict(top_p=float("nan")), moe.MOE_E_INVAL)])
 def test_bad_dims_rejected(L, bad, code):
-    base = dict(hidden=256, inter=128, n_experts=8, top_k=2, has_shared=1, wfmt=0)
+    base = dict(hidden=256, inter=128, n_experts=8, top_k=2, has_shared=1, wfmt=0, top_p=0.0)
     base.update(bad)
     d = moe.MoeDims(**base)
     assert moe.moe_packed_bytes(d) == 0
@@ -113,3 +114,11 @@ def test_route_and_pack_argument_errors(L):
     assert rc == moe.MOE_E_INVAL  # packed_out not 256-aligned
     rc = L.moe_pack(ctypes.byref(d), P(16), None, P(16), P(16), P(16), P(16), None, P(256), None)
     assert rc == moe.MOE_E_INVAL
+
+
+def test_top_p_accepted_range(L):
+    """top_p in [0, 1] is valid (0 and 1 keep all slots); sizes do not depend on it."""
+    for p in (0.0, 0.5, 1.0):
+        d = moe.MoeDims(256, 128, 8, 2, 1, 0, p)
+        assert moe.moe_packed_bytes(d) == moe.moe_packed_bytes(moe.MoeDims(256, 128, 8, 2, 1, 0))
+        assert moe.moe_workspace_bytes(d, 4) == moe.moe_workspace_bytes(moe.MoeDims(256, 128, 8, 2, 1, 0), 4)
