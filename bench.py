@@ -366,8 +366,8 @@ def main():
     del ch
     torch.cuda.empty_cache()
     if not args.no_secondary:
-        for name, L, steps in (("decode_b8", 8, 128), ("e2m1_b1", 32, 512), ("e2m1_b4", 32, 256),
-                               ("prefill_2048", 2, 8)):
+        for name, L, steps in (("decode_b8", 8, 128), ("decode_b1_topp", 8, 512), ("e2m1_b1", 32, 512),
+                               ("e2m1_b4", 32, 256), ("prefill_2048", 2, 8)):
             try:
                 c2, r2, _ = run_workload(name, L, steps, 32, stage_reps=2)
                 secondary.append(r2)

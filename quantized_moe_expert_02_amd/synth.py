@@ -67,6 +67,8 @@ WORKLOADS = {
     "tiny": dict(dims=Dims(256, 128, 8, 2, 1, INT4_ROW), tokens=4),
     "decode_b1": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=1),
     "decode_b8": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=8),
+    # adaptive expert top-p 0.7 (hakusoku.com story 8412, section 実装済み機能)
+    "decode_b1_topp": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW, top_p=0.7), tokens=1),
     "e2m1_b1": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=1),
     "e2m1_b4": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=4),
     "prefill_2048": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=2048, zipf=1.1),
