@@ -61,7 +61,7 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   // decode K-splits: one wavefront per K-segment, four per workgroup
   q.ks_gu = split_factor(q.H, 4);  // routed experts
   q.ks_sgu = shared_split(q.H);    // shared expert, streamed while routing
-  q.ks_dn = split_factor(q.I, 4);
+  q.ks_dn = split_factor(q.I, 2);  // 2 K-segments x 2 row blocks per workgroup
   // Counters: the first 256 words for route-stage counters, then one per
   // (slot, gate/up row block) for the largest decode batch, then one per
   // down row block.

@@ -613,11 +613,12 @@ struct DnLds {
 };
 
 template <int FMT, int NT, int KT>
-__device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, int rb, int nw, int i0, float scale,
+__device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, int rb, int seg, int i0, float scale,
                                         DnLds<KT>& ls) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (wave < nw) {
-    const int c0 = wave * a.cpu_dn;
+  const bool active = rb < a.H / 64;  // the last workgroup of a slot may overhang
+  if (active) {
+    const int c0 = seg * a.cpu_dn;
     const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / 32) + c0) * 64 + lane;
     const guint2* sc = nullptr;
     if (FMT == MOE_W_E2M1_B16)
@@ -648,11 +649,11 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
     for (int t = 0; t < NT; ++t) ls.r[wave][t][lane] = acc[0][t];
   }
   __syncthreads();
-  if (wave == 0) {
+  if (active && seg == 0) {  // first wavefront of this row block adds its segments in order
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       float v = 0.f;
-      for (int q = 0; q < nw; ++q) v += ls.r[q][t][lane];
+      for (int q = 0; q < a.ks_dn; ++q) v += ls.r[wave + q][t][lane];
       int tok, row;
       slot_token(a, si, i0 + t, tok, row);
       st_dev(a.p_dn + (size_t)row * a.H + 64 * rb + lane, v * scale);
@@ -661,23 +662,25 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
   __syncthreads();  // LDS is reused by the next tile
 }
 
+// Workgroup = (slot s, kWpg / ks_dn consecutive output row blocks); wavefront
+// w takes row block rbg * (kWpg / ks_dn) + w / ks_dn, K-segment w % ks_dn.
 template <int FMT, int KT>
-__device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rb, DnLds<KT>& ls) {
+__device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rbg, DnLds<KT>& ls) {
   SlotInfo si;
   if (!get_slot(a, s, si)) return;  // uniform over the workgroup
-  const int lane = threadIdx.x & 63;
-  const int r = 64 * rb + lane;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int rb = rbg * (kWpg / a.ks_dn) + wave / a.ks_dn, seg = wave % a.ks_dn;
+  const int r = 64 * min(rb, a.H / 64 - 1) + lane;
   float scale;
   if (FMT == MOE_W_INT4_ROW)
     scale = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sd_off)[r]);
   else
     scale = reinterpret_cast<const float*>(si.base + a.L.g3_off)[2];
-  const int nw = a.ks_dn;
   for (int i0 = 0; i0 < si.n; i0 += KT) {
-    if (KT == 1 || si.n - i0 == 1) dn_tile<FMT, 1, KT>(a, si, rb, nw, i0, scale, ls);
-    else dn_tile<FMT, KT, KT>(a, si, rb, nw, i0, scale, ls);
+    if (KT == 1 || si.n - i0 == 1) dn_tile<FMT, 1, KT>(a, si, rb, seg, i0, scale, ls);
+    else dn_tile<FMT, KT, KT>(a, si, rb, seg, i0, scale, ls);
   }
-  if (threadIdx.x >= 64) return;
+  if (seg != 0 || rb >= a.H / 64) return;
   const uint32_t nu = __builtin_amdgcn_readfirstlane(*a.n_unique);
   if (!arrive_last(a.dn_cnt + rb, (uint32_t)a.S + nu)) return;
   // last slot of this row block: y[t] = sum over the token's slots in slot
@@ -731,7 +734,7 @@ __global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_
 template <int FMT, int KT>
 __global__ __launch_bounds__(64 * kWpg) void k_dn_phase(DecArgs a) {
   __shared__ DnLds<KT> dl;
-  const int per_slot = a.H / 64;
+  const int rpw = kWpg / a.ks_dn, per_slot = (a.H / 64 + rpw - 1) / rpw;
   dn_unit<FMT, KT>(a, blockIdx.x / per_slot, blockIdx.x % per_slot, dl);
 }
 
@@ -742,7 +745,8 @@ hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, con
   const dim3 blk(64 * kWpg);
   launch_k(k_route_phase<FMT, KT>, dim3(a.n_router_wg + sgu_wg), blk, s, se.start(0), se.stop(0), a, x);
   launch_k(k_gu_phase<FMT, KT>, dim3((a.slots_max - a.S) * (a.I / 64)), blk, s, se.start(1), se.stop(1), a, x);
-  launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * (a.H / 64)), blk, s, se.start(2), se.stop(2), a);
+  const int rpw = kWpg / a.ks_dn;
+  launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * ((a.H / 64 + rpw - 1) / rpw)), blk, s, se.start(2), se.stop(2), a);
   return hipGetLastError();
 }
 
