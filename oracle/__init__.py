@@ -1,4 +1,4 @@
-"""CPU oracle for the 4-bit MoE FFN layer (test infrastructure only).
+"""CPU oracle for the quantised MoE FFN layer (test infrastructure only).
 
 Only the tests, the smoke check and the CPU-baseline leg of the benchmark
 load this package.  The GPU library never imports, links or calls it.
@@ -42,6 +42,8 @@ def lib():
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         L.oracle_fp16_values.argtypes = [P, i64, P]
         L.oracle_int4_values.argtypes = [P, i64, P]
+        L.oracle_int8_values.argtypes = [P, i64, P]
+        L.oracle_int2_values.argtypes = [P, i64, P]
         L.oracle_e2m1_values.argtypes = [P, i64, P]
         L.oracle_e4m3_values.argtypes = [P, i64, P]
         L.oracle_dequant.argtypes = [i32, P, P, ctypes.c_float, i32, i32, P]
@@ -90,6 +92,20 @@ def int4_values(q: np.ndarray) -> np.ndarray:
     q = np.ascontiguousarray(q, dtype=np.uint8)
     out = np.empty(2 * q.size, dtype=np.int32)
     lib().oracle_int4_values(_ptr(q), q.size, _ptr(out))
+    return out
+
+
+def int8_values(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(q.size, dtype=np.int32)
+    lib().oracle_int8_values(_ptr(q), q.size, _ptr(out))
+    return out
+
+
+def int2_values(q: np.ndarray) -> np.ndarray:
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    out = np.empty(4 * q.size, dtype=np.int32)
+    lib().oracle_int2_values(_ptr(q), q.size, _ptr(out))
     return out
 
 

@@ -1,4 +1,4 @@
-// CPU oracle for the 4-bit MoE FFN layer.  TEST INFRASTRUCTURE ONLY: it is
+// CPU oracle for the quantised MoE FFN layer.  TEST INFRASTRUCTURE ONLY: it is
 // used by the tests, by the smoke check and by the CPU-baseline timing, and
 // it shares no code with the GPU library.
 //
@@ -17,6 +17,8 @@
 //    section 実装済み機能); or NVFP4-style e2m1 codes decoded inside the matmul
 //    ("GTX 1070向け35BパラメータMoEモデル推論エンジン公開", 648news.com, section
 //    "VRAMとシステムメモリで重みを分割する設計" and the NVFP4 glossary entry);
+//    or the int8 and int2 per-row-scale formats of the same Colibrì kernels
+//    (hakusoku.com, section 実装済み機能);
 //  * a DeepSeek-V3-style sigmoid router and a shared expert (hakusoku.com,
 //    section 実装済み機能), 8 of 256 experts per token (same page, sections
 //    Colibrì and 性能・要件);
@@ -44,7 +46,10 @@
 
 namespace {
 
-enum { FMT_INT4_ROW = 0, FMT_E2M1_B16 = 1 };
+enum { FMT_INT4_ROW = 0, FMT_E2M1_B16 = 1, FMT_INT8_ROW = 2, FMT_INT2_ROW = 3 };
+
+// Bits per stored code of each format.
+int code_bits(int fmt) { return fmt == FMT_INT8_ROW ? 8 : fmt == FMT_INT2_ROW ? 2 : 4; }
 
 struct Dims {
   int H, I, E, k, has_shared, fmt;
@@ -75,6 +80,16 @@ inline int nibble(const uint8_t* row, int64_t col) {
 // Two's-complement int4: codes 8..15 stand for -8..-1.
 inline int int4_value(int code) { return code >= 8 ? code - 16 : code; }
 
+// Two's-complement int8: bytes 128..255 stand for -128..-1.
+inline int int8_value(uint8_t b) { return b >= 128 ? (int)b - 256 : (int)b; }
+
+// Element `col` of a 2-bit-packed row: element 4j+i sits in bits 2i..2i+1
+// of byte j; two's complement, so codes 2 and 3 stand for -2 and -1.
+inline int int2_value(const uint8_t* row, int64_t col) {
+  const int code = (row[col >> 2] >> (2 * (col & 3))) & 3;
+  return code >= 2 ? code - 4 : code;
+}
+
 // OCP FP4 E2M1: bit 3 sign, bits 2..1 exponent (bias 1), bit 0 mantissa.
 // Exponent 0 is subnormal (0 or 0.5); otherwise (1 + m/2) * 2^(e-1).
 double e2m1_value(int code) {
@@ -98,9 +113,14 @@ double e4m3_value(uint8_t b) {
   return sign ? -mag : mag;
 }
 
-// One quantised matrix in canonical storage: q[rows][cols/2] nibbles plus
-// either a binary16 scale per row (INT4_ROW) or an e4m3 scale per 16 columns
-// and an fp32 tensor scale g (E2M1_B16).
+// One quantised matrix in canonical storage: q[rows][cols*bits/8] codes plus
+// either a binary16 scale per row (INT4_ROW, INT8_ROW, INT2_ROW) or an e4m3
+// scale per 16 columns and an fp32 tensor scale g (E2M1_B16).  The integer
+// formats are those of the Colibrì engine's int8/int4/int2 kernels with a
+// scale per row ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法",
+// hakusoku.com, section 実装済み機能); the bit layout of int8 and int2 is a
+// reading (the page gives none): one byte per int8 code, four int2 codes per
+// byte from the least significant bits up, both two's complement.
 struct QMat {
   const uint8_t* q;
   const void* s;
@@ -109,12 +129,12 @@ struct QMat {
 
   // The real-valued weight W[r][c] that the code and its scales stand for.
   double w(int r, int64_t c) const {
-    const uint8_t* row = q + (int64_t)r * (cols / 2);
+    const uint8_t* row = q + (int64_t)r * cols * code_bits(fmt) / 8;
+    const uint16_t* s16 = (const uint16_t*)s;
+    if (fmt == FMT_INT8_ROW) return (double)int8_value(row[c]) * fp16_value(s16[r]);
+    if (fmt == FMT_INT2_ROW) return (double)int2_value(row, c) * fp16_value(s16[r]);
     const int code = nibble(row, c);
-    if (fmt == FMT_INT4_ROW) {
-      const uint16_t* s16 = (const uint16_t*)s;
-      return (double)int4_value(code) * fp16_value(s16[r]);
-    }
+    if (fmt == FMT_INT4_ROW) return (double)int4_value(code) * fp16_value(s16[r]);
     const uint8_t* s8 = (const uint8_t*)s + (int64_t)r * (cols / 16);
     return e2m1_value(code) * e4m3_value(s8[c / 16]) * g;
   }
@@ -229,7 +249,7 @@ void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const flo
 
 bool dims_ok(const Dims& d) {
   return d.H > 0 && d.I > 0 && d.E > 0 && d.k >= 1 && d.k <= d.E && d.H % 32 == 0 && d.I % 32 == 0 &&
-         (d.fmt == FMT_INT4_ROW || d.fmt == FMT_E2M1_B16);
+         d.fmt >= FMT_INT4_ROW && d.fmt <= FMT_INT2_ROW;
 }
 
 Dims to_dims(const int32_t* p) { return Dims{p[0], p[1], p[2], p[3], p[4], p[5]}; }
@@ -246,6 +266,13 @@ void oracle_fp16_values(const uint16_t* in, int64_t n, double* out) {
 void oracle_int4_values(const uint8_t* q, int64_t nbytes, int32_t* out) {
   for (int64_t i = 0; i < 2 * nbytes; ++i) out[i] = int4_value(nibble(q, i));
 }
+void oracle_int8_values(const uint8_t* q, int64_t nbytes, int32_t* out) {
+  for (int64_t i = 0; i < nbytes; ++i) out[i] = int8_value(q[i]);
+}
+// Four codes per byte, element 4j+i from bits 2i..2i+1 of byte j.
+void oracle_int2_values(const uint8_t* q, int64_t nbytes, int32_t* out) {
+  for (int64_t i = 0; i < 4 * nbytes; ++i) out[i] = int2_value(q, i);
+}
 void oracle_e2m1_values(const uint8_t* q, int64_t nbytes, double* out) {
   for (int64_t i = 0; i < 2 * nbytes; ++i) out[i] = e2m1_value(nibble(q, i));
 }
@@ -256,7 +283,7 @@ void oracle_e4m3_values(const uint8_t* s, int64_t n, double* out) {
 // Dense weight matrix W[rows][cols] (double) of one canonical matrix.
 int oracle_dequant(int32_t fmt, const uint8_t* q, const void* s, float g, int32_t rows, int32_t cols,
                    double* out) {
-  if (cols % 32 || rows <= 0) return -1;
+  if (cols % 32 || rows <= 0 || fmt < FMT_INT4_ROW || fmt > FMT_INT2_ROW) return -1;
   QMat m{q, s, (double)g, rows, cols, fmt};
   for (int r = 0; r < rows; ++r)
     for (int c = 0; c < cols; ++c) out[(int64_t)r * cols + c] = m.w(r, c);

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the 4-bit MoE FFN layer.
+"""Seeded synthetic inputs for the quantised MoE FFN layer.
 
 This module only draws random numbers and encodes them into the canonical
 storage format; it holds none of the layer's arithmetic (no routing, no
@@ -7,13 +7,16 @@ CPU oracle consume the bytes it produces.
 
 Canonical storage format (all row-major, little-endian):
 
-* ``q[rows][cols/2]`` uint8 per matrix (gate ``[I][H]``, up ``[I][H]``,
-  down ``[H][I]``); element ``2j`` sits in the low nibble of byte ``j``,
-  element ``2j+1`` in the high nibble.
+* ``q[rows][cols*bits/8]`` uint8 per matrix (gate ``[I][H]``, up ``[I][H]``,
+  down ``[H][I]``).  4-bit codes: element ``2j`` sits in the low nibble of
+  byte ``j``, element ``2j+1`` in the high nibble.  INT8_ROW: one
+  two's-complement byte per element.  INT2_ROW: element ``4j+i`` in bits
+  ``2i..2i+1`` of byte ``j``, two's complement in [-2, 1].
 * INT4_ROW: a nibble is a two's-complement integer in [-8, 7]; one binary16
   scale per output row (``s[rows]``).  This is the
   "int4 with a per-row scale" format of the Colibrì engine (hakusoku.com
-  story 8412, section 実装済み機能).
+  story 8412, section 実装済み機能).  INT8_ROW and INT2_ROW are that engine's
+  int8 and int2 kernels' formats, with the same per-row binary16 scale.
 * E2M1_B16: a nibble is an OCP FP4 E2M1 code; one OCP FP8 E4M3 scale byte per
   16 consecutive weights along the row (``s[rows][cols/16]``) and one fp32
   tensor scale per matrix (``g``).  This is the NVFP4-style format that the
@@ -23,7 +26,8 @@ Canonical storage format (all row-major, little-endian):
 
 Value distributions follow the layer workloads: activations ~ N(0, 1) rounded
 to binary16, router weights ~ N(0, 0.02) fp32, expert weights ~ N(0, 0.02)
-quantised symmetrically (int4: scale = amax_row / 7; e2m1: tensor scale
+quantised symmetrically (int4: scale = amax_row / 7; int8: amax_row / 127;
+int2: amax_row / 2, codes clamped to [-2, 1]; e2m1: tensor scale
 g = amax / (6 * 448), block scale = e4m3(amax_block / (6 g))).
 """
 from __future__ import annotations
@@ -37,6 +41,14 @@ import torch
 
 INT4_ROW = 0
 E2M1_B16 = 1
+INT8_ROW = 2
+INT2_ROW = 3
+ROW_SCALED = (INT4_ROW, INT8_ROW, INT2_ROW)
+
+
+def code_bits(wfmt: int) -> int:
+    """Bits per stored weight code."""
+    return {INT4_ROW: 4, E2M1_B16: 4, INT8_ROW: 8, INT2_ROW: 2}[wfmt]
 
 # Binary16/E4M3 encoders are torch's own conversions; the e2m1 encoder below
 # picks the nearest representable magnitude by bucketing at the midpoints of
@@ -72,6 +84,11 @@ WORKLOADS = {
     "e2m1_b1": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=1),
     "e2m1_b4": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=4),
     "prefill_2048": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=2048, zipf=1.1),
+    # the same layer with int8 / int2 per-row-scale weights (hakusoku.com
+    # story 8412, section 実装済み機能: int8/int4/int2 kernels, row scales)
+    "int8_b1": dict(dims=Dims(6144, 2048, 256, 8, 1, INT8_ROW), tokens=1),
+    "int2_b1": dict(dims=Dims(6144, 2048, 256, 8, 1, INT2_ROW), tokens=1),
+    "int2_b8": dict(dims=Dims(6144, 2048, 256, 8, 1, INT2_ROW), tokens=8),
 }
 
 
@@ -101,6 +118,23 @@ def quantize_int4_rows(w: torch.Tensor):
     return pack_nibbles(q & 0xF), s16
 
 
+def quantize_int_rows(w: torch.Tensor, wfmt: int):
+    """fp32 [.., rows, cols] -> (q uint8 [.., rows, cols*bits/8], s binary16 [.., rows]) for
+    INT4_ROW, INT8_ROW or INT2_ROW."""
+    if wfmt == INT4_ROW:
+        return quantize_int4_rows(w)
+    qmin, qmax, div = (-128, 127, 127.0) if wfmt == INT8_ROW else (-2, 1, 2.0)
+    amax = w.abs().amax(dim=-1)
+    s16 = (amax / div).to(torch.float16)
+    s16 = torch.where(s16 == 0, torch.ones_like(s16), s16)
+    q = torch.clamp(torch.round(w / s16.float().unsqueeze(-1)), qmin, qmax).to(torch.int16)
+    if wfmt == INT8_ROW:
+        return (q & 0xFF).to(torch.uint8).contiguous(), s16
+    c = (q & 0x3).to(torch.uint8)
+    packed = c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)
+    return packed.contiguous(), s16
+
+
 def quantize_e2m1_blocks(w: torch.Tensor):
     """fp32 [.., rows, cols] -> (q uint8 [.., rows, cols/2], s uint8 e4m3 [.., rows, cols/16], g fp32 [..])."""
     lead = w.shape[:-2]
@@ -125,11 +159,11 @@ class Layer:
     """One MoE layer in canonical format.  Expert tensors are stacked with
     index ``n_experts`` holding the shared expert (when ``has_shared``)."""
     dims: Dims
-    q_gate: torch.Tensor  # uint8 [E+S][I][H/2]
-    s_gate: torch.Tensor  # int4: binary16 [E+S][I]; e2m1: uint8 e4m3 [E+S][I][H/16]
+    q_gate: torch.Tensor  # uint8 [E+S][I][H*bits/8]
+    s_gate: torch.Tensor  # integer formats: binary16 [E+S][I]; e2m1: uint8 e4m3 [E+S][I][H/16]
     q_up: torch.Tensor
     s_up: torch.Tensor
-    q_down: torch.Tensor  # uint8 [E+S][H][I/2]
+    q_down: torch.Tensor  # uint8 [E+S][H][I*bits/8]
     s_down: torch.Tensor
     g3: torch.Tensor      # fp32 [E+S][3] (1.0 for INT4_ROW)
     router_w: torch.Tensor  # fp32 [E][H]
@@ -149,10 +183,11 @@ def make_experts(dims: Dims, n: int, seed_tag, device="cpu", std=0.02, batch=8):
     """Quantised expert weights for ``n`` experts (the last one is the shared
     expert when the caller counts it in ``n``)."""
     H, I = dims.hidden, dims.inter
-    qg = torch.empty((n, I, H // 2), dtype=torch.uint8, device=device)
+    b = code_bits(dims.wfmt)
+    qg = torch.empty((n, I, H * b // 8), dtype=torch.uint8, device=device)
     qu = torch.empty_like(qg)
-    qd = torch.empty((n, H, I // 2), dtype=torch.uint8, device=device)
-    if dims.wfmt == INT4_ROW:
+    qd = torch.empty((n, H, I * b // 8), dtype=torch.uint8, device=device)
+    if dims.wfmt in ROW_SCALED:
         sg = torch.empty((n, I), dtype=torch.float16, device=device)
         su = torch.empty_like(sg)
         sd = torch.empty((n, H), dtype=torch.float16, device=device)
@@ -170,8 +205,8 @@ def make_experts(dims: Dims, n: int, seed_tag, device="cpu", std=0.02, batch=8):
                 for e in range(e0, e1)]) * std
             mats.append(w)
         for m, (qdst, sdst) in enumerate(((qg, sg), (qu, su), (qd, sd))):
-            if dims.wfmt == INT4_ROW:
-                q, s = quantize_int4_rows(mats[m])
+            if dims.wfmt in ROW_SCALED:
+                q, s = quantize_int_rows(mats[m], dims.wfmt)
                 qdst[e0:e1] = q
                 sdst[e0:e1] = s
             else:

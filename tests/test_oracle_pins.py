@@ -26,6 +26,21 @@ def _np_int4_codes(q: np.ndarray) -> np.ndarray:
     return out
 
 
+def _np_int8_codes(q: np.ndarray) -> np.ndarray:
+    return np.asarray(q, dtype=np.uint8).view(np.int8).astype(np.int64)
+
+
+def _np_int2_codes(q: np.ndarray) -> np.ndarray:
+    """Two's-complement 2-bit fields, element 4j+i from bits 2i..2i+1 of byte
+    j: move the field to the top of an int8 and shift it back arithmetically."""
+    q = np.asarray(q, dtype=np.uint8)
+    out = np.empty(q.shape[:-1] + (4 * q.shape[-1],), dtype=np.int64)
+    for i in range(4):
+        top = (q << (6 - 2 * i)).astype(np.uint8).view(np.int8)
+        out[..., i::4] = top >> 6
+    return out
+
+
 def _golden_e2m1():
     vals = {}
     with open(os.path.join(GOLDEN, "e2m1_values.txt")) as f:
@@ -43,8 +58,9 @@ def _np_dequant(layer, e, which):
     numpy binary16, torch E4M3 and the OCP E2M1 table."""
     q = getattr(layer, "q_" + which)[e].numpy()
     s = getattr(layer, "s_" + which)[e]
-    if layer.dims.wfmt == synth.INT4_ROW:
-        codes = _np_int4_codes(q).astype(np.float64)
+    decode = {synth.INT4_ROW: _np_int4_codes, synth.INT8_ROW: _np_int8_codes, synth.INT2_ROW: _np_int2_codes}
+    if layer.dims.wfmt in decode:
+        codes = decode[layer.dims.wfmt](q).astype(np.float64)
         return codes * s.numpy().astype(np.float64)[:, None]
     table = _golden_e2m1()
     nib = np.empty(q.shape[:-1] + (2 * q.shape[-1],), dtype=np.int64)
@@ -89,6 +105,49 @@ def test_int4_pack_unpack_round_trip(orc):
     assert np.array_equal(orc.int4_values(packed).reshape(37, 64), codes)
 
 
+def test_int8_all_256_bytes(orc):
+    q = np.arange(256, dtype=np.uint8)
+    got = orc.int8_values(q)
+    assert np.array_equal(got, np.arange(256).astype(np.uint8).view(np.int8))
+    assert got.min() == -128 and got.max() == 127
+
+
+def test_int2_all_256_bytes(orc):
+    q = np.arange(256, dtype=np.uint8)
+    got = orc.int2_values(q).reshape(256, 4)
+    assert np.array_equal(got, _np_int2_codes(q[:, None]))
+    # 0b11_10_01_00: fields from the least significant bits up are 0, 1, -2, -1
+    assert got[0xE4].tolist() == [0, 1, -2, -1]
+    assert got.min() == -2 and got.max() == 1
+
+
+@pytest.mark.parametrize("fmt,lo,hi,per_byte", [(synth.INT8_ROW, -128, 128, 1), (synth.INT2_ROW, -2, 2, 4)])
+def test_int8_int2_pack_round_trip(orc, fmt, lo, hi, per_byte):
+    """Codes packed by an explicit numpy formula read back unchanged, and the
+    encoder's codes for weights that are exact integers read back as those
+    integers."""
+    rng = np.random.default_rng(2)
+    codes = rng.integers(lo, hi, size=(5, 64))
+    codes[:, 0] = lo
+    if fmt == synth.INT8_ROW:
+        packed = (codes & 0xFF).astype(np.uint8)
+        got = orc.int8_values(packed)
+    else:
+        f = (codes & 3).astype(np.uint8)
+        packed = (f[:, 0::4] | (f[:, 1::4] << 2) | (f[:, 2::4] << 4) | (f[:, 3::4] << 6)).astype(np.uint8)
+        got = orc.int2_values(packed)
+    assert packed.shape == (5, 64 // per_byte)
+    assert np.array_equal(got.reshape(5, 64), codes)
+    # encoder: codes within its range [-127, 127] (int8) or [-2, 1] (int2)
+    # and the largest magnitude in every row, so the row scale is exactly 1
+    enc = np.clip(codes, -127, 127)
+    enc[:, 0] = -127 if fmt == synth.INT8_ROW else -2
+    q, sc = synth.quantize_int_rows(torch.tensor(enc.astype(np.float32)), fmt)
+    assert torch.all(sc == 1.0)
+    vals = orc.int8_values(q.numpy()) if fmt == synth.INT8_ROW else orc.int2_values(q.numpy())
+    assert np.array_equal(vals.reshape(5, 64), enc)
+
+
 def test_e2m1_all_16_codes(orc):
     q = np.array([c | (c2 << 4) for c in range(16) for c2 in (0,)], dtype=np.uint8)
     got = orc.e2m1_values(q)[0::2]
@@ -117,7 +176,10 @@ def test_e2m1_times_e4m3_exact_in_fp16():
     assert np.array_equal(prod.astype(np.float16).astype(np.float64), prod)
 
 
-@pytest.mark.parametrize("fmt", [synth.INT4_ROW, synth.E2M1_B16])
+ALL_FMTS = [synth.INT4_ROW, synth.E2M1_B16, synth.INT8_ROW, synth.INT2_ROW]
+
+
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_dequant_matches_independent_decode(orc, fmt):
     dims = synth.Dims(64, 128, 2, 1, 0, fmt)
     layer = synth.make_layer(dims, ("dequant", fmt))
@@ -200,7 +262,7 @@ def test_route_empty_batch(orc):
 
 
 # ---- expert FFN and the whole layer ---------------------------------------
-@pytest.mark.parametrize("fmt", [synth.INT4_ROW, synth.E2M1_B16])
+@pytest.mark.parametrize("fmt", ALL_FMTS)
 def test_single_expert_equals_dense_swiglu(orc, fmt):
     """E=1, k=1, no shared expert: the routing weight is exactly one and the
     layer is a dense SwiGLU FFN, computed here with numpy matmuls."""
