@@ -1,4 +1,4 @@
-"""Benchmark of the 4-bit MoE FFN layer on one MI355X.
+"""Benchmark of the quantised MoE FFN layer on one MI355X.
 
 A step is one call of moe_w4a16_forward (route, union, experts, combine) on
 one batch.  Steps cycle over L independent layer instances (each with all
@@ -39,6 +39,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 # launch streams the routed experts only.
 STAGES = {"decode": ("route_shared_gate_up", "gate_up", "down"), "prefill": ("route", "gate_up", "down")}
 DOMINANT = {"decode": (1, "k_gu_phase"), "prefill": (1, "k_gu_gemm")}
+WEIGHT_NAMES = {synth.INT4_ROW: "int4_row", synth.E2M1_B16: "e2m1_b16", synth.INT8_ROW: "int8_row",
+                synth.INT2_ROW: "int2_row"}
 
 
 def log(*a):
@@ -47,15 +49,15 @@ def log(*a):
 
 # ---- algorithmic work -------------------------------------------------------
 def scale_bytes(d, rows, cols):
-    return rows * 2 if d.wfmt == synth.INT4_ROW else rows * (cols // 16)
+    return rows * 2 if d.wfmt in synth.ROW_SCALED else rows * (cols // 16)
 
 
 def expert_gu_bytes(d):
-    return d.inter * d.hidden + 2 * scale_bytes(d, d.inter, d.hidden)
+    return 2 * d.inter * d.hidden * synth.code_bits(d.wfmt) // 8 + 2 * scale_bytes(d, d.inter, d.hidden)
 
 
 def expert_dn_bytes(d):
-    return d.hidden * d.inter // 2 + scale_bytes(d, d.hidden, d.inter)
+    return d.hidden * d.inter * synth.code_bits(d.wfmt) // 8 + scale_bytes(d, d.hidden, d.inter)
 
 
 def layer_bytes(d, T, n_touched):
@@ -367,7 +369,8 @@ def main():
     torch.cuda.empty_cache()
     if not args.no_secondary:
         for name, L, steps in (("decode_b8", 8, 128), ("decode_b1_topp", 8, 512), ("e2m1_b1", 32, 512),
-                               ("e2m1_b4", 32, 256), ("prefill_2048", 2, 8)):
+                               ("e2m1_b4", 32, 256), ("int8_b1", 8, 512), ("int2_b1", 8, 512),
+                               ("int2_b8", 8, 128), ("prefill_2048", 2, 8)):
             try:
                 c2, r2, _ = run_workload(name, L, steps, 32, stage_reps=2)
                 secondary.append(r2)
@@ -390,7 +393,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "hidden": d.hidden, "inter": d.inter, "experts": d.n_experts,
                    "shared_experts": d.has_shared, "top_k": d.top_k, "tokens": T,
-                   "weights": "int4_row" if d.wfmt == 0 else "e2m1_b16", "layers_chained": args.layers},
+                   "weights": WEIGHT_NAMES[d.wfmt], "layers_chained": args.layers},
         "layer_hbm_gbps": res["layer_hbm_gbps"],
         "layer_hbm_frac": res["layer_hbm_gbps"] / HBM_PEAK_GBPS,
         "mean_unique_experts": U,

@@ -68,7 +68,14 @@ typedef enum {
   /* OCP FP4 E2M1 codes; one OCP FP8 E4M3 (FN) scale per 16 consecutive
    * weights along the row, and one fp32 tensor scale g per matrix:
    * W[r][c] = e2m1(q[r][c]) * e4m3(s[r][c/16]) * g. */
-  MOE_W_E2M1_B16 = 1
+  MOE_W_E2M1_B16 = 1,
+  /* int8 two's complement in [-128, 127], or int2 two's complement in
+   * [-2, 1]; one binary16 scale per output row: W[r][c] = q[r][c] * s[r].
+   * The int8/int2 kernels with per-row scales of the Colibrì engine
+   * ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法", hakusoku.com,
+   * section 実装済み機能). */
+  MOE_W_INT8_ROW = 2,
+  MOE_W_INT2_ROW = 3
 } moe_wfmt_t;
 
 /* Layer shape (host struct).  Supported: hidden and inter multiples of 128,
@@ -110,10 +117,14 @@ size_t moe_workspace_bytes(const moe_dims_t* d, int32_t T);
 size_t moe_workspace_sync_bytes(const moe_dims_t* d);
 
 /* Canonical expert -> packed device layout (a byte permutation; the values
- * are unchanged).  Canonical inputs, all row-major on the device:
- *   q_gate, q_up: uint8 [I][H/2]; q_down: uint8 [H][I/2]; element 2j in the
- *     low nibble of byte j, element 2j+1 in the high nibble;
- *   INT4_ROW: s_gate, s_up: binary16 [I]; s_down: binary16 [H]; g3 ignored;
+ * are unchanged).  Canonical inputs, all row-major on the device, with
+ * b = 8 (INT8_ROW), 2 (INT2_ROW) or 4 (the others) bits per code:
+ *   q_gate, q_up: uint8 [I][H*b/8]; q_down: uint8 [H][I*b/8];
+ *     4-bit codes: element 2j in the low nibble of byte j, element 2j+1 in
+ *     the high nibble; INT8_ROW: one byte per element; INT2_ROW: element
+ *     4j+i in bits 2i..2i+1 of byte j;
+ *   INT4_ROW, INT8_ROW, INT2_ROW: s_gate, s_up: binary16 [I]; s_down:
+ *     binary16 [H]; g3 ignored;
  *   E2M1_B16: s_gate, s_up: uint8 E4M3 [I][H/16]; s_down: uint8 [H][I/16];
  *     g3: fp32 [3] tensor scales (gate, up, down), or NULL for 1.0.
  * packed_out receives moe_packed_bytes(d) bytes. */

@@ -1,4 +1,4 @@
-"""Python binding of the MI355X 4-bit MoE FFN layer library (libmoe_w4a16.so).
+"""Python binding of the MI355X quantised MoE FFN layer library (libmoe_w4a16.so).
 
 Argument marshalling only: every step of the layer runs in the library's HIP
 kernels.  PyTorch provides device memory and the current stream.  The
@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_w4a16.so")
 
 MOE_OK, MOE_E_INVAL, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_HIP = 0, -1, -2, -3, -4
-MOE_W_INT4_ROW, MOE_W_E2M1_B16 = 0, 1
+MOE_W_INT4_ROW, MOE_W_E2M1_B16, MOE_W_INT8_ROW, MOE_W_INT2_ROW = 0, 1, 2, 3
+_CODE_BITS = {MOE_W_INT4_ROW: 4, MOE_W_E2M1_B16: 4, MOE_W_INT8_ROW: 8, MOE_W_INT2_ROW: 2}
 
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
            "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_decode_max_tokens",
@@ -138,10 +139,11 @@ def moe_unpack(dims, packed, stream=None):
     d = _dims(dims)
     H, I = d.hidden, d.inter
     dev = packed.device
-    qg = torch.empty((I, H // 2), dtype=torch.uint8, device=dev)
+    b = _CODE_BITS.get(d.wfmt, 4)
+    qg = torch.empty((I, H * b // 8), dtype=torch.uint8, device=dev)
     qu = torch.empty_like(qg)
-    qd = torch.empty((H, I // 2), dtype=torch.uint8, device=dev)
-    if d.wfmt == MOE_W_INT4_ROW:
+    qd = torch.empty((H, I * b // 8), dtype=torch.uint8, device=dev)
+    if d.wfmt != MOE_W_E2M1_B16:
         sg = torch.empty(I, dtype=torch.float16, device=dev)
         su = torch.empty_like(sg)
         sd = torch.empty(H, dtype=torch.float16, device=dev)

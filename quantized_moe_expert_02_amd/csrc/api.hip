@@ -36,7 +36,7 @@ int check_dims(const moe_dims_t* d) {
     return MOE_E_INVAL;
   if (d->has_shared != 0 && d->has_shared != 1) return MOE_E_INVAL;
   if (!(d->top_p >= 0.0f && d->top_p <= 1.0f)) return MOE_E_INVAL;  // NaN fails too
-  if (d->wfmt != MOE_W_INT4_ROW && d->wfmt != MOE_W_E2M1_B16) return MOE_E_UNSUPPORTED;
+  if (d->wfmt < MOE_W_INT4_ROW || d->wfmt > MOE_W_INT2_ROW) return MOE_E_UNSUPPORTED;
   if (d->hidden % 128 || d->inter % 128) return MOE_E_UNSUPPORTED;
   if (d->n_experts > kMaxExperts || d->top_k > kMaxTopK) return MOE_E_UNSUPPORTED;
   if ((int64_t)d->hidden * d->inter > (int64_t)1 << 30) return MOE_E_UNSUPPORTED;

@@ -13,21 +13,28 @@ namespace moe {
 // ---------------------------------------------------------------------------
 // Packed device layout of one expert (written by moe_pack).
 //
-// Weights are stored in 1 KiB blocks of 64 rows x 32 columns: lane l of a
-// wavefront reads the 16 bytes at offset 16*l, which hold row l's 32
-// consecutive columns, so one 128-bit load per lane pulls one contiguous KiB.
-//   GU region:  for rb in [0, I/64), c in [0, H/32): [gate block][up block]
+// Weights are stored in 1 KiB blocks ("chunks") of 64 rows x C columns,
+// C = 128 / bits per code (16 for int8, 32 for the 4-bit formats, 64 for
+// int2): lane l of a wavefront reads the 16 bytes at offset 16*l, which hold
+// row l's C consecutive columns, so one 128-bit load per lane pulls one
+// contiguous KiB.
+//   GU region:  for rb in [0, I/64), c in [0, H/C): [gate block][up block]
 //               (2 KiB per step, so gate row i and up row i sit in one lane)
-//   D region:   for rb in [0, H/64), c in [0, I/32): [down block]
-// Inside a lane's 16 bytes, dword m holds columns 32c + 8m + (0..7).
-//   INT4_ROW: nibble position p (bits 4p..4p+3) of that dword holds column
-//     offset 2p (p < 4) or 2(p-4)+1 (p >= 4), stored offset-binary (q + 8),
-//     so that (d & 0x000F000F) and (d & 0x00F000F0) each yield a pair of
-//     adjacent columns.
+//   D region:   for rb in [0, H/64), c in [0, I/C): [down block]
+// Inside a lane's 16 bytes, dword m holds columns Cc + (C/4)m + (0..C/4-1),
+// arranged so that masking the dword yields binary16 pairs of adjacent
+// columns:
+//   INT4_ROW: nibble position p (bits 4p..4p+3) holds column offset 2p
+//     (p < 4) or 2(p-4)+1 (p >= 4), offset binary (q + 8): (d & 0x000F000F)
+//     and (d & 0x00F000F0) each yield a pair of adjacent columns.
 //   E2M1_B16: byte b of the dword holds columns 2b (low nibble) and 2b+1
 //     (high nibble), codes unchanged.
+//   INT8_ROW: bytes 0, 2 hold columns 0, 1 and bytes 1, 3 columns 2, 3,
+//     offset binary (q + 128).
+//   INT2_ROW: column 2j sits in bits 2j..2j+1 and column 2j+1 in bits
+//     16+2j..17+2j (j = 0..7), offset binary (q + 2).
 // Scales:
-//   INT4_ROW: binary16 gate[I], up[I], down[H].
+//   INT4_ROW, INT8_ROW, INT2_ROW: binary16 gate[I], up[I], down[H].
 //   E2M1_B16: e4m3 block scales grouped per 4 chunks (128 columns): for the
 //     GU region [rb][H/128][gate: 64 lanes x 8 B][up: 64 lanes x 8 B], for
 //     the D region [rb][I/128][64 lanes x 8 B]; byte 2j / 2j+1 of a lane's
@@ -45,13 +52,17 @@ struct Layout {
 
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Bits per weight code, and whether the format has one binary16 scale per row.
+constexpr int code_bits(int wfmt) { return wfmt == MOE_W_INT8_ROW ? 8 : wfmt == MOE_W_INT2_ROW ? 2 : 4; }
+constexpr bool row_scaled(int wfmt) { return wfmt != MOE_W_E2M1_B16; }
+
 inline Layout layout_of(const moe_dims_t& d) {
   Layout L{};
-  const size_t H = (size_t)d.hidden, I = (size_t)d.inter;
+  const size_t H = (size_t)d.hidden, I = (size_t)d.inter, b = (size_t)code_bits(d.wfmt);
   size_t off = 0;
-  L.gu_off = off; off = align256(off + I * H);        // gate + up, 4 bits each
-  L.d_off = off;  off = align256(off + H * I / 2);
-  if (d.wfmt == MOE_W_INT4_ROW) {
+  L.gu_off = off; off = align256(off + 2 * I * H * b / 8);  // gate + up
+  L.d_off = off;  off = align256(off + H * I * b / 8);
+  if (row_scaled(d.wfmt)) {
     L.sg_off = off; off = align256(off + I * 2);
     L.su_off = off; off = align256(off + I * 2);
     L.sd_off = off; off = align256(off + H * 2);

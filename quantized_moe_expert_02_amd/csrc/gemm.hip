@@ -3,13 +3,14 @@
 //
 // Each unique expert is applied to all of its tokens at once (the batch-wise
 // MoE union, "Show HN: 低速のコンピュータでGLM 5.2を動かす方法", hakusoku.com,
-// section 実装済み機能); its 4-bit weights are decoded in registers, straight
-// into matrix-core operands, as exact binary16 values (int4 codes are small
-// integers; e2m1 x e4m3 has at most 6 significant bits) -- the in-register
+// section 実装済み機能); its weights are decoded in registers, straight into
+// matrix-core operands, as exact binary16 values (int8/int4/int2 codes are
+// small integers; e2m1 x e4m3 has at most 6 significant bits) -- the in-register
 // decode of the Ornith engine ("GTX 1070向け35BパラメータMoEモデル推論エンジン公開",
 // section "VRAMとシステムメモリで重みを分割する設計") -- and multiplied on
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  Row scales (int4) or the tensor scale (e2m1) are applied
-// in the epilogue, as is the SwiGLU.
+// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  Row scales (integer
+// formats) or the tensor scale (e2m1) are applied in the epilogue, as is the
+// SwiGLU.
 //
 //   k_expert_gemm<.., 2>:  tile = 64 tokens of one expert x 512 gate rows +
 //                          512 up rows -> h (binary16, one row per pair)
@@ -28,7 +29,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 guint4;
 
 constexpr int BM = kPrefillTileRows;  // tokens per tile
-constexpr int XP = 40;                // halves per LDS token row (32 + 8 pad)
+
+// Per-format shape of one K-slice of the main loop: SC columns, WPS 16-byte
+// pieces (chunks of the packed layout) per lane and matrix, SC / 32 MFMA
+// K-steps; kDepth slices of weights in flight (a multiple of the activation
+// ring's depth, 2).
+template <int FMT>
+struct Slice {
+  static constexpr int SC = FMT == MOE_W_INT2_ROW ? 64 : 32;
+  static constexpr int WPS = FMT == MOE_W_INT8_ROW ? 2 : 1;
+  static constexpr int STEPS = SC / 32;
+  static constexpr int XP = SC + 8;  // halves per LDS token row (8 pad)
+  static constexpr int kDepth = WPS == 1 ? 6 : 2;
+};
 
 struct GemmArgs {
   const SlotEntry* slots;
@@ -57,6 +70,27 @@ __device__ __forceinline__ half8_t dequant_int4(uint32_t d) {
   const half2_t p1 = as_h2((d & 0x00F000F0u) | 0x54005400u) + k72;
   const half2_t p2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + k1032;
   const half2_t p3 = as_h2((d8 & 0x00F000F0u) | 0x54005400u) + k72;
+  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// int8 (bytes 0, 2 = columns 0, 1; bytes 1, 3 = columns 2, 3; offset
+// binary) -> 4 consecutive binary16 values: 1024 + u - 1152 = q.
+__device__ __forceinline__ void dequant_int8(uint32_t d, half2_t& p0, half2_t& p1) {
+  const half2_t k1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  p0 = as_h2((d & 0x00FF00FFu) | 0x64006400u) + k1152;
+  p1 = as_h2(((d >> 8) & 0x00FF00FFu) | 0x64006400u) + k1152;
+}
+
+// int2 (column 2j in bits 2j, column 2j+1 in bits 16+2j, offset binary) ->
+// columns 8h .. 8h+7 of the dword's 16 as binary16: the field at bit 2j
+// lands in the mantissa of 1024, 256, 64 or 16 (unit in the last place
+// 2^-2j), and base + u - (base + 2) = q.
+__device__ __forceinline__ half8_t dequant_int2(uint32_t d, int h) {
+  const uint32_t e = h ? d >> 8 : d;
+  const half2_t p0 = as_h2((e & 0x00030003u) | 0x64006400u) + half2_t{(_Float16)-1026.0f, (_Float16)-1026.0f};
+  const half2_t p1 = as_h2((e & 0x000C000Cu) | 0x5C005C00u) + half2_t{(_Float16)-258.0f, (_Float16)-258.0f};
+  const half2_t p2 = as_h2((e & 0x00300030u) | 0x54005400u) + half2_t{(_Float16)-66.0f, (_Float16)-66.0f};
+  const half2_t p3 = as_h2((e & 0x00C000C0u) | 0x4C004C00u) + half2_t{(_Float16)-18.0f, (_Float16)-18.0f};
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
@@ -94,27 +128,65 @@ __device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t&
   d3 = r23[1];
 }
 
-// One packed 64-row x 32-column block in a wavefront (lane l: row l, dword b =
-// columns 8b..8b+7) -> the B operands of four v_mfma_f32_16x16x32_f16, one per
-// 16-row group q: lane 16g+n receives row 16q+n, columns 8g..8g+7.
+// One K-slice of a 64-row block in a wavefront -> the B operands of the
+// v_mfma_f32_16x16x32_f16 steps, b[step][q] for the 16-row group q: lane
+// 16g+n receives row 16q+n and eight columns that depend on the format (the
+// A operands are read from LDS to match, see a_operand):
+//   4-bit: one chunk, dword b = columns 8b..8b+7 -> lane group g takes
+//     columns 8g..8g+7;
+//   int8: two chunks, dword b = columns 4b..4b+3 of each -> lane group g
+//     takes columns 4g..4g+3 and 16+4g..16+4g+3;
+//   int2: one chunk of 64 columns, dword b = columns 16b..16b+15 -> lane
+//     group g takes columns 16g+8s .. 16g+8s+7 in step s.
 // E2M1: `sc` holds this lane's two block-scale bytes (columns 0-15, 16-31).
 template <int FMT>
-__device__ __forceinline__ void block_to_operands(u32x4 w, uint32_t sc, half8_t (&b)[4]) {
-  uint32_t d0 = w.x, d1 = w.y, d2 = w.z, d3 = w.w;
+__device__ __forceinline__ void block_to_operands(const u32x4 (&w)[Slice<FMT>::WPS], uint32_t sc,
+                                                  half8_t (&b)[Slice<FMT>::STEPS][4]) {
+  uint32_t d0 = w[0].x, d1 = w[0].y, d2 = w[0].z, d3 = w[0].w;
   transpose4(d0, d1, d2, d3);
+  const uint32_t d[4] = {d0, d1, d2, d3};
   if (FMT == MOE_W_INT4_ROW) {
-    b[0] = dequant_int4(d0);
-    b[1] = dequant_int4(d1);
-    b[2] = dequant_int4(d2);
-    b[3] = dequant_int4(d3);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) b[0][q] = dequant_int4(d[q]);
+  } else if (FMT == MOE_W_INT8_ROW) {
+    uint32_t f0 = w[Slice<FMT>::WPS - 1].x, f1 = w[Slice<FMT>::WPS - 1].y, f2 = w[Slice<FMT>::WPS - 1].z,
+             f3 = w[Slice<FMT>::WPS - 1].w;
+    transpose4(f0, f1, f2, f3);
+    const uint32_t f[4] = {f0, f1, f2, f3};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      half2_t p0, p1, p2, p3;
+      dequant_int8(d[q], p0, p1);
+      dequant_int8(f[q], p2, p3);
+      b[0][q] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+  } else if (FMT == MOE_W_INT2_ROW) {
+#pragma unroll
+    for (int st = 0; st < Slice<FMT>::STEPS; ++st)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) b[st][q] = dequant_int2(d[q], st);
   } else {
     uint32_t t0 = sc & 0xFF, t1 = sc & 0xFF, t2 = (sc >> 8) & 0xFF, t3 = (sc >> 8) & 0xFF;
     transpose4(t0, t1, t2, t3);
-    b[0] = dequant_e2m1(d0, e4m3_half2(t0));
-    b[1] = dequant_e2m1(d1, e4m3_half2(t1));
-    b[2] = dequant_e2m1(d2, e4m3_half2(t2));
-    b[3] = dequant_e2m1(d3, e4m3_half2(t3));
+    b[0][0] = dequant_e2m1(d[0], e4m3_half2(t0));
+    b[0][1] = dequant_e2m1(d[1], e4m3_half2(t1));
+    b[0][2] = dequant_e2m1(d[2], e4m3_half2(t2));
+    b[0][3] = dequant_e2m1(d[3], e4m3_half2(t3));
   }
+}
+
+// A operand of MFMA step `st` for token row `r` of an LDS slice, matching
+// block_to_operands' columns for lane group g.
+template <int FMT>
+__device__ __forceinline__ half8_t a_operand(const _Float16* row, int g, int st) {
+  if (FMT == MOE_W_INT8_ROW) {
+    typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+    const half4_t lo = *reinterpret_cast<const half4_t*>(row + 4 * g);
+    const half4_t hi = *reinterpret_cast<const half4_t*>(row + 16 + 4 * g);
+    return half8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  }
+  if (FMT == MOE_W_INT2_ROW) return *reinterpret_cast<const half8_t*>(row + 16 * g + 8 * st);
+  return *reinterpret_cast<const half8_t*>(row + 8 * g);
 }
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
@@ -147,6 +219,8 @@ constexpr int kGemmWaves = 8;  // wavefronts per workgroup, 64 rows each
 
 template <int FMT, int NM>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int nx) {
+  typedef Slice<FMT> SL;
+  constexpr int SC = SL::SC, WPS = SL::WPS, XP = SL::XP;
   __shared__ __attribute__((aligned(16))) _Float16 sx[2][BM][XP];
   __shared__ int s_act[BM], s_out[BM];
   __shared__ float s_w[BM];
@@ -174,32 +248,34 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   }
   __syncthreads();
   const uint16_t* act = (NM == 2) ? a.x : a.h;
-  const int nch = K / 32;
-  // this thread's 16-byte share of an activation slice: token tid/4, columns
-  // 8*(tid%4) (threads 0..255; the others only compute)
-  const bool xload = tid < 4 * BM;
-  const int xm = (tid >> 2) & (BM - 1), xq = tid & 3;
+  const int nch = K / SC;  // slices
+  // this thread's 16-byte share of an activation slice: token tid/(SC/8),
+  // columns 8*(tid%(SC/8)) (threads past BM*SC/8 only compute)
+  constexpr int XQ = SC / 8;
+  const bool xload = tid < XQ * BM;
+  const int xm = (tid / XQ) & (BM - 1), xq = tid % XQ;
   const int xrow = xload ? s_act[xm] : -1;
   const uint16_t* xsrc = act + (size_t)(xrow < 0 ? 0 : xrow) * K + 8 * xq;
-  // weights: lane's 16 bytes of block (rb, chunk c) of matrix m
+  // weights: lane's 16 bytes of block (rb, chunk c) of matrix m; a slice is
+  // WPS chunks, nch * WPS chunks per row
   const guint4* wsrc;
   const uint8_t* ssrc = nullptr;
   if (NM == 2) {
-    wsrc = (const guint4*)(se.base + a.L.gu_off) + (size_t)rb * nch * 2 * 64 + lane;
+    wsrc = (const guint4*)(se.base + a.L.gu_off) + (size_t)rb * nch * WPS * 2 * 64 + lane;
     if (FMT == MOE_W_E2M1_B16) ssrc = se.base + a.L.sgu_off + ((size_t)rb * (K / 128) * 2 * 64 + lane) * 8;
   } else {
-    wsrc = (const guint4*)(se.base + a.L.d_off) + (size_t)rb * nch * 64 + lane;
+    wsrc = (const guint4*)(se.base + a.L.d_off) + (size_t)rb * nch * WPS * 64 + lane;
     if (FMT == MOE_W_E2M1_B16) ssrc = se.base + a.L.sdd_off + ((size_t)rb * (K / 128) * 64 + lane) * 8;
   }
-  auto load_w = [&](int c, int m) -> u32x4 {
-    return __builtin_nontemporal_load(wsrc + ((size_t)c * NM + m) * 64);
+  auto load_w = [&](int c, int m, int p) -> u32x4 {
+    return __builtin_nontemporal_load(wsrc + ((size_t)(c * WPS + p) * NM + m) * 64);
   };
   auto load_s = [&](int c, int m) -> uint32_t {
     const uint8_t* p = ssrc + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3);
     return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
   };
   auto load_x = [&](int c) -> u32x4 {
-    return xrow < 0 ? u32x4{0, 0, 0, 0} : *reinterpret_cast<const u32x4*>(xsrc + 32 * c);
+    return xrow < 0 ? u32x4{0, 0, 0, 0} : *reinterpret_cast<const u32x4*>(xsrc + SC * c);
   };
 
   f32x4 acc[NM][4][4];  // [matrix][row group q][token group mt]
@@ -212,8 +288,8 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
 
   // Weights stream through a ring of kDepth register slices (loads issued
   // kDepth slices ahead); activations through a double-buffered LDS slice.
-  constexpr int kDepth = 6;
-  u32x4 ring[kDepth][NM];
+  constexpr int kDepth = SL::kDepth;
+  u32x4 ring[kDepth][NM][WPS];
   uint32_t sring[kDepth][NM];
 #pragma unroll
   for (int j = 0; j < kDepth; ++j)
@@ -221,12 +297,14 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     for (int m = 0; m < NM; ++m) {
       sring[j][m] = 0;
       if (active && j < nch) {
-        ring[j][m] = load_w(j, m);
+#pragma unroll
+        for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(j, m, p);
         if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(j, m);
       }
     }
   // activation slices: register ring kXDepth deep feeding the LDS double buffer
   constexpr int kXDepth = 2;
+  static_assert(kDepth % kXDepth == 0, "xring slot j % kXDepth must hold slice c + 1");
   u32x4 xring[kXDepth];
 #pragma unroll
   for (int j = 0; j < kXDepth; ++j) xring[j] = (j + 1 < nch) ? load_x(j + 1) : u32x4{0, 0, 0, 0};
@@ -242,29 +320,36 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
       const u32x4 xn = xring[j % kXDepth];
       if (c + 1 + kXDepth < nch) xring[j % kXDepth] = load_x(c + 1 + kXDepth);
       if (active) {
-        u32x4 wv[NM];
+        u32x4 wv[NM][WPS];
         uint32_t sv[NM];
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          wv[m] = ring[j][m];
+#pragma unroll
+          for (int p = 0; p < WPS; ++p) wv[m][p] = ring[j][m][p];
           sv[m] = sring[j][m];
           if (c + kDepth < nch) {
-            ring[j][m] = load_w(c + kDepth, m);
+#pragma unroll
+            for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(c + kDepth, m, p);
             if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(c + kDepth, m);
           }
         }
-        half8_t av[4];
+        half8_t av[SL::STEPS][4];
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt) av[mt] = *reinterpret_cast<const half8_t*>(&sx[c & 1][16 * mt + n][8 * g]);
+        for (int st = 0; st < SL::STEPS; ++st)
+#pragma unroll
+          for (int mt = 0; mt < 4; ++mt) av[st][mt] = a_operand<FMT>(&sx[c & 1][16 * mt + n][0], g, st);
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          half8_t b[4];
+          half8_t b[SL::STEPS][4];
           block_to_operands<FMT>(wv[m], sv[m], b);
 #pragma unroll
-          for (int q = 0; q < 4; ++q)
+          for (int st = 0; st < SL::STEPS; ++st)
 #pragma unroll
-            for (int mt = 0; mt < 4; ++mt)
-              acc[m][q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[mt], b[q], acc[m][q][mt], 0, 0, 0);
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+              for (int mt = 0; mt < 4; ++mt)
+                acc[m][q][mt] =
+                    __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][mt], b[st][q], acc[m][q][mt], 0, 0, 0);
         }
       }
       if (xload && c + 1 < nch) *reinterpret_cast<u32x4*>(&sx[(c + 1) & 1][xm][8 * xq]) = xn;
@@ -278,7 +363,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     const int row = rb * 64 + 16 * q + n;
     if (NM == 2) {
       float sgv, suv;
-      if (FMT == MOE_W_INT4_ROW) {
+      if (row_scaled(FMT)) {
         sgv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sg_off)[row]);
         suv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.su_off)[row]);
       } else {
@@ -298,7 +383,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
         }
     } else {
       float sd;
-      if (FMT == MOE_W_INT4_ROW)
+      if (row_scaled(FMT))
         sd = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sd_off)[row]);
       else
         sd = reinterpret_cast<const float*>(se.base + a.L.g3_off)[2];
@@ -355,16 +440,16 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   const int rows_per_wg = 64 * kGemmWaves;
   const int nx_gu = (p.I + rows_per_wg - 1) / rows_per_wg, nx_dn = (p.H + rows_per_wg - 1) / rows_per_wg;
   const dim3 blk(64 * kGemmWaves);
-  if (d.wfmt == MOE_W_INT4_ROW)
-    launch_k(k_expert_gemm<MOE_W_INT4_ROW, 2>, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
-  else
-    launch_k(k_expert_gemm<MOE_W_E2M1_B16, 2>, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (d.wfmt == MOE_W_INT4_ROW)
-    launch_k(k_expert_gemm<MOE_W_INT4_ROW, 1>, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
-  else
-    launch_k(k_expert_gemm<MOE_W_E2M1_B16, 1>, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
+  auto gemms = [&](auto gu, auto dn) {
+    launch_k(gu, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
+    launch_k(dn, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
+  };
+  switch (d.wfmt) {
+    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2>, k_expert_gemm<MOE_W_INT4_ROW, 1>); break;
+    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2>, k_expert_gemm<MOE_W_INT8_ROW, 1>); break;
+    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1>); break;
+    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2>, k_expert_gemm<MOE_W_E2M1_B16, 1>); break;
+  }
   launch_k(k_combine, dim3((p.H + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
   return hipGetLastError();
 }

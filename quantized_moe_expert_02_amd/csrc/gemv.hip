@@ -1,5 +1,6 @@
 // Decode path (small batches): the experts of the batch union as split-K
-// GEMVs that stream the packed 4-bit weights once per unique expert.
+// GEMVs that stream the packed weights (4-, 8- or 2-bit codes) once per
+// unique expert.
 //
 // Weights are decoded in registers right before the dot products, never
 // expanded to fp16 in memory -- the design the Ornith engine uses for its
@@ -11,15 +12,12 @@
 //
 // Work split.  A unit is one wavefront: (expert slot, block of 64 output
 // rows, K-segment).  Lane l owns output row 64*rb + l and streams that row's
-// 32-column chunks as 128-bit loads (one contiguous KiB per wavefront per
-// load).  Activations are wave-uniform, so they are read through the scalar
-// cache.  Each unit writes fp32 partial sums; the last unit of a group (a
-// device-scope atomic counter, fence-protected) reduces the partials in a
-// fixed order, so results are deterministic and no float atomics are used.
-//
-//   k_gu_gemv:  gate and up rows together -> SwiGLU -> h (binary16)
-//   k_dn_gemv:  down rows -> scaled partials -> routing-weighted combine of
-//               the k slots plus the shared expert -> y (binary16)
+// 16-byte chunks as 128-bit loads (one contiguous KiB per wavefront per
+// load).  Activations are wave-uniform: x is read through the scalar cache,
+// h through LDS.  Partial sums are reduced in a fixed order (LDS within a
+// workgroup, device-scope arrival counters across workgroups), so results
+// are deterministic and no float atomics are used.  The three launches are
+// described below, before the kernels.
 #include "wave.h"
 
 namespace moe {
@@ -39,32 +37,82 @@ typedef __attribute__((address_space(3))) const u32x4 lu32x4;
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
-// The two nibble masks live in VGPRs so that each mask-and-insert below is a
-// single v_and_or_b32 (a VOP3 instruction takes no literal on gfx9, and only
-// one scalar operand).
-struct Int4Masks {
-  uint32_t lo, hi;
+// Per-format constants of the packed layout (common.h): C columns per
+// 1 KiB chunk, XPC activation vectors (8 binary16 each) per chunk, U chunks
+// per ring batch (128 columns for int2, else 4 chunks; an E2M1 scale group
+// is 4 chunks).
+template <int FMT>
+struct Fmt {
+  static constexpr int C = 128 / code_bits(FMT);
+  static constexpr int XPC = C / 8;
+  static constexpr int U = FMT == MOE_W_INT2_ROW ? 2 : 4;
 };
 
-__device__ __forceinline__ Int4Masks int4_masks() {
-  Int4Masks m;
-  asm volatile("v_mov_b32 %0, 0x000F000F" : "=v"(m.lo));
-  asm volatile("v_mov_b32 %0, 0x00F000F0" : "=v"(m.hi));
-  return m;
+// The masks live in VGPRs so that each mask-and-insert below is a single
+// v_and_or_b32 (a VOP3 instruction takes no literal on gfx9, and only one
+// scalar operand).
+struct Masks {
+  uint32_t m[4];
+};
+
+__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ Masks make_masks() {
+  Masks k{};
+  if (FMT == MOE_W_INT4_ROW) {
+    k.m[0] = vgpr_const(0x000F000Fu);
+    k.m[1] = vgpr_const(0x00F000F0u);
+  } else if (FMT == MOE_W_INT8_ROW) {
+    k.m[0] = vgpr_const(0x00FF00FFu);
+  } else if (FMT == MOE_W_INT2_ROW) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.m[j] = vgpr_const(0x00030003u << (2 * j));
+  }
+  return k;
 }
 
 // int4 (device order, offset binary) -> four half2 pairs of exact integers.
 // (d & 0x000F000F) | 0x6400 gives 1024 + u; (d & 0x00F000F0) | 0x5400 gives
 // 64 + u; subtracting 1032 / 72 leaves q = u - 8 exactly.
-__device__ __forceinline__ void dec_int4(uint32_t d, const Int4Masks& mk, half2_t& p0, half2_t& p1, half2_t& p2,
+__device__ __forceinline__ void dec_int4(uint32_t d, const Masks& mk, half2_t& p0, half2_t& p1, half2_t& p2,
                                          half2_t& p3) {
   const half2_t k1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t d8 = d >> 8;
-  p0 = as_h2((d & mk.lo) | 0x64006400u) + k1032;
-  p1 = as_h2((d & mk.hi) | 0x54005400u) + k72;
-  p2 = as_h2((d8 & mk.lo) | 0x64006400u) + k1032;
-  p3 = as_h2((d8 & mk.hi) | 0x54005400u) + k72;
+  p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1032;
+  p1 = as_h2((d & mk.m[1]) | 0x54005400u) + k72;
+  p2 = as_h2((d8 & mk.m[0]) | 0x64006400u) + k1032;
+  p3 = as_h2((d8 & mk.m[1]) | 0x54005400u) + k72;
+}
+
+// int8 (bytes 0, 2 = columns 0, 1; bytes 1, 3 = columns 2, 3; offset
+// binary) -> two half2 pairs: (d & 0x00FF00FF) | 0x6400 gives 1024 + u, and
+// 1024 + u - 1152 = q exactly (|q| <= 128).
+__device__ __forceinline__ void dec_int8(uint32_t d, const Masks& mk, half2_t& p0, half2_t& p1) {
+  const half2_t k1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
+  p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1152;
+  p1 = as_h2(((d >> 8) & mk.m[0]) | 0x64006400u) + k1152;
+}
+
+// int2 (columns 2j / 2j+1 in bits 2j / 16+2j; offset binary) -> eight half2
+// pairs.  The field at bit 2j (j < 4) is placed in the mantissa of a binary16
+// whose unit in the last place is 2^-2j, i.e. 1024, 256, 64, 16 + u; pairs
+// 4..7 take the same fields of d >> 8.  Subtracting base + 2 leaves q.
+__device__ __forceinline__ void dec_int2(uint32_t d, const Masks& mk, half2_t (&p)[8]) {
+  const uint32_t magic[4] = {0x64006400u, 0x5C005C00u, 0x54005400u, 0x4C004C00u};
+  const float off[4] = {-1026.0f, -258.0f, -66.0f, -18.0f};
+  const uint32_t d8 = d >> 8;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const half2_t k = {(_Float16)off[j], (_Float16)off[j]};
+    p[j] = as_h2((d & mk.m[j]) | magic[j]) + k;
+    p[4 + j] = as_h2((d8 & mk.m[j]) | magic[j]) + k;
+  }
 }
 
 // e2m1 codes (byte b = columns 2b, 2b+1) -> four half2 pairs, multiplied by
@@ -112,42 +160,67 @@ __device__ __forceinline__ void load_batch(const guint4* __restrict__ w, const g
   }
 }
 
+// Dword i of a chunk of matrix m against the chunk's activations xv.
+template <int FMT, int NM, int NT, int XPC>
+__device__ __forceinline__ void dot_dword(uint32_t d, int i, int m, half2_t s, const u32x4 (&xv)[NT][XPC],
+                                          const Masks& mk, float (&acc)[NM][NT]) {
+  if (FMT == MOE_W_INT8_ROW) {  // columns 4i .. 4i+3
+    half2_t p0, p1;
+    dec_int8(d, mk, p0, p1);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 v = xv[t][i / 2];
+      acc[m][t] = __builtin_amdgcn_fdot2(p0, as_h2((i & 1) ? v.z : v.x), acc[m][t], false);
+      acc[m][t] = __builtin_amdgcn_fdot2(p1, as_h2((i & 1) ? v.w : v.y), acc[m][t], false);
+    }
+  } else if (FMT == MOE_W_INT2_ROW) {  // columns 16i .. 16i+15
+    half2_t p[8];
+    dec_int2(d, mk, p);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      acc[m][t] = dot8(p[0], p[1], p[2], p[3], xv[t][2 * i], acc[m][t]);
+      acc[m][t] = dot8(p[4], p[5], p[6], p[7], xv[t][2 * i + 1], acc[m][t]);
+    }
+  } else {  // columns 8i .. 8i+7
+    half2_t p0, p1, p2, p3;
+    if (FMT == MOE_W_INT4_ROW) dec_int4(d, mk, p0, p1, p2, p3);
+    else dec_e2m1(d, s, p0, p1, p2, p3);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[m][t] = dot8(p0, p1, p2, p3, xv[t][i], acc[m][t]);
+  }
+}
+
 template <int FMT, int NM, int NT, int U, typename AP>
 __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u32x2 (&sv)[NM], int c,
-                                              const AP* act, const Int4Masks& mk, float (&acc)[NM][NT]) {
+                                              const AP* act, const Masks& mk, float (&acc)[NM][NT]) {
+  constexpr int XPC = Fmt<FMT>::XPC;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     // keep each chunk's activation loads next to their use: hoisting them
-    // over the whole batch needs 16*NT registers per chunk at once
+    // over the whole batch needs U*XPC*4*NT registers at once
     __builtin_amdgcn_sched_barrier(0);
-    u32x4 xv[NT][4];
+    u32x4 xv[NT][XPC];
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) xv[t][i] = act[t][(c + u) * 4 + i];
+      for (int i = 0; i < XPC; ++i) xv[t][i] = act[t][(c + u) * XPC + i];
 #pragma unroll
     for (int m = 0; m < NM; ++m) {
       const uint32_t dw[4] = {wv[u][m].x, wv[u][m].y, wv[u][m].z, wv[u][m].w};
-      half2_t s0, s1;
+      half2_t s0{}, s1{};
       if (FMT == MOE_W_E2M1_B16) {
         const uint32_t sb = (u < 2) ? sv[m].x : sv[m].y;
         s0 = e4m3_pair(sb, (u & 1) * 2);
         s1 = e4m3_pair(sb, (u & 1) * 2 + 1);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        half2_t p0, p1, p2, p3;
-        if (FMT == MOE_W_INT4_ROW) dec_int4(dw[i], mk, p0, p1, p2, p3);
-        else dec_e2m1(dw[i], i < 2 ? s0 : s1, p0, p1, p2, p3);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) acc[m][t] = dot8(p0, p1, p2, p3, xv[t][i], acc[m][t]);
-      }
+      for (int i = 0; i < 4; ++i) dot_dword<FMT, NM, NT, XPC>(dw[i], i, m, i < 2 ? s0 : s1, xv, mk, acc);
     }
   }
 }
 
-// Streams `nch` chunks (a multiple of 4) for NM matrices (gate+up: NM=2) and
-// NT activation rows into acc through a ring of D four-chunk batches: the
+// Streams `nch` chunks (a multiple of U) for NM matrices (gate+up: NM=2) and
+// NT activation rows into acc through a ring of D batches of U chunks: the
 // first D batches are requested at once, then `pre()` runs (a caller's own
 // loads, overlapping the weights in flight), and every batch is reloaded with
 // the batch D ahead right after it has been decoded and multiplied.
@@ -155,14 +228,15 @@ __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u3
 //      chunk c is at w + (c*NM + m)*64 (uint4 units).
 //   sc: E2M1 only: this lane's 8 scale bytes of the first 4-chunk group of
 //      matrix 0; matrix m of group g is at sc + (g*NM + m)*64 (uint2 units).
-//   act[t]: wave-uniform activation rows, already offset to column 32*c0.
-//      Rows that stay unchanged for the whole launch are passed as
-//      constant-address-space pointers, which makes their loads scalar.
+//   act[t]: wave-uniform activation rows, already offset to the first
+//      chunk's columns.  Rows that stay unchanged for the whole launch are
+//      passed as constant-address-space pointers, which makes their loads
+//      scalar.
 template <int FMT, int NM, int NT, int D, typename AP, typename Pre>
 __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const guint2* __restrict__ sc,
                                             const AP* act, int nch, float (&acc)[NM][NT], Pre&& pre) {
-  const Int4Masks mk = int4_masks();
-  constexpr int U = 4;  // chunks per batch (one E2M1 scale group)
+  const Masks mk = make_masks<FMT>();
+  constexpr int U = Fmt<FMT>::U;
   u32x4 wv[D][U][NM];
   u32x2 sv[D][NM];
   const int nb = nch / U;
@@ -206,9 +280,9 @@ __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const 
 // ===========================================================================
 
 constexpr int kWpg = 4;           // wavefronts per workgroup
-constexpr int kStageChunks = 32;  // h columns staged in LDS per step: 32 x 32
-constexpr int kGuDepth = 2;       // gate/up: 4-chunk batches in flight (16 KiB)
-constexpr int kDnDepth = 2;       // down: 4-chunk batches in flight (8 KiB)
+constexpr int kStageCols = 1024;  // h columns staged in LDS per step
+constexpr int kStageVec = kStageCols / 8;  // ... as 16-byte vectors per token
+constexpr int kRingChunks = 8;    // chunks in flight per matrix (gate/up: 16 KiB, down: 8 KiB)
 constexpr int kSyRouter = 64;     // router arrival counters (uint32 index in the sync region):
 constexpr int kRouterGroups = 8;  //   top counter, then one per group of router workgroups
 
@@ -238,7 +312,7 @@ struct DecArgs {
   uint32_t* gu_cnt;   // [I/64] shared-expert groups
   uint32_t* dn_cnt;   // [H/64]
   int ks_gu, ks_sgu, ks_dn;     // K-segments: routed gate/up, shared gate/up, down
-  int cpu_gu, cpu_sgu, cpu_dn;  // 32-column chunks per K-segment
+  int cpu_gu, cpu_sgu, cpu_dn;  // chunks per K-segment
   int slots_max, rows_total;
   int rsplit, seg4;   // router units per expert, 16-byte columns per router unit
   int n_router;       // E * rsplit
@@ -488,7 +562,8 @@ __device__ __forceinline__ void gu_stream(const DecArgs& a, const uint16_t* __re
                                           int rb, int ks, int nch, int i0, float (&acc)[2][NT]) {
   const int lane = threadIdx.x & 63;
   const int c0 = ks * nch;
-  const guint4* w = (const guint4*)(si.base + a.L.gu_off) + ((size_t)rb * (a.H / 32) + c0) * 2 * 64 + lane;
+  constexpr int C = Fmt<FMT>::C;
+  const guint4* w = (const guint4*)(si.base + a.L.gu_off) + ((size_t)rb * (a.H / C) + c0) * 2 * 64 + lane;
   const guint2* sc = nullptr;
   if (FMT == MOE_W_E2M1_B16)
     sc = (const guint2*)(si.base + a.L.sgu_off) + ((size_t)rb * (a.H / 128) + c0 / 4) * 2 * 64 + lane;
@@ -497,11 +572,11 @@ __device__ __forceinline__ void gu_stream(const DecArgs& a, const uint16_t* __re
   for (int t = 0; t < NT; ++t) {
     int tok, row;
     slot_token(a, si, i0 + t, tok, row);
-    act[t] = (const cu32x4*)(x + (size_t)tok * a.H + 32 * c0);
+    act[t] = (const cu32x4*)(x + (size_t)tok * a.H + C * c0);
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[0][t] = acc[1][t] = 0.f;
-  stream_ring<FMT, 2, NT, kGuDepth>(w, sc, act, nch, acc, [] {});
+  stream_ring<FMT, 2, NT, kRingChunks / Fmt<FMT>::U>(w, sc, act, nch, acc, [] {});
 }
 
 // h for token row `row` of this block from its gate/up sums (wavefront 0).
@@ -509,7 +584,7 @@ template <int FMT>
 __device__ __forceinline__ void gu_finish(const DecArgs& a, const SlotInfo& si, int rb, int row, float g, float u) {
   const int r = 64 * rb + (threadIdx.x & 63);
   float sg, su;
-  if (FMT == MOE_W_INT4_ROW) {
+  if (row_scaled(FMT)) {
     sg = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sg_off)[r]);
     su = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.su_off)[r]);
   } else {
@@ -603,12 +678,12 @@ __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __res
 // Wavefront w streams K-segment w for a tile of NT tokens, with its h row
 // pieces staged in its own LDS region: vector loads of h mixed into the
 // weight stream would make every weight batch wait for them (the vector
-// memory counter retires in order), so each step of kStageChunks chunks
+// memory counter retires in order), so each step of kStageCols columns
 // requests its first weight batches, then stages h while those are in
 // flight, then streams.
 template <int KT>
 struct DnLds {
-  u32x4 h[kWpg][KT * kStageChunks * 4];  // per wavefront: KT tokens x 32 chunks x 64 B
+  u32x4 h[kWpg][KT * kStageVec];  // per wavefront: KT tokens x kStageCols binary16
   float r[kWpg][KT][64];
 };
 
@@ -619,28 +694,29 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
   const bool active = rb < a.H / 64;  // the last workgroup of a slot may overhang
   if (active) {
     const int c0 = seg * a.cpu_dn;
-    const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / 32) + c0) * 64 + lane;
+    constexpr int C = Fmt<FMT>::C, XPC = Fmt<FMT>::XPC, kStage = kStageCols / C;
+    const guint4* w = (const guint4*)(si.base + a.L.d_off) + ((size_t)rb * (a.I / C) + c0) * 64 + lane;
     const guint2* sc = nullptr;
     if (FMT == MOE_W_E2M1_B16)
       sc = (const guint2*)(si.base + a.L.sdd_off) + ((size_t)rb * (a.I / 128) + c0 / 4) * 64 + lane;
     u32x4* hl = ls.h[wave];
     const lu32x4* act[NT];  // LDS
 #pragma unroll
-    for (int t = 0; t < NT; ++t) act[t] = (const lu32x4*)(hl + t * kStageChunks * 4);
+    for (int t = 0; t < NT; ++t) act[t] = (const lu32x4*)(hl + t * kStageVec);
     float acc[1][NT];
 #pragma unroll
     for (int t = 0; t < NT; ++t) acc[0][t] = 0.f;
-    for (int p0 = 0; p0 < a.cpu_dn; p0 += kStageChunks) {
-      const int np = min(kStageChunks, a.cpu_dn - p0);
+    for (int p0 = 0; p0 < a.cpu_dn; p0 += kStage) {
+      const int np = min(kStage, a.cpu_dn - p0);
       wave_lds_sync();  // the previous step's LDS reads are done
-      stream_ring<FMT, 1, NT, kDnDepth>(
+      stream_ring<FMT, 1, NT, kRingChunks / Fmt<FMT>::U>(
           w + (size_t)p0 * 64, FMT == MOE_W_E2M1_B16 ? sc + (size_t)(p0 / 4) * 64 : sc, act, np, acc, [&] {
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
               int tok, row;
               slot_token(a, si, i0 + t, tok, row);
-              const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)row * a.I + 32 * c0);
-              for (int q = lane; q < np * 4; q += 64) hl[t * kStageChunks * 4 + q] = src[p0 * 4 + q];
+              const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)row * a.I + C * c0);
+              for (int q = lane; q < np * XPC; q += 64) hl[t * kStageVec + q] = src[p0 * XPC + q];
             }
             wave_lds_sync();
           });
@@ -672,7 +748,7 @@ __device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rbg, DnLds<
   const int rb = rbg * (kWpg / a.ks_dn) + wave / a.ks_dn, seg = wave % a.ks_dn;
   const int r = 64 * min(rb, a.H / 64 - 1) + lane;
   float scale;
-  if (FMT == MOE_W_INT4_ROW)
+  if (row_scaled(FMT))
     scale = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sd_off)[r]);
   else
     scale = reinterpret_cast<const float*>(si.base + a.L.g3_off)[2];
@@ -787,9 +863,10 @@ hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t
   a.ks_gu = p.ks_gu;
   a.ks_sgu = p.ks_sgu;
   a.ks_dn = p.ks_dn;
-  a.cpu_gu = (p.H / 32) / p.ks_gu;
-  a.cpu_sgu = (p.H / 32) / p.ks_sgu;
-  a.cpu_dn = (p.I / 32) / p.ks_dn;
+  const int C = 128 / code_bits(d.wfmt);  // columns per chunk
+  a.cpu_gu = (p.H / C) / p.ks_gu;
+  a.cpu_sgu = (p.H / C) / p.ks_sgu;
+  a.cpu_dn = (p.I / C) / p.ks_dn;
   a.slots_max = p.slots_max;
   a.rows_total = p.rows_total;
   // router units: enough column segments that each needs one batch of loads
@@ -799,9 +876,16 @@ hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t
   a.n_router = p.E * a.rsplit;
   a.n_router_wg = (a.n_router + kWpg - 1) / kWpg;
   // a single token never needs the two-token tiles, which cost registers
-  if (d.wfmt == MOE_W_INT4_ROW)
-    return p.T == 1 ? launch_phases<MOE_W_INT4_ROW, 1>(a, x, s, se) : launch_phases<MOE_W_INT4_ROW, 2>(a, x, s, se);
-  return p.T == 1 ? launch_phases<MOE_W_E2M1_B16, 1>(a, x, s, se) : launch_phases<MOE_W_E2M1_B16, 2>(a, x, s, se);
+  switch (d.wfmt) {
+    case MOE_W_INT4_ROW:
+      return p.T == 1 ? launch_phases<MOE_W_INT4_ROW, 1>(a, x, s, se) : launch_phases<MOE_W_INT4_ROW, 2>(a, x, s, se);
+    case MOE_W_INT8_ROW:
+      return p.T == 1 ? launch_phases<MOE_W_INT8_ROW, 1>(a, x, s, se) : launch_phases<MOE_W_INT8_ROW, 2>(a, x, s, se);
+    case MOE_W_INT2_ROW:
+      return p.T == 1 ? launch_phases<MOE_W_INT2_ROW, 1>(a, x, s, se) : launch_phases<MOE_W_INT2_ROW, 2>(a, x, s, se);
+    default:
+      return p.T == 1 ? launch_phases<MOE_W_E2M1_B16, 1>(a, x, s, se) : launch_phases<MOE_W_E2M1_B16, 2>(a, x, s, se);
+  }
 }
 
 }  // namespace moe

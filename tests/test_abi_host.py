@@ -39,15 +39,16 @@ def test_status_strings(L):
         assert moe.moe_status_string(c)
 
 
-DIMS = [synth.Dims(6144, 2048, 256, 8, 1, 0), synth.Dims(2048, 512, 256, 8, 1, 1), synth.Dims(256, 128, 8, 2, 1, 0)]
+DIMS = [synth.Dims(6144, 2048, 256, 8, 1, 0), synth.Dims(2048, 512, 256, 8, 1, 1), synth.Dims(256, 128, 8, 2, 1, 0),
+        synth.Dims(6144, 2048, 256, 8, 1, 2), synth.Dims(6144, 2048, 256, 8, 1, 3), synth.Dims(256, 128, 8, 2, 1, 3)]
 
 
 @pytest.mark.parametrize("d", DIMS)
 def test_sizes(L, d):
     pb = moe.moe_packed_bytes(d)
-    wbytes = d.inter * d.hidden * 3 // 2
+    wbytes = d.inter * d.hidden * 3 * synth.code_bits(d.wfmt) // 8
     assert pb >= wbytes and pb % 256 == 0
-    if d.wfmt == 0:
+    if d.wfmt in synth.ROW_SCALED:
         assert pb - wbytes < 2 * (2 * d.inter + d.hidden) + 4 * 256
     if d == DIMS[0]:
         assert wbytes + 2 * (2 * d.inter + d.hidden) == 18_894_848  # ~19 MB per expert
@@ -60,7 +61,7 @@ def test_sizes(L, d):
     (dict(hidden=100), moe.MOE_E_UNSUPPORTED), (dict(inter=96), moe.MOE_E_UNSUPPORTED),
     (dict(top_k=0), moe.MOE_E_INVAL), (dict(top_k=9, n_experts=8), moe.MOE_E_INVAL),
     (dict(n_experts=2048), moe.MOE_E_UNSUPPORTED), (dict(top_k=40, n_experts=64), moe.MOE_E_UNSUPPORTED),
-    (dict(wfmt=5), moe.MOE_E_UNSUPPORTED), (dict(has_shared=2), moe.MOE_E_INVAL),
+    (dict(wfmt=4), moe.MOE_E_UNSUPPORTED), (dict(wfmt=-1), moe.MOE_E_UNSUPPORTED), (dict(has_shared=2), moe.MOE_E_INVAL),
     (dict(top_p=-0.1), moe.MOE_E_INVAL), (dict(top_p=1.5), moe.MOE_E_INVAL), (dict(top_p=float("nan")), moe.MOE_E_INVAL)])
 def test_bad_dims_rejected(L, bad, code):
     base = dict(hidden=256, inter=128, n_experts=8, top_k=2, has_shared=1, wfmt=0, top_p=0.0)

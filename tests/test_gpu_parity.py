@@ -33,7 +33,9 @@ def _check_route(out, r, T, k):
 
 # ---- pack / unpack ---------------------------------------------------------
 @pytest.mark.parametrize("dims", [synth.Dims(256, 128, 2, 1, 1, 0), synth.Dims(384, 256, 2, 1, 1, 1),
-                                  synth.Dims(6144, 2048, 1, 1, 1, 0), synth.Dims(2048, 512, 1, 1, 1, 1)])
+                                  synth.Dims(6144, 2048, 1, 1, 1, 0), synth.Dims(2048, 512, 1, 1, 1, 1),
+                                  synth.Dims(256, 128, 2, 1, 1, 2), synth.Dims(384, 256, 2, 1, 1, 3),
+                                  synth.Dims(6144, 2048, 1, 1, 1, 2), synth.Dims(6144, 2048, 1, 1, 1, 3)])
 def test_pack_unpack_round_trip(dims):
     _log("pack", dims)
     layer = synth.make_layer(dims, ("pack", dims.as_tuple()), device=DEV)
@@ -105,6 +107,12 @@ def _small_cases():
         ("e2m1_small", synth.Dims(256, 256, 8, 2, 1, 1), 4),
         ("e2m1_ragged", synth.Dims(384, 384, 33, 3, 0, 1), 7),
         ("dense_e1k1", synth.Dims(128, 128, 1, 1, 0, 0), 3),
+        ("int8_small", synth.Dims(256, 128, 8, 2, 1, 2), 4),
+        ("int8_ragged", synth.Dims(384, 256, 100, 6, 1, 2), 16),
+        ("int2_small", synth.Dims(256, 128, 8, 2, 1, 3), 4),
+        ("int2_ragged", synth.Dims(384, 384, 33, 3, 0, 3), 7),
+        ("int2_dense_e1k1", synth.Dims(128, 128, 1, 1, 0, 3), 3),
+        ("int8_dense_e1k1", synth.Dims(128, 128, 1, 1, 0, 2), 1),
     ]
 
 
@@ -126,7 +134,7 @@ def test_forward_small_matches_oracle(name, dims, T):
     assert_close(y, y_ref, name)
 
 
-@pytest.mark.parametrize("name", ["decode_b1", "decode_b8", "e2m1_b1", "e2m1_b4"])
+@pytest.mark.parametrize("name", ["decode_b1", "decode_b8", "e2m1_b1", "e2m1_b4", "int8_b1", "int2_b1", "int2_b8"])
 def test_forward_full_size_matches_oracle(name):
     """Full-size decode layers (all 256 + 1 experts resident), every output
     element checked against the oracle."""
@@ -219,6 +227,10 @@ PREFILL_CASES = [
     ("noshared_t33", synth.Dims(256, 128, 16, 3, 0, 0), 33),
     ("e2m1_t40", synth.Dims(256, 256, 8, 2, 1, 1), 40),
     ("e2m1_ragged_t129", synth.Dims(384, 384, 33, 3, 1, 1), 129),
+    ("int8_t40", synth.Dims(256, 256, 8, 2, 1, 2), 40),
+    ("int8_ragged_t70", synth.Dims(384, 256, 100, 6, 1, 2), 70),
+    ("int2_t40", synth.Dims(256, 128, 8, 2, 1, 3), 40),
+    ("int2_ragged_t129", synth.Dims(384, 384, 33, 3, 0, 3), 129),
 ]
 
 
@@ -264,11 +276,13 @@ def test_prefill_full_size_sampled():
          f"rel_l2={rel:.2e} max_abs={mx:.2e}")
 
 
-def test_decode_and_prefill_agree():
+@pytest.mark.parametrize("wfmt", [synth.INT4_ROW, synth.INT8_ROW, synth.INT2_ROW])
+def test_decode_and_prefill_agree(wfmt):
     """The same tokens through the prefill path (one batch of T > threshold)
     and the GEMV path (one token per call) give the same layer output."""
-    dims = synth.Dims(1024, 256, 32, 4, 1, 0)
-    layer = synth.make_layer(dims, "agree")
+    _log("agree", wfmt)
+    dims = synth.Dims(1024, 256, 32, 4, 1, wfmt)
+    layer = synth.make_layer(dims, "agree" if wfmt == synth.INT4_ROW else ("agree", wfmt))
     T = moe.moe_decode_max_tokens() + 1
     x = synth.make_tokens(dims, T, "agree").to(DEV)
     pl = moe.PackedLayer.from_layer(layer)
@@ -317,6 +331,7 @@ TOPP_FORWARD_CASES = [
     ("e2m1_topp", synth.Dims(256, 256, 8, 2, 1, 1, top_p=0.51), 4),
     ("prefill_topp_t40", synth.Dims(256, 128, 16, 4, 1, 0, top_p=0.5), 40),
     ("prefill_e2m1_topp_t129", synth.Dims(384, 384, 33, 3, 1, 1, top_p=0.7), 129),
+    ("int2_topp", synth.Dims(256, 128, 8, 2, 1, 3, top_p=0.51), 4),
 ]
 
 
