@@ -40,79 +40,33 @@ __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast
 // Per-format constants of the packed layout (common.h): C columns per
 // 1 KiB chunk, XPC activation vectors (8 binary16 each) per chunk, U chunks
 // per ring batch (128 columns for int2, else 4 chunks; an E2M1 scale group
-// is 4 chunks).
+// is 4 chunks).  NCLS accumulator classes and the code offset OFF of the
+// integer decode below.
 template <int FMT>
 struct Fmt {
   static constexpr int C = 128 / code_bits(FMT);
   static constexpr int XPC = C / 8;
   static constexpr int U = FMT == MOE_W_INT2_ROW ? 2 : 4;
+  static constexpr int NCLS = FMT == MOE_W_INT2_ROW ? 4 : FMT == MOE_W_INT4_ROW ? 2 : 1;
+  static constexpr float OFF = FMT == MOE_W_INT2_ROW ? 2.f : FMT == MOE_W_INT4_ROW ? 8.f : 128.f;
 };
 
-// The masks live in VGPRs so that each mask-and-insert below is a single
-// v_and_or_b32 (a VOP3 instruction takes no literal on gfx9, and only one
-// scalar operand).
-struct Masks {
-  uint32_t m[4];
-};
-
-__device__ __forceinline__ uint32_t vgpr_const(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
-  return r;
-}
-
+// Integer codes are decoded without any arithmetic: masking a dword leaves
+// the offset-binary code u of two adjacent columns in the low mantissa bits
+// of a half2, i.e. the binary16 subnormals u * 2^-24 * 2^b for a field at bit
+// b of the 16-bit half (exact while the field stays below bit 10).  The dot
+// products accumulate these per bit position b (a "class"), each class is
+// scaled back by 2^24 / 2^b (exact), and the offset is removed once per
+// K-segment as OFF * sum(x), which the callers compute alongside:
+// sum (u - OFF) x = sum u x - OFF sum x.
+//   INT4_ROW: fields at bits 0 and 4 of d and of d >> 8 (classes 2^0, 2^4);
+//   INT8_ROW: bytes 0/2 of d and of d >> 8 (one class);
+//   INT2_ROW: fields at bits 0, 2, 4, 6 of d and of d >> 8 (classes 4^j).
 template <int FMT>
-__device__ __forceinline__ Masks make_masks() {
-  Masks k{};
-  if (FMT == MOE_W_INT4_ROW) {
-    k.m[0] = vgpr_const(0x000F000Fu);
-    k.m[1] = vgpr_const(0x00F000F0u);
-  } else if (FMT == MOE_W_INT8_ROW) {
-    k.m[0] = vgpr_const(0x00FF00FFu);
-  } else if (FMT == MOE_W_INT2_ROW) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) k.m[j] = vgpr_const(0x00030003u << (2 * j));
-  }
-  return k;
-}
-
-// int4 (device order, offset binary) -> four half2 pairs of exact integers.
-// (d & 0x000F000F) | 0x6400 gives 1024 + u; (d & 0x00F000F0) | 0x5400 gives
-// 64 + u; subtracting 1032 / 72 leaves q = u - 8 exactly.
-__device__ __forceinline__ void dec_int4(uint32_t d, const Masks& mk, half2_t& p0, half2_t& p1, half2_t& p2,
-                                         half2_t& p3) {
-  const half2_t k1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const half2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const uint32_t d8 = d >> 8;
-  p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1032;
-  p1 = as_h2((d & mk.m[1]) | 0x54005400u) + k72;
-  p2 = as_h2((d8 & mk.m[0]) | 0x64006400u) + k1032;
-  p3 = as_h2((d8 & mk.m[1]) | 0x54005400u) + k72;
-}
-
-// int8 (bytes 0, 2 = columns 0, 1; bytes 1, 3 = columns 2, 3; offset
-// binary) -> two half2 pairs: (d & 0x00FF00FF) | 0x6400 gives 1024 + u, and
-// 1024 + u - 1152 = q exactly (|q| <= 128).
-__device__ __forceinline__ void dec_int8(uint32_t d, const Masks& mk, half2_t& p0, half2_t& p1) {
-  const half2_t k1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1152;
-  p1 = as_h2(((d >> 8) & mk.m[0]) | 0x64006400u) + k1152;
-}
-
-// int2 (columns 2j / 2j+1 in bits 2j / 16+2j; offset binary) -> eight half2
-// pairs.  The field at bit 2j (j < 4) is placed in the mantissa of a binary16
-// whose unit in the last place is 2^-2j, i.e. 1024, 256, 64, 16 + u; pairs
-// 4..7 take the same fields of d >> 8.  Subtracting base + 2 leaves q.
-__device__ __forceinline__ void dec_int2(uint32_t d, const Masks& mk, half2_t (&p)[8]) {
-  const uint32_t magic[4] = {0x64006400u, 0x5C005C00u, 0x54005400u, 0x4C004C00u};
-  const float off[4] = {-1026.0f, -258.0f, -66.0f, -18.0f};
-  const uint32_t d8 = d >> 8;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const half2_t k = {(_Float16)off[j], (_Float16)off[j]};
-    p[j] = as_h2((d & mk.m[j]) | magic[j]) + k;
-    p[4 + j] = as_h2((d8 & mk.m[j]) | magic[j]) + k;
-  }
+__device__ __forceinline__ constexpr float class_scale(int j) {
+  return FMT == MOE_W_INT2_ROW ? 16777216.0f / (float)(1 << (2 * j))
+         : FMT == MOE_W_INT4_ROW ? 16777216.0f / (float)(1 << (4 * j))
+         : FMT == MOE_W_INT8_ROW ? 16777216.0f : 1.0f;
 }
 
 // e2m1 codes (byte b = columns 2b, 2b+1) -> four half2 pairs, multiplied by
@@ -160,39 +114,68 @@ __device__ __forceinline__ void load_batch(const guint4* __restrict__ w, const g
   }
 }
 
-// Dword i of a chunk of matrix m against the chunk's activations xv.
-template <int FMT, int NM, int NT, int XPC>
+__device__ __forceinline__ float fdot2(uint32_t w, uint32_t x, float acc) {
+  return __builtin_amdgcn_fdot2(as_h2(w), as_h2(x), acc, false);
+}
+
+// acc + the sum of the eight binary16 values in v.
+__device__ __forceinline__ float sum8(u32x4 v, float acc) {
+  constexpr uint32_t kOnes = 0x3C003C00u;  // (1.0, 1.0)
+  acc = fdot2(v.x, kOnes, acc);
+  acc = fdot2(v.y, kOnes, acc);
+  acc = fdot2(v.z, kOnes, acc);
+  return fdot2(v.w, kOnes, acc);
+}
+
+// Dword i of a chunk of matrix m against the chunk's activations xv, into
+// the class accumulators cl[m][t][class].
+template <int FMT, int NM, int NT, int XPC, int NCLS>
 __device__ __forceinline__ void dot_dword(uint32_t d, int i, int m, half2_t s, const u32x4 (&xv)[NT][XPC],
-                                          const Masks& mk, float (&acc)[NM][NT]) {
+                                          float (&cl)[NM][NT][NCLS]) {
+  const uint32_t d8 = d >> 8;
   if (FMT == MOE_W_INT8_ROW) {  // columns 4i .. 4i+3
-    half2_t p0, p1;
-    dec_int8(d, mk, p0, p1);
+    const uint32_t e0 = d & 0x00FF00FFu, e1 = d8 & 0x00FF00FFu;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const u32x4 v = xv[t][i / 2];
-      acc[m][t] = __builtin_amdgcn_fdot2(p0, as_h2((i & 1) ? v.z : v.x), acc[m][t], false);
-      acc[m][t] = __builtin_amdgcn_fdot2(p1, as_h2((i & 1) ? v.w : v.y), acc[m][t], false);
+      cl[m][t][0] = fdot2(e0, (i & 1) ? v.z : v.x, cl[m][t][0]);
+      cl[m][t][0] = fdot2(e1, (i & 1) ? v.w : v.y, cl[m][t][0]);
     }
-  } else if (FMT == MOE_W_INT2_ROW) {  // columns 16i .. 16i+15
-    half2_t p[8];
-    dec_int2(d, mk, p);
+  } else if (FMT == MOE_W_INT2_ROW) {  // columns 16i .. 16i+15: pair j of d, pair 4+j of d >> 8
+    uint32_t e[8];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      e[j] = d & (0x00030003u << (2 * j));
+      e[4 + j] = d8 & (0x00030003u << (2 * j));
+    }
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      acc[m][t] = dot8(p[0], p[1], p[2], p[3], xv[t][2 * i], acc[m][t]);
-      acc[m][t] = dot8(p[4], p[5], p[6], p[7], xv[t][2 * i + 1], acc[m][t]);
-    }
-  } else {  // columns 8i .. 8i+7
-    half2_t p0, p1, p2, p3;
-    if (FMT == MOE_W_INT4_ROW) dec_int4(d, mk, p0, p1, p2, p3);
-    else dec_e2m1(d, s, p0, p1, p2, p3);
+      const u32x4 a = xv[t][2 * i], b = xv[t][2 * i + 1];
+      const uint32_t xa[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[m][t] = dot8(p0, p1, p2, p3, xv[t][i], acc[m][t]);
+      for (int j = 0; j < 8; ++j) cl[m][t][j & 3] = fdot2(e[j], xa[j], cl[m][t][j & 3]);
+    }
+  } else if (FMT == MOE_W_INT4_ROW) {  // columns 8i .. 8i+7
+    const uint32_t e0 = d & 0x000F000Fu, e1 = d & 0x00F000F0u, e2 = d8 & 0x000F000Fu, e3 = d8 & 0x00F000F0u;
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      const u32x4 v = xv[t][i];
+      cl[m][t][0] = fdot2(e0, v.x, cl[m][t][0]);
+      cl[m][t][1] = fdot2(e1, v.y, cl[m][t][1]);
+      cl[m][t][0] = fdot2(e2, v.z, cl[m][t][0]);
+      cl[m][t][1] = fdot2(e3, v.w, cl[m][t][1]);
+    }
+  } else {  // E2M1: columns 8i .. 8i+7, block scale s
+    half2_t p0, p1, p2, p3;
+    dec_e2m1(d, s, p0, p1, p2, p3);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) cl[m][t][0] = dot8(p0, p1, p2, p3, xv[t][i], cl[m][t][0]);
   }
 }
 
 template <int FMT, int NM, int NT, int U, typename AP>
 __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u32x2 (&sv)[NM], int c,
-                                              const AP* act, const Masks& mk, float (&acc)[NM][NT]) {
+                                              const AP* act, float (&cl)[NM][NT][Fmt<FMT>::NCLS]) {
   constexpr int XPC = Fmt<FMT>::XPC;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -214,16 +197,18 @@ __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u3
         s1 = e4m3_pair(sb, (u & 1) * 2 + 1);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) dot_dword<FMT, NM, NT, XPC>(dw[i], i, m, i < 2 ? s0 : s1, xv, mk, acc);
+      for (int i = 0; i < 4; ++i) dot_dword<FMT, NM, NT, XPC>(dw[i], i, m, i < 2 ? s0 : s1, xv, cl);
     }
   }
 }
 
 // Streams `nch` chunks (a multiple of U) for NM matrices (gate+up: NM=2) and
-// NT activation rows into acc through a ring of D batches of U chunks: the
-// first D batches are requested at once, then `pre()` runs (a caller's own
-// loads, overlapping the weights in flight), and every batch is reloaded with
-// the batch D ahead right after it has been decoded and multiplied.
+// NT activation rows and adds sum_c u[c] * x[c] to acc (integer formats: u
+// is the code before its offset is removed), through a ring of D batches of
+// U chunks: the first D batches are requested at once, then `pre()` runs (a
+// caller's own loads, overlapping the weights in flight), and every batch is
+// reloaded with the batch D ahead right after it has been decoded and
+// multiplied.
 //   w: this lane's 16 bytes in the first chunk of matrix 0; matrix m of
 //      chunk c is at w + (c*NM + m)*64 (uint4 units).
 //   sc: E2M1 only: this lane's 8 scale bytes of the first 4-chunk group of
@@ -235,10 +220,16 @@ __device__ __forceinline__ void compute_batch(const u32x4 (&wv)[U][NM], const u3
 template <int FMT, int NM, int NT, int D, typename AP, typename Pre>
 __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const guint2* __restrict__ sc,
                                             const AP* act, int nch, float (&acc)[NM][NT], Pre&& pre) {
-  const Masks mk = make_masks<FMT>();
-  constexpr int U = Fmt<FMT>::U;
+  constexpr int U = Fmt<FMT>::U, NCLS = Fmt<FMT>::NCLS;
   u32x4 wv[D][U][NM];
   u32x2 sv[D][NM];
+  float cl[NM][NT][NCLS];
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < NCLS; ++j) cl[m][t][j] = 0.f;
   const int nb = nch / U;
 #pragma unroll
   for (int d = 0; d < D; ++d)
@@ -249,11 +240,17 @@ __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const 
     for (int d = 0; d < D; ++d) {
       const int b = b0 + d;
       if (b < nb) {
-        compute_batch<FMT, NM, NT, U>(wv[d], sv[d], b * U, act, mk, acc);
+        compute_batch<FMT, NM, NT, U>(wv[d], sv[d], b * U, act, cl);
         if (b + D < nb) load_batch<FMT, NM, U>(w, sc, (b + D) * U, wv[d], sv[d]);
       }
     }
   }
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int j = 0; j < NCLS; ++j) acc[m][t] += cl[m][t][j] * class_scale<FMT>(j);
 }
 
 // ===========================================================================
@@ -283,6 +280,7 @@ constexpr int kWpg = 4;           // wavefronts per workgroup
 constexpr int kStageCols = 1024;  // h columns staged in LDS per step
 constexpr int kStageVec = kStageCols / 8;  // ... as 16-byte vectors per token
 constexpr int kRingChunks = 8;    // chunks in flight per matrix (gate/up: 16 KiB, down: 8 KiB)
+constexpr int kSumPieces = 4;     // 16-byte activation pieces per lane held for the offset sum
 constexpr int kSyRouter = 64;     // router arrival counters (uint32 index in the sync region):
 constexpr int kRouterGroups = 8;  //   top counter, then one per group of router workgroups
 
@@ -568,15 +566,50 @@ __device__ __forceinline__ void gu_stream(const DecArgs& a, const uint16_t* __re
   if (FMT == MOE_W_E2M1_B16)
     sc = (const guint2*)(si.base + a.L.sgu_off) + ((size_t)rb * (a.H / 128) + c0 / 4) * 2 * 64 + lane;
   const cu32x4* act[NT];  // x is read-only during the launch
+  const u32x4* xg[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     int tok, row;
     slot_token(a, si, i0 + t, tok, row);
-    act[t] = (const cu32x4*)(x + (size_t)tok * a.H + C * c0);
+    xg[t] = reinterpret_cast<const u32x4*>(x + (size_t)tok * a.H + C * c0);
+    act[t] = (const cu32x4*)xg[t];
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[0][t] = acc[1][t] = 0.f;
-  stream_ring<FMT, 2, NT, kRingChunks / Fmt<FMT>::U>(w, sc, act, nch, acc, [] {});
+  if (!row_scaled(FMT)) {
+    stream_ring<FMT, 2, NT, kRingChunks / Fmt<FMT>::U>(w, sc, act, nch, acc, [] {});
+    return;
+  }
+  // sum of the segment's activations for the code offset: the lanes load
+  // its 16-byte pieces (before the weights, so that waiting for them does
+  // not wait for the weights) and add them up while the weights stream in
+  const int npc = nch * Fmt<FMT>::XPC;
+  u32x4 xp[NT][kSumPieces];
+  float xs[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    xs[t] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSumPieces; ++i) {
+      const int q = lane + 64 * i;
+      xp[t][i] = q < npc ? xg[t][q] : u32x4{0, 0, 0, 0};
+    }
+  }
+  stream_ring<FMT, 2, NT, kRingChunks / Fmt<FMT>::U>(w, sc, act, nch, acc, [&] {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+#pragma unroll
+      for (int i = 0; i < kSumPieces; ++i) xs[t] = sum8(xp[t][i], xs[t]);
+      for (int q = lane + 64 * kSumPieces; q < npc; q += 64)
+        xs[t] = sum8(xg[t][q], xs[t]);
+    }
+  });
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const float off = Fmt<FMT>::OFF * wave_sum_f32(xs[t]);
+    acc[0][t] -= off;
+    acc[1][t] -= off;
+  }
 }
 
 // h for token row `row` of this block from its gate/up sums (wavefront 0).
@@ -703,9 +736,9 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
     const lu32x4* act[NT];  // LDS
 #pragma unroll
     for (int t = 0; t < NT; ++t) act[t] = (const lu32x4*)(hl + t * kStageVec);
-    float acc[1][NT];
+    float acc[1][NT], hs[NT];  // hs: this lane's share of the h sum (code offset)
 #pragma unroll
-    for (int t = 0; t < NT; ++t) acc[0][t] = 0.f;
+    for (int t = 0; t < NT; ++t) acc[0][t] = hs[t] = 0.f;
     for (int p0 = 0; p0 < a.cpu_dn; p0 += kStage) {
       const int np = min(kStage, a.cpu_dn - p0);
       wave_lds_sync();  // the previous step's LDS reads are done
@@ -716,10 +749,18 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
               int tok, row;
               slot_token(a, si, i0 + t, tok, row);
               const u32x4* src = reinterpret_cast<const u32x4*>(a.h + (size_t)row * a.I + C * c0);
-              for (int q = lane; q < np * XPC; q += 64) hl[t * kStageVec + q] = src[p0 * XPC + q];
+              for (int q = lane; q < np * XPC; q += 64) {
+                const u32x4 v = src[p0 * XPC + q];
+                hl[t * kStageVec + q] = v;
+                if (row_scaled(FMT)) hs[t] = sum8(v, hs[t]);
+              }
             }
             wave_lds_sync();
           });
+    }
+    if (row_scaled(FMT)) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[0][t] -= Fmt<FMT>::OFF * wave_sum_f32(hs[t]);
     }
 #pragma unroll
     for (int t = 0; t < NT; ++t) ls.r[wave][t][lane] = acc[0][t];
