@@ -133,7 +133,7 @@ template <int FMT, int NM, int NT, int XPC, int NCLS>
 __device__ __forceinline__ void dot_dword(uint32_t d, int i, int m, half2_t s, const u32x4 (&xv)[NT][XPC],
                                           float (&cl)[NM][NT][NCLS]) {
   const uint32_t d8 = d >> 8;
-  if (FMT == MOE_W_INT8_ROW) {  // columns 4i .. 4i+3
+  if constexpr (FMT == MOE_W_INT8_ROW) {  // columns 4i .. 4i+3
     const uint32_t e0 = d & 0x00FF00FFu, e1 = d8 & 0x00FF00FFu;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -141,7 +141,7 @@ __device__ __forceinline__ void dot_dword(uint32_t d, int i, int m, half2_t s, c
       cl[m][t][0] = fdot2(e0, (i & 1) ? v.z : v.x, cl[m][t][0]);
       cl[m][t][0] = fdot2(e1, (i & 1) ? v.w : v.y, cl[m][t][0]);
     }
-  } else if (FMT == MOE_W_INT2_ROW) {  // columns 16i .. 16i+15: pair j of d, pair 4+j of d >> 8
+  } else if constexpr (FMT == MOE_W_INT2_ROW) {  // columns 16i .. 16i+15: pair j of d, pair 4+j of d >> 8
     uint32_t e[8];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -155,7 +155,7 @@ __device__ __forceinline__ void dot_dword(uint32_t d, int i, int m, half2_t s, c
 #pragma unroll
       for (int j = 0; j < 8; ++j) cl[m][t][j & 3] = fdot2(e[j], xa[j], cl[m][t][j & 3]);
     }
-  } else if (FMT == MOE_W_INT4_ROW) {  // columns 8i .. 8i+7
+  } else if constexpr (FMT == MOE_W_INT4_ROW) {  // columns 8i .. 8i+7
     const uint32_t e0 = d & 0x000F000Fu, e1 = d & 0x00F000F0u, e2 = d8 & 0x000F000Fu, e3 = d8 & 0x00F000F0u;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -323,6 +323,15 @@ struct SlotInfo {
   int p0;  // first entry in pairs (routed) or -1 (shared)
 };
 
+// Tables that an earlier launch wrote (slot table, pairs) are read with
+// scalar loads through constant-address-space pointers: they wait on the
+// scalar memory counter, so a lookup issued after the weight loads does not
+// wait for those (vector loads complete in order).
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 // Slot s of the call: the shared expert needs no routing; routed slots come
 // from the table the route phase wrote.  Returns false for unused slots.
 __device__ __forceinline__ bool get_slot(const DecArgs& a, int s, SlotInfo& si) {
@@ -332,10 +341,11 @@ __device__ __forceinline__ bool get_slot(const DecArgs& a, int s, SlotInfo& si) 
     si.p0 = -1;
     return true;
   }
-  const SlotEntry e = a.slots[s];
-  si.base = e.base;
-  si.n = __builtin_amdgcn_readfirstlane(e.n);
-  si.p0 = __builtin_amdgcn_readfirstlane(e.p0);
+  static_assert(sizeof(SlotEntry) == 16, "slot entry is one 16-byte scalar load");
+  const u32x4 e = ld_const(reinterpret_cast<const u32x4*>(a.slots), s);
+  si.base = reinterpret_cast<const uint8_t*>((uint64_t)e.x | ((uint64_t)e.y << 32));
+  si.n = (int)e.z;
+  si.p0 = (int)e.w;
   return si.n > 0;
 }
 
@@ -346,7 +356,7 @@ __device__ __forceinline__ void slot_token(const DecArgs& a, const SlotInfo& si,
     t = i;
     row = a.T * a.k + i;
   } else {
-    const int p = __builtin_amdgcn_readfirstlane(a.pairs[si.p0 + i]);
+    const int p = ld_const(a.pairs, si.p0 + i);
     t = p / a.k;
     row = p;
   }
@@ -565,48 +575,40 @@ __device__ __forceinline__ void gu_stream(const DecArgs& a, const uint16_t* __re
   const guint2* sc = nullptr;
   if (FMT == MOE_W_E2M1_B16)
     sc = (const guint2*)(si.base + a.L.sgu_off) + ((size_t)rb * (a.H / 128) + c0 / 4) * 2 * 64 + lane;
-  const cu32x4* act[NT];  // x is read-only during the launch
-  const u32x4* xg[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    int tok, row;
-    slot_token(a, si, i0 + t, tok, row);
-    xg[t] = reinterpret_cast<const u32x4*>(x + (size_t)tok * a.H + C * c0);
-    act[t] = (const cu32x4*)xg[t];
-  }
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[0][t] = acc[1][t] = 0.f;
-  if (!row_scaled(FMT)) {
-    stream_ring<FMT, 2, NT, kRingChunks / Fmt<FMT>::U>(w, sc, act, nch, acc, [] {});
-    return;
-  }
-  // sum of the segment's activations for the code offset: the lanes load
-  // its 16-byte pieces (before the weights, so that waiting for them does
-  // not wait for the weights) and add them up while the weights stream in
+  // The weights are requested first; the tokens' rows are looked up while
+  // they are in flight.  Integer formats also need the sum of the segment's
+  // activations (code offset): the lanes request its 16-byte pieces after
+  // the first weights and add them up after the stream.
+  const cu32x4* act[NT];  // x is read-only during the launch
+  const u32x4* xg[NT];
   const int npc = nch * Fmt<FMT>::XPC;
   u32x4 xp[NT][kSumPieces];
-  float xs[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    xs[t] = 0.f;
-#pragma unroll
-    for (int i = 0; i < kSumPieces; ++i) {
-      const int q = lane + 64 * i;
-      xp[t][i] = q < npc ? xg[t][q] : u32x4{0, 0, 0, 0};
-    }
-  }
   stream_ring<FMT, 2, NT, kRingChunks / Fmt<FMT>::U>(w, sc, act, nch, acc, [&] {
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
+      int tok, row;
+      slot_token(a, si, i0 + t, tok, row);
+      xg[t] = reinterpret_cast<const u32x4*>(x + (size_t)tok * a.H + C * c0);
+      act[t] = (const cu32x4*)xg[t];
+      if (row_scaled(FMT)) {
 #pragma unroll
-      for (int i = 0; i < kSumPieces; ++i) xs[t] = sum8(xp[t][i], xs[t]);
-      for (int q = lane + 64 * kSumPieces; q < npc; q += 64)
-        xs[t] = sum8(xg[t][q], xs[t]);
+        for (int i = 0; i < kSumPieces; ++i) {
+          const int q = lane + 64 * i;
+          xp[t][i] = xg[t][q < npc ? q : 0];
+        }
+      }
     }
   });
+  if (!row_scaled(FMT)) return;
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const float off = Fmt<FMT>::OFF * wave_sum_f32(xs[t]);
+    float xs = 0.f;
+#pragma unroll
+    for (int i = 0; i < kSumPieces; ++i) xs = (lane + 64 * i < npc) ? sum8(xp[t][i], xs) : xs;
+    for (int q = lane + 64 * kSumPieces; q < npc; q += 64) xs = sum8(xg[t][q], xs);
+    const float off = Fmt<FMT>::OFF * wave_sum_f32(xs);
     acc[0][t] -= off;
     acc[1][t] -= off;
   }
