@@ -614,20 +614,38 @@ __device__ __forceinline__ void gu_stream(const DecArgs& a, const uint16_t* __re
   }
 }
 
+// Gate and up scales of this lane's row of block rb, as stored (binary16
+// row scales, or the E2M1 fp32 tensor scales).  Requested before the
+// weights and converted only where they are used, so that nothing waits
+// for them before the weight stream starts.
+struct GuScales {
+  uint32_t g, u;
+};
+
+template <int FMT>
+__device__ __forceinline__ GuScales gu_scales(const DecArgs& a, const SlotInfo& si, int rb) {
+  typedef __attribute__((address_space(1))) const uint16_t gu16;
+  typedef __attribute__((address_space(1))) const uint32_t gu32;
+  const int r = 64 * rb + (threadIdx.x & 63);
+  if (row_scaled(FMT))
+    return GuScales{(uint32_t)((gu16*)(si.base + a.L.sg_off))[r], (uint32_t)((gu16*)(si.base + a.L.su_off))[r]};
+  gu32* g3 = (gu32*)(si.base + a.L.g3_off);
+  return GuScales{g3[0], g3[1]};
+}
+
+template <int FMT>
+__device__ __forceinline__ float scale_value(uint32_t bits) {
+  return row_scaled(FMT) ? (float)__builtin_bit_cast(_Float16, (uint16_t)bits) : __builtin_bit_cast(float, bits);
+}
+
 // h for token row `row` of this block from its gate/up sums (wavefront 0).
 template <int FMT>
-__device__ __forceinline__ void gu_finish(const DecArgs& a, const SlotInfo& si, int rb, int row, float g, float u) {
+__device__ __forceinline__ void gu_finish(const DecArgs& a, GuScales gs, int rb, int row, float g, float u) {
   const int r = 64 * rb + (threadIdx.x & 63);
-  float sg, su;
-  if (row_scaled(FMT)) {
-    sg = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.sg_off)[r]);
-    su = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(si.base + a.L.su_off)[r]);
-  } else {
-    const float* g3 = reinterpret_cast<const float*>(si.base + a.L.g3_off);
-    sg = g3[0];
-    su = g3[1];
-  }
-  const float hv = silu(g * sg) * (u * su);
+  // opaque from here on: keeps the conversion (and the wait for the load)
+  // from being hoisted in front of the weight stream
+  asm volatile("" : "+v"(gs.g), "+v"(gs.u));
+  const float hv = silu(g * scale_value<FMT>(gs.g)) * (u * scale_value<FMT>(gs.u));
   a.h[(size_t)row * a.I + r] = __builtin_bit_cast(uint16_t, (_Float16)hv);  // read by the next launch
 }
 
@@ -638,7 +656,7 @@ __device__ __forceinline__ void gu_finish(const DecArgs& a, const SlotInfo& si, 
 template <int FMT, int NT, int KT>
 __device__ __forceinline__ void gu_tile_group(const DecArgs& a, const uint16_t* __restrict__ x, const SlotInfo& si,
                                               int s, int rb, int grp, int ngrp, int nw, int nch, int i0,
-                                              GuLds<KT>& ls) {
+                                              GuScales gs, GuLds<KT>& ls) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (wave < nw) {
     float acc[2][NT];
@@ -661,7 +679,7 @@ __device__ __forceinline__ void gu_tile_group(const DecArgs& a, const uint16_t* 
       int tok, row;
       slot_token(a, si, i0 + t, tok, row);
       if (ngrp == 1) {
-        gu_finish<FMT>(a, si, rb, row, g, u);
+        gu_finish<FMT>(a, gs, rb, row, g, u);
       } else {
         float* pr = a.p_gu + (((size_t)grp * a.rows_total + row) * 2) * a.I + 64 * rb + lane;
         st_dev(pr, g);
@@ -677,9 +695,10 @@ __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __res
                                          int ngrp, int nw, int nch, GuLds<KT>& ls) {
   SlotInfo si;
   if (!get_slot(a, s, si)) return;  // uniform over the workgroup
+  const GuScales gs = gu_scales<FMT>(a, si, rb);
   for (int i0 = 0; i0 < si.n; i0 += KT) {
-    if (KT == 1 || si.n - i0 == 1) gu_tile_group<FMT, 1, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, ls);
-    else gu_tile_group<FMT, KT, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, ls);
+    if (KT == 1 || si.n - i0 == 1) gu_tile_group<FMT, 1, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, gs, ls);
+    else gu_tile_group<FMT, KT, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, gs, ls);
   }
   if (ngrp == 1 || threadIdx.x >= 64) return;
   if (!arrive_last(a.gu_cnt + rb, (uint32_t)ngrp)) return;
@@ -705,7 +724,7 @@ __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __res
           u += pu[q];
         }
     }
-    gu_finish<FMT>(a, si, rb, row, g, u);
+    gu_finish<FMT>(a, gs, rb, row, g, u);
   }
 }
 
