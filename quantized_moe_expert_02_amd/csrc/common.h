@@ -199,7 +199,7 @@ __device__ __forceinline__ uint32_t publish_arrival(uint32_t* counter) {
   uint32_t prev = 0;
   if ((threadIdx.x & 63) == 0)
     prev = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  prev = __shfl(prev, 0, 64);
+  prev = __builtin_amdgcn_readfirstlane(prev);  // lane 0's value (all lanes are active)
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   return prev;
 }

@@ -415,11 +415,7 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const
     pres += c > 0;
   }
   // inclusive scan of (present << 16 | count) across the wavefront
-  int v = (pres << 16) | cnt;
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(v, off, 64);
-    if (lane >= off) v += o;
-  }
+  int v = wave_inclusive_scan((pres << 16) | cnt);
   const int excl = v - ((pres << 16) | cnt);
   int up = excl >> 16, uc = excl & 0xFFFF;
 #pragma unroll

@@ -74,11 +74,28 @@ __device__ __forceinline__ int top_p_keep(float s, float tot, int k, float p) {
   return k;
 }
 
-// Every lane ends with the wave-wide fp32 sum, butterfly order (the same on
-// every lane).
+// Every lane ends with the wave-wide fp32 sum, added as a pairwise tree
+// (lanes 2i and 2i+1 first, then pairs of pairs, ...), the same on every lane.
 __device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int m = 1; m < kWave; m <<= 1) v += __shfl_xor(v, m, kWave);
+  v += __builtin_bit_cast(float, partner<1>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, partner<2>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, partner<4>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, partner<8>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, partner<16>(__builtin_bit_cast(int, v)));
+  v += __builtin_bit_cast(float, partner<32>(__builtin_bit_cast(int, v)));
+  return v;
+}
+
+// Inclusive prefix sum over the lanes (lane l gets v_0 + ... + v_l): row
+// shifts within each row of 16 lanes, then the row broadcasts of lanes 15
+// and 31 into the rows above.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, true);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
   return v;
 }
 
@@ -227,19 +244,28 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < kPer; ++i) v[t][i] = 0.0;
-  for (int s = 0; s < nz; ++s) {
-    double zs[NT][kPer];
+  // all planes are requested at once (one memory latency), then added in
+  // plane order
+  constexpr int PG = kPer * NT * kMaxLogitParts <= 40 ? kMaxLogitParts : 1;
+  for (int s0 = 0; s0 < nz; s0 += PG) {
+    double zs[PG][NT][kPer];
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+    for (int s = 0; s < PG; ++s)
 #pragma unroll
-      for (int i = 0; i < kPer; ++i) {
-        const int e = lane + i * kWave;
-        zs[t][i] = (e < E) ? z[s * zstride + (size_t)t * E + e] : 0.0;
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < kPer; ++i) {
+          const int e = lane + i * kWave;
+          zs[s][t][i] = (e < E && s0 + s < nz) ? z[(s0 + s) * zstride + (size_t)t * E + e] : 0.0;
+        }
+#pragma unroll
+    for (int s = 0; s < PG; ++s)
+      if (s0 + s < nz) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int i = 0; i < kPer; ++i) v[t][i] += zs[s][t][i];
       }
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int i = 0; i < kPer; ++i) v[t][i] += zs[t][i];
   }
   uint64_t key[NT][kPer];
   int idx[NT][kPer];
