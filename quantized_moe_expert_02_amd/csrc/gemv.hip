@@ -393,12 +393,12 @@ struct UnionLds {
   uint32_t mask[kMaxExperts];  // tokens per expert (bit t)
   int base[kMaxExperts];       // first pair of each expert
   int pe[kDecodeMaxTokens * kMaxTopK];
+  const uint8_t* ep[kMaxExperts];  // packed expert pointers, staged by the caller
 };
 
-// Lane l owns experts [l*per, l*per + per); ep[i] is the packed pointer of
-// its i-th expert, loaded ahead by the caller.
+// Lane l owns experts [l*per, l*per + per).
 constexpr int kMaxPer = kMaxExperts / 64;
-__device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const uint8_t* const (&ep)[kMaxPer]) {
+__device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
   const int lane = threadIdx.x & 63;
   const int P = a.T * a.k;
   const int per = (a.E + 63) / 64;
@@ -428,7 +428,7 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls, const
         a.uniq_ids[up] = e;
         a.uniq_off[up] = uc;
         SlotEntry se;
-        se.base = ep[i];
+        se.base = ls.ep[e];
         se.n = c;
         se.p0 = uc;
         a.slots[a.S + up] = se;
@@ -535,22 +535,17 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
   __syncthreads();
   if (!s_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-  // the expert pointers the union needs are requested first, so that they
-  // arrive while the logits are loaded and ranked
-  const uint8_t* ep[kMaxPer];
-  {
-    const int per = (a.E + 63) / 64, e0 = lane * per;
-#pragma unroll
-    for (int i = 0; i < kMaxPer; ++i)
-      ep[i] = (wave == 0 && i < per && e0 + i < a.E) ? (const uint8_t*)a.experts[e0 + i] : nullptr;
-  }
+  // The last wavefront stages the expert pointers the union needs in LDS
+  // (wavefront 0, which ranks the first token, does not wait for them).
+  if (wave == kWpg - 1)
+    for (int e = lane; e < a.E; e += 64) ls.ep[e] = (const uint8_t*)a.experts[e];
   const int tpw = (a.T + kWpg - 1) / kWpg;
   const int t0 = wave * tpw, t1 = min(a.T, t0 + tpw);
   for (int t = t0; t < t1; ++t)
     topk_tokens(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k, a.top_p, 1,
                 a.topk_idx + t * a.k, a.topk_w + t * a.k, ls.pe + t * a.k);
   __syncthreads();
-  if (wave == 0) union_step(a, ls, ep);
+  if (wave == 0) union_step(a, ls);
 }
 
 // ---- gate/up: one (slot, 64-row block) per workgroup --------------------------
