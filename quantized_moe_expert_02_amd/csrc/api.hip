@@ -30,6 +30,20 @@ int shared_split(int K) {
   return split_factor(K, 4);
 }
 
+// Split of the routed experts' gate/up: four K-segments per workgroup, and
+// more groups of four (partials handed to the last group) while the launch
+// would hold fewer than kGuTargetWaves wavefronts for `slots` experts.
+constexpr int kGuTargetWaves = 1024;
+int routed_split(int K, int I, int slots) {
+  const int g = K / 128;
+  int best = split_factor(K, 4);
+  for (int f = 8; f <= 16; f += 4) {
+    if ((long)slots * (I / 64) * best >= kGuTargetWaves) break;
+    if (g % f == 0) best = f;
+  }
+  return best;
+}
+
 int check_dims(const moe_dims_t* d) {
   if (!d) return MOE_E_INVAL;
   if (d->n_experts < 1 || d->top_k < 1 || d->top_k > d->n_experts || d->hidden <= 0 || d->inter <= 0)
@@ -59,7 +73,7 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.slots_max = q.S + (int)std::min<int64_t>(q.E, (int64_t)T * q.k);
   q.rows_total = T * q.k + T;
   // decode K-splits: one wavefront per K-segment, four per workgroup
-  q.ks_gu = split_factor(q.H, 4);  // routed experts
+  q.ks_gu = routed_split(q.H, q.I, (int)std::min<int64_t>(q.E, (int64_t)T * q.k));  // routed experts
   q.ks_sgu = shared_split(q.H);    // shared expert, streamed while routing
   q.ks_dn = split_factor(q.I, 2);  // 2 K-segments x 2 row blocks per workgroup
   // Counters: the first 256 words for route-stage counters, then one per
@@ -90,8 +104,8 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.slots_off = off; off = up256(off + (size_t)q.slots_max * sizeof(SlotEntry));
   q.h_off = off; off = up256(off + (size_t)q.rows_total * q.I * 2);
   if (q.decode) {
-    const int sgu_groups = q.ks_sgu > 4 ? q.ks_sgu / 4 : 1;
-    q.p_gu_off = off; off = up256(off + (size_t)sgu_groups * q.rows_total * 2 * q.I * 4);
+    const int groups = std::max(q.ks_sgu > 4 ? q.ks_sgu / 4 : 1, q.ks_gu > 4 ? q.ks_gu / 4 : 1);
+    q.p_gu_off = off; off = up256(off + (size_t)groups * q.rows_total * 2 * q.I * 4);
     q.p_dn_off = off; off = up256(off + (size_t)q.rows_total * q.H * 4);
   } else {
     q.p_gu_off = 0;

@@ -304,10 +304,10 @@ struct DecArgs {
   int32_t* pairs;
   SlotEntry* slots;
   uint16_t* h;
-  float* p_gu;        // shared expert: one partial plane per group of K-segments
+  float* p_gu;        // one partial plane per group of K-segments (shared and routed rows)
   float* p_dn;        // [rows_total][H] scaled slot partials
   uint32_t* sync;
-  uint32_t* gu_cnt;   // [I/64] shared-expert groups
+  uint32_t* gu_cnt;   // [slot][I/64] arrivals of K-segment groups
   uint32_t* dn_cnt;   // [H/64]
   int ks_gu, ks_sgu, ks_dn;     // K-segments: routed gate/up, shared gate/up, down
   int cpu_gu, cpu_sgu, cpu_dn;  // chunks per K-segment
@@ -692,7 +692,7 @@ __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __res
     else gu_tile_group<FMT, KT, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, gs, ls);
   }
   if (ngrp == 1 || threadIdx.x >= 64) return;
-  if (!arrive_last(a.gu_cnt + rb, (uint32_t)ngrp)) return;
+  if (!arrive_last(a.gu_cnt + (size_t)s * (a.I / 64) + rb, (uint32_t)ngrp)) return;
   const int lane = threadIdx.x & 63;
   for (int i = 0; i < si.n; ++i) {
     int tok, row;
@@ -856,8 +856,10 @@ __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint
 template <int FMT, int KT>
 __global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_t* __restrict__ x) {
   __shared__ GuLds<KT> gl;
-  const int per_slot = a.I / 64;
-  gu_group<FMT, KT>(a, x, a.S + blockIdx.x / per_slot, blockIdx.x % per_slot, 0, 1, a.ks_gu, a.cpu_gu, gl);
+  // workgroup = (slot, row block, group of kWpg K-segments)
+  const int nw = min(kWpg, a.ks_gu), ngrp = a.ks_gu / nw, per_slot = (a.I / 64) * ngrp;
+  const int r = blockIdx.x % per_slot;
+  gu_group<FMT, KT>(a, x, a.S + blockIdx.x / per_slot, r / ngrp, r % ngrp, ngrp, nw, a.cpu_gu, gl);
 }
 
 template <int FMT, int KT>
@@ -873,7 +875,8 @@ hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, con
   const int sgu_wg = a.S * (a.I / 64) * (a.ks_sgu / nw);
   const dim3 blk(64 * kWpg);
   launch_k(k_route_phase<FMT, KT>, dim3(a.n_router_wg + sgu_wg), blk, s, se.start(0), se.stop(0), a, x);
-  launch_k(k_gu_phase<FMT, KT>, dim3((a.slots_max - a.S) * (a.I / 64)), blk, s, se.start(1), se.stop(1), a, x);
+  const int gu_wg = (a.slots_max - a.S) * (a.I / 64) * (a.ks_gu / min(kWpg, a.ks_gu));
+  launch_k(k_gu_phase<FMT, KT>, dim3(gu_wg), blk, s, se.start(1), se.stop(1), a, x);
   const int rpw = kWpg / a.ks_dn;
   launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * ((a.H / 64 + rpw - 1) / rpw)), blk, s, se.start(2), se.stop(2), a);
   return hipGetLastError();
