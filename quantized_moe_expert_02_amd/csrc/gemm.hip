@@ -61,36 +61,64 @@ struct GemmArgs {
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
 
+// Field masks held in VGPRs, so that each mask-and-insert below is one
+// v_and_or_b32 (a VOP3 instruction takes no literal on gfx9 and at most one
+// scalar operand; the magic constant takes that slot).
+struct DecMasks {
+  uint32_t m[4];
+};
+
+__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ DecMasks dec_masks() {
+  DecMasks k{};
+  if (FMT == MOE_W_INT4_ROW) {
+    k.m[0] = in_vgpr(0x000F000Fu);
+    k.m[1] = in_vgpr(0x00F000F0u);
+  } else if (FMT == MOE_W_INT8_ROW) {
+    k.m[0] = in_vgpr(0x00FF00FFu);
+  } else if (FMT == MOE_W_INT2_ROW) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) k.m[j] = in_vgpr(0x00030003u << (2 * j));
+  }
+  return k;
+}
+
 // int4 (device order, offset binary) -> 8 consecutive binary16 values.
-__device__ __forceinline__ half8_t dequant_int4(uint32_t d) {
+__device__ __forceinline__ half8_t dequant_int4(uint32_t d, const DecMasks& mk) {
   const half2_t k1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const half2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
   const uint32_t d8 = d >> 8;
-  const half2_t p0 = as_h2((d & 0x000F000Fu) | 0x64006400u) + k1032;
-  const half2_t p1 = as_h2((d & 0x00F000F0u) | 0x54005400u) + k72;
-  const half2_t p2 = as_h2((d8 & 0x000F000Fu) | 0x64006400u) + k1032;
-  const half2_t p3 = as_h2((d8 & 0x00F000F0u) | 0x54005400u) + k72;
+  const half2_t p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1032;
+  const half2_t p1 = as_h2((d & mk.m[1]) | 0x54005400u) + k72;
+  const half2_t p2 = as_h2((d8 & mk.m[0]) | 0x64006400u) + k1032;
+  const half2_t p3 = as_h2((d8 & mk.m[1]) | 0x54005400u) + k72;
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
 // int8 (bytes 0, 2 = columns 0, 1; bytes 1, 3 = columns 2, 3; offset
 // binary) -> 4 consecutive binary16 values: 1024 + u - 1152 = q.
-__device__ __forceinline__ void dequant_int8(uint32_t d, half2_t& p0, half2_t& p1) {
+__device__ __forceinline__ void dequant_int8(uint32_t d, const DecMasks& mk, half2_t& p0, half2_t& p1) {
   const half2_t k1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  p0 = as_h2((d & 0x00FF00FFu) | 0x64006400u) + k1152;
-  p1 = as_h2(((d >> 8) & 0x00FF00FFu) | 0x64006400u) + k1152;
+  p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1152;
+  p1 = as_h2(((d >> 8) & mk.m[0]) | 0x64006400u) + k1152;
 }
 
 // int2 (column 2j in bits 2j, column 2j+1 in bits 16+2j, offset binary) ->
 // columns 8h .. 8h+7 of the dword's 16 as binary16: the field at bit 2j
 // lands in the mantissa of 1024, 256, 64 or 16 (unit in the last place
 // 2^-2j), and base + u - (base + 2) = q.
-__device__ __forceinline__ half8_t dequant_int2(uint32_t d, int h) {
+__device__ __forceinline__ half8_t dequant_int2(uint32_t d, int h, const DecMasks& mk) {
   const uint32_t e = h ? d >> 8 : d;
-  const half2_t p0 = as_h2((e & 0x00030003u) | 0x64006400u) + half2_t{(_Float16)-1026.0f, (_Float16)-1026.0f};
-  const half2_t p1 = as_h2((e & 0x000C000Cu) | 0x5C005C00u) + half2_t{(_Float16)-258.0f, (_Float16)-258.0f};
-  const half2_t p2 = as_h2((e & 0x00300030u) | 0x54005400u) + half2_t{(_Float16)-66.0f, (_Float16)-66.0f};
-  const half2_t p3 = as_h2((e & 0x00C000C0u) | 0x4C004C00u) + half2_t{(_Float16)-18.0f, (_Float16)-18.0f};
+  const half2_t p0 = as_h2((e & mk.m[0]) | 0x64006400u) + half2_t{(_Float16)-1026.0f, (_Float16)-1026.0f};
+  const half2_t p1 = as_h2((e & mk.m[1]) | 0x5C005C00u) + half2_t{(_Float16)-258.0f, (_Float16)-258.0f};
+  const half2_t p2 = as_h2((e & mk.m[2]) | 0x54005400u) + half2_t{(_Float16)-66.0f, (_Float16)-66.0f};
+  const half2_t p3 = as_h2((e & mk.m[3]) | 0x4C004C00u) + half2_t{(_Float16)-18.0f, (_Float16)-18.0f};
   return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
 }
 
@@ -140,14 +168,14 @@ __device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t&
 //     group g takes columns 16g+8s .. 16g+8s+7 in step s.
 // E2M1: `sc` holds this lane's two block-scale bytes (columns 0-15, 16-31).
 template <int FMT>
-__device__ __forceinline__ void block_to_operands(const u32x4 (&w)[Slice<FMT>::WPS], uint32_t sc,
+__device__ __forceinline__ void block_to_operands(const u32x4 (&w)[Slice<FMT>::WPS], uint32_t sc, const DecMasks& mk,
                                                   half8_t (&b)[Slice<FMT>::STEPS][4]) {
   uint32_t d0 = w[0].x, d1 = w[0].y, d2 = w[0].z, d3 = w[0].w;
   transpose4(d0, d1, d2, d3);
   const uint32_t d[4] = {d0, d1, d2, d3};
   if (FMT == MOE_W_INT4_ROW) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b[0][q] = dequant_int4(d[q]);
+    for (int q = 0; q < 4; ++q) b[0][q] = dequant_int4(d[q], mk);
   } else if (FMT == MOE_W_INT8_ROW) {
     uint32_t f0 = w[Slice<FMT>::WPS - 1].x, f1 = w[Slice<FMT>::WPS - 1].y, f2 = w[Slice<FMT>::WPS - 1].z,
              f3 = w[Slice<FMT>::WPS - 1].w;
@@ -156,15 +184,15 @@ __device__ __forceinline__ void block_to_operands(const u32x4 (&w)[Slice<FMT>::W
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       half2_t p0, p1, p2, p3;
-      dequant_int8(d[q], p0, p1);
-      dequant_int8(f[q], p2, p3);
+      dequant_int8(d[q], mk, p0, p1);
+      dequant_int8(f[q], mk, p2, p3);
       b[0][q] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
     }
   } else if (FMT == MOE_W_INT2_ROW) {
 #pragma unroll
     for (int st = 0; st < Slice<FMT>::STEPS; ++st)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) b[st][q] = dequant_int2(d[q], st);
+      for (int q = 0; q < 4; ++q) b[st][q] = dequant_int2(d[q], st, mk);
   } else {
     uint32_t t0 = sc & 0xFF, t1 = sc & 0xFF, t2 = (sc >> 8) & 0xFF, t3 = (sc >> 8) & 0xFF;
     transpose4(t0, t1, t2, t3);
@@ -311,6 +339,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   if (xload) *reinterpret_cast<u32x4*>(&sx[0][xm][8 * xq]) = load_x(0);
   __syncthreads();
   const int n = lane & 15, g = lane >> 4;
+  const DecMasks mk = dec_masks<FMT>();
   for (int c0 = 0; c0 < nch; c0 += kDepth) {
 #pragma unroll
     for (int j = 0; j < kDepth; ++j) {
@@ -341,7 +370,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
           half8_t b[SL::STEPS][4];
-          block_to_operands<FMT>(wv[m], sv[m], b);
+          block_to_operands<FMT>(wv[m], sv[m], mk, b);
 #pragma unroll
           for (int st = 0; st < SL::STEPS; ++st)
 #pragma unroll
