@@ -23,7 +23,8 @@ _CODE_BITS = {MOE_W_INT4_ROW: 4, MOE_W_E2M1_B16: 4, MOE_W_INT8_ROW: 8, MOE_W_INT
 
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
            "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_decode_max_tokens",
-           "moe_status_string")
+           "moe_status_string", "moe_tier_create", "moe_tier_destroy", "moe_tier_use", "moe_tier_prefetch",
+           "moe_tier_slot", "moe_tier_stats")
 
 
 class MoeDims(ctypes.Structure):
@@ -35,6 +36,11 @@ class MoeDims(ctypes.Structure):
 class MoeWeights(ctypes.Structure):
     _fields_ = [("experts", ctypes.c_void_p), ("shared", ctypes.c_void_p), ("router_w", ctypes.c_void_p),
                 ("router_b", ctypes.c_void_p)]
+
+
+class MoeTierStats(ctypes.Structure):
+    _fields_ = [("hits", ctypes.c_int64), ("misses", ctypes.c_int64), ("promotions", ctypes.c_int64),
+                ("evictions", ctypes.c_int64), ("prefetched", ctypes.c_int64), ("bytes_promoted", ctypes.c_int64)]
 
 
 class MoeError(RuntimeError):
@@ -73,6 +79,18 @@ def lib():
         L.moe_w4a16_forward_profiled.argtypes = [D, W, P, i32, P, P, P, P, sz, P, P, i32]
         L.moe_w4a16_forward_profiled.restype = ctypes.c_int
         L.moe_decode_max_tokens.restype = i32
+        L.moe_tier_create.argtypes = [D, i32, P, P, i32, P, P, ctypes.POINTER(P)]
+        L.moe_tier_create.restype = ctypes.c_int
+        L.moe_tier_destroy.argtypes = [P]
+        L.moe_tier_destroy.restype = ctypes.c_int
+        L.moe_tier_use.argtypes = [P, i32, P, i32, P]
+        L.moe_tier_use.restype = ctypes.c_int
+        L.moe_tier_prefetch.argtypes = [P, i32, P, i32, P]
+        L.moe_tier_prefetch.restype = ctypes.c_int
+        L.moe_tier_slot.argtypes = [P, i32, i32]
+        L.moe_tier_slot.restype = i32
+        L.moe_tier_stats.argtypes = [P, ctypes.POINTER(MoeTierStats)]
+        L.moe_tier_stats.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -254,3 +272,66 @@ def moe_w4a16_forward_profiled(layer: PackedLayer, x: torch.Tensor, y: torch.Ten
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w4a16_forward_profiled")
     return y
+
+
+# ---- tiered expert residency (include/moe_tier.h) ---------------------------
+class Tier:
+    """A moe_tier manager.  `host_ptrs` are the (host) addresses of the packed
+    experts of every layer, layer-major; `slots` / `table` are device tensors
+    (None for the bookkeeping-only dry mode); `copy_stream` a torch stream."""
+
+    def __init__(self, dims, n_layers: int, host_ptrs, slots_per_layer: int, slots=None, table=None,
+                 copy_stream=None):
+        self.dims = _dims(dims)
+        self.n_layers = n_layers
+        n = n_layers * self.dims.n_experts
+        if len(host_ptrs) != n:
+            raise ValueError("host_ptrs must hold n_layers * n_experts addresses")
+        self._host = (ctypes.c_void_p * n)(*host_ptrs)
+        self.slots, self.table, self.copy_stream = slots, table, copy_stream
+        h = ctypes.c_void_p()
+        rc = lib().moe_tier_create(ctypes.byref(self.dims), n_layers, self._host, _p(slots), slots_per_layer,
+                                   _p(table), None if copy_stream is None else _stream(copy_stream),
+                                   ctypes.byref(h))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_tier_create")
+        self._h = h
+
+    def close(self):
+        if self._h:
+            lib().moe_tier_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _call(self, fn, layer, experts, stream):
+        e = (ctypes.c_int32 * len(experts))(*[int(v) for v in experts])
+        s = None if self.copy_stream is None and stream is None else _stream(stream)
+        rc = fn(self._h, int(layer), e, len(experts), s)
+        if rc != MOE_OK:
+            raise MoeError(rc, fn.__name__)
+
+    def use(self, layer, experts, stream=None):
+        self._call(lib().moe_tier_use, layer, experts, stream)
+
+    def prefetch(self, layer, experts, stream=None):
+        self._call(lib().moe_tier_prefetch, layer, experts, stream)
+
+    def slot(self, layer, expert) -> int:
+        return int(lib().moe_tier_slot(self._h, int(layer), int(expert)))
+
+    def stats(self) -> dict:
+        st = MoeTierStats()
+        rc = lib().moe_tier_stats(self._h, ctypes.byref(st))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_tier_stats")
+        return {f: int(getattr(st, f)) for f, _ in MoeTierStats._fields_}
+
+    def weights(self, layer, router_w, router_b, shared_ptr) -> MoeWeights:
+        """moe_weights_t of one layer that reads its experts through the table."""
+        ptr = self.table.data_ptr() + layer * self.dims.n_experts * 8
+        return MoeWeights(ptr, shared_ptr, router_w.data_ptr(), None if router_b is None else router_b.data_ptr())
