@@ -284,6 +284,110 @@ def cpu_baseline(ch: Chain, budget_s: float = 12.0, max_tokens: int = 64):
 
 
 # ---- main ----------------------------------------------------------------------
+def tiered_decode(n_layers: int = 2, slots: int = 32, tokens: int = 48, warmup: int = 16, rho: float = 0.9):
+    """Batch-1 decode of n_layers layers of the headline shape whose routed
+    experts live in pinned host memory (moe_tier.h), through a host-driven
+    loop.  Tokens follow a seeded random walk (consecutive tokens correlated
+    by rho) and pass through the layers on a residual stream,
+    x_{l+1} = x_l + y_l.  Modes:
+      hbm        every expert in HBM (the same loop, for reference);
+      host       no slots: every routed expert is read over PCIe (the
+                 unions are still reported, to count the misses);
+      lru_after  LRU slots; the layer runs first (misses read over PCIe),
+                 then its union is reported and the misses are promoted;
+      lru_load   LRU slots; the layer is routed first, its union reported,
+                 and the compute stream waits for the promotions before the
+                 layer runs (every expert read from HBM, misses copied once);
+      lru_load_next  lru_load plus the next-layer prefetch: before layer l
+                 runs, layer l+1's router is applied to the current residual
+                 and its union prefetched, overlapping layer l;
+      hot        HOT slots (most used experts); misses read over PCIe."""
+    import ctypes
+    d = synth.WORKLOADS["decode_b1"]["dims"]
+    E = d.n_experts
+    t0 = time.time()
+    base = synth.make_layer(d, ("tiered", 0), device="cuda")
+    pl0 = moe.PackedLayer.from_layer(base)
+    del base
+    pb = pl0.packed.shape[1]
+    routers = [synth.make_router(d, ("tiered", l), device="cuda") for l in range(n_layers)]
+    layers = [moe.PackedLayer(d, pl0.packed, rw, rb) for rw, rb in routers]  # same experts, own routers
+    buf = torch.empty(n_layers * E * pb + 256, dtype=torch.uint8, pin_memory=True)
+    off = (-buf.data_ptr()) % 256
+    host = buf[off:off + n_layers * E * pb].view(n_layers, E, pb)
+    for l in range(n_layers):
+        host[l].copy_(pl0.packed[:E].cpu())
+    ptrs = [host.data_ptr() + (l * E + e) * pb for l in range(n_layers) for e in range(E)]
+    slot_mem = torch.empty(max(1, n_layers * slots) * pb, dtype=torch.uint8, device="cuda")
+    table = torch.zeros(n_layers * E, dtype=torch.int64, device="cuda")
+    copy_stream = torch.cuda.Stream()
+    ws = moe.workspace(d, 1)
+    log(f"[bench] tiered: {n_layers} layers x {E * pb / 1e9:.2f} GB pinned, built in {time.time() - t0:.1f}s")
+    g = torch.Generator(device="cpu").manual_seed(1234)
+    walk = [torch.randn((1, d.hidden), generator=g)]
+    for _ in range(tokens + warmup - 1):
+        walk.append(rho * walk[-1] + (1 - rho * rho) ** 0.5 * torch.randn((1, d.hidden), generator=g))
+    xs = [w.to(torch.float16).to("cuda") for w in walk]
+    ti = torch.empty((1, d.top_k), dtype=torch.int32, device="cuda")
+    y = torch.empty((1, d.hidden), dtype=torch.float16, device="cuda")
+    dd = moe._dims(d)
+
+    def union_of(layer, x):
+        r = moe.moe_route(layer, x, ws=ws)
+        return r["uniq_ids"][:int(r["n_unique"][0])].cpu().tolist()
+
+    out = {"workload": "tiered_decode_b1", "layers": n_layers, "slots_per_layer": slots, "tokens": tokens,
+           "warmup": warmup, "rho": rho, "expert_bytes": pb, "modes": {}}
+    for mode in ("hbm", "host", "lru_after", "lru_load", "lru_load_next", "hot"):
+        C = 0 if mode in ("hbm", "host") else slots
+        policy = moe.MOE_TIER_HOT if mode == "hot" else moe.MOE_TIER_LRU
+        tier = moe.Tier(d, n_layers, ptrs, C, slots=slot_mem if C else None, table=table, copy_stream=copy_stream,
+                        policy=policy)
+        st0, t_start = None, None
+        for t in range(tokens + warmup):
+            if t == warmup:
+                torch.cuda.synchronize()
+                st0, t_start = tier.stats(), time.perf_counter()
+            x = xs[t]
+            for l in range(n_layers):
+                if mode in ("lru_load", "lru_load_next"):
+                    tier.use(l, union_of(layers[l], x))
+                    tier.sync()
+                if mode == "lru_load_next" and l + 1 < n_layers:
+                    tier.prefetch(l + 1, union_of(layers[l + 1], x))
+                if mode == "hbm":
+                    w = layers[l].weights()
+                else:
+                    w = tier.weights(l, layers[l].router_w, layers[l].router_b, layers[l].shared_ptr)
+                rc = moe.lib().moe_w4a16_forward(ctypes.byref(dd), ctypes.byref(w), moe._p(x), 1, moe._p(y),
+                                                 moe._p(ti), None, moe._p(ws), ws.numel(), moe._stream(None))
+                if rc != moe.MOE_OK:
+                    raise moe.MoeError(rc, "moe_w4a16_forward")
+                if mode in ("host", "lru_after", "hot"):
+                    tier.use(l, sorted(set(ti.cpu().numpy().ravel().tolist())))
+                x = x + y
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t_start
+        st = tier.stats()
+        tier.close()
+        torch.cuda.current_stream().wait_stream(copy_stream)
+        torch.cuda.synchronize()
+        hits, misses = st["hits"] - st0["hits"], st["misses"] - st0["misses"]
+        promos = st["promotions"] - st0["promotions"]
+        res = {"ms_per_token": dt / tokens * 1e3, "tokens_per_s": tokens / dt}
+        if mode != "hbm":
+            # bytes over PCIe: promotions, plus the misses that the layer itself read from host memory
+            read = 0 if mode.startswith("lru_load") else misses
+            res.update({"hit_rate": hits / max(1, hits + misses), "misses_per_token": misses / tokens,
+                        "promotions_per_token": promos / tokens,
+                        "pcie_gb_per_token": (read + promos) * pb / tokens / 1e9,
+                        "pcie_gbps": (read + promos) * pb / dt / 1e9})
+        out["modes"][mode] = res
+        log(f"[bench] tiered {mode}: " + json.dumps({k: round(v, 4) for k, v in res.items()}))
+    del host, buf, slot_mem
+    return out
+
+
 def path_of(T):
     return "decode" if T <= moe.moe_decode_max_tokens() else "prefill"
 
@@ -328,6 +432,7 @@ def main():
     ap.add_argument("--workload", default="decode_b1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--tiered-only", action="store_true", help="run only the tiered-residency decode line")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain elementwise copy (torch.neg) over this many MB, so that hardware "
                          "traffic counters taken over the run can be scaled against a kernel of known traffic")
@@ -347,6 +452,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    if args.tiered_only:
+        print(json.dumps(tiered_decode()))
+        return
     ch, res, touched = run_workload(args.workload, args.layers, args.steps, args.warmup)
     d, T = ch.dims, ch.T
     path = path_of(T)
@@ -378,6 +486,10 @@ def main():
                 torch.cuda.empty_cache()
             except Exception as e:
                 secondary.append({"workload": name, "error": str(e)})
+        try:
+            secondary.append(tiered_decode())
+        except Exception as e:
+            secondary.append({"workload": "tiered_decode_b1", "error": str(e)})
     out = {
         "metric": METRIC,
         "value": res["tokens_per_s"],

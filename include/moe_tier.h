@@ -13,7 +13,7 @@
  *
  * Here: every layer's packed experts live in pinned host memory (the lower
  * tier); each layer owns `slots_per_layer` expert slots in HBM (the upper
- * tier, an LRU cache).  The manager keeps a device table [L][E] of expert
+ * tier, a cache with one of the replacement policies below).  The manager keeps a device table [L][E] of expert
  * pointers: entry (l, e) points at the expert's HBM slot when it is
  * resident and at its pinned host copy otherwise, so
  *   moe_weights_t.experts = table + l * E
@@ -55,6 +55,20 @@ extern "C" {
 
 typedef struct moe_tier moe_tier_t;
 
+/* Replacement policies.
+ *   MOE_TIER_LRU: every reported miss is promoted into the layer's slots,
+ *     evicting the least recently used expert (the per-layer LRU cache of
+ *     the Colibrì engine).  Pair it with moe_tier_sync before the forward
+ *     call to load missing experts before they are used.
+ *   MOE_TIER_HOT: the layer keeps its most used experts: every report adds
+ *     one to the reported experts' use counts after all of the layer's
+ *     counts decay by a factor 15/16; a non-resident expert is promoted
+ *     only into a free slot or when its count exceeds the lowest count among
+ *     the residents (that expert is evicted).  Misses are read over PCIe
+ *     (the Ornith engine's most-used experts in GPU memory, the rest read
+ *     from pinned system memory). */
+typedef enum { MOE_TIER_LRU = 0, MOE_TIER_HOT = 1 } moe_tier_policy_t;
+
 typedef struct {
   int64_t hits;        /* experts resident in HBM when moe_tier_use reported them */
   int64_t misses;      /* experts that were read from host memory              */
@@ -77,30 +91,36 @@ typedef struct {
  *     written by the manager; create fills it with the host copies and
  *     waits for that copy to finish.
  *   copy_stream: hipStream_t for promotions (not NULL).
+ *   policy: a moe_tier_policy_t.
  * Dry mode: slots == NULL, table == NULL and copy_stream == NULL keep the
  * bookkeeping only (no HIP call at all; host_experts entries need only be
- * non-NULL) -- the LRU policy on its own, for traces and tests.
+ * non-NULL) -- the replacement policy on its own, for traces and tests.
  * Returns MOE_OK and *out, MOE_E_INVAL for bad arguments (including a host
  * pointer that the GPU cannot map), MOE_E_HIP on a HIP failure. */
 int moe_tier_create(const moe_dims_t* d, int32_t n_layers, const void* const* host_experts, void* slots,
-                    int32_t slots_per_layer, void* table, void* copy_stream, moe_tier_t** out);
+                    int32_t slots_per_layer, void* table, void* copy_stream, int32_t policy, moe_tier_t** out);
 
 /* Releases the manager (its events and host memory).  The caller makes
  * sure that no work it queued through the manager is still pending. */
 int moe_tier_destroy(moe_tier_t* t);
 
-/* Reports that a step of layer `layer` used the n experts in `experts`
- * (host array, indices in [0, n_experts), repeats allowed): resident ones
- * count as hits and become most recently used; the others count as misses
- * and are promoted into the layer's slots, evicting the least recently used
- * experts (LRU).  Kernels and waits go onto `stream` (the stream of the
- * layer's forward calls) and the copy stream; nothing synchronises. */
+/* Reports that a step of layer `layer` uses (or used) the n experts in
+ * `experts` (host array, indices in [0, n_experts), repeats allowed):
+ * resident ones count as hits and become most recently used; the others
+ * count as misses and are promoted as the policy decides.  Kernels and waits
+ * go onto `stream` (the stream of the layer's forward calls) and the copy
+ * stream; nothing synchronises. */
 int moe_tier_use(moe_tier_t* t, int32_t layer, const int32_t* experts, int32_t n, void* stream);
 
 /* Promotes experts ahead of use (the next-layer prefetch): like
  * moe_tier_use, but resident experts are only refreshed and nothing counts
  * as a hit or a miss. */
 int moe_tier_prefetch(moe_tier_t* t, int32_t layer, const int32_t* experts, int32_t n, void* stream);
+
+/* Makes `stream` wait until every promotion enqueued so far has been copied
+ * and switched in the table, so that forward calls queued afterwards read
+ * those experts from HBM. */
+int moe_tier_sync(moe_tier_t* t, void* stream);
 
 /* HBM slot index (within the layer) holding expert e of layer l, or -1 when
  * it is read from host memory (the manager's view: a promotion counts from

@@ -24,7 +24,8 @@ _CODE_BITS = {MOE_W_INT4_ROW: 4, MOE_W_E2M1_B16: 4, MOE_W_INT8_ROW: 8, MOE_W_INT
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
            "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_decode_max_tokens",
            "moe_status_string", "moe_tier_create", "moe_tier_destroy", "moe_tier_use", "moe_tier_prefetch",
-           "moe_tier_slot", "moe_tier_stats")
+           "moe_tier_slot", "moe_tier_stats", "moe_tier_sync")
+MOE_TIER_LRU, MOE_TIER_HOT = 0, 1
 
 
 class MoeDims(ctypes.Structure):
@@ -79,7 +80,7 @@ def lib():
         L.moe_w4a16_forward_profiled.argtypes = [D, W, P, i32, P, P, P, P, sz, P, P, i32]
         L.moe_w4a16_forward_profiled.restype = ctypes.c_int
         L.moe_decode_max_tokens.restype = i32
-        L.moe_tier_create.argtypes = [D, i32, P, P, i32, P, P, ctypes.POINTER(P)]
+        L.moe_tier_create.argtypes = [D, i32, P, P, i32, P, P, i32, ctypes.POINTER(P)]
         L.moe_tier_create.restype = ctypes.c_int
         L.moe_tier_destroy.argtypes = [P]
         L.moe_tier_destroy.restype = ctypes.c_int
@@ -91,6 +92,8 @@ def lib():
         L.moe_tier_slot.restype = i32
         L.moe_tier_stats.argtypes = [P, ctypes.POINTER(MoeTierStats)]
         L.moe_tier_stats.restype = ctypes.c_int
+        L.moe_tier_sync.argtypes = [P, P]
+        L.moe_tier_sync.restype = ctypes.c_int
         L.moe_status_string.argtypes = [ctypes.c_int]
         L.moe_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -281,7 +284,7 @@ class Tier:
     (None for the bookkeeping-only dry mode); `copy_stream` a torch stream."""
 
     def __init__(self, dims, n_layers: int, host_ptrs, slots_per_layer: int, slots=None, table=None,
-                 copy_stream=None):
+                 copy_stream=None, policy: int = MOE_TIER_LRU):
         self.dims = _dims(dims)
         self.n_layers = n_layers
         n = n_layers * self.dims.n_experts
@@ -291,7 +294,7 @@ class Tier:
         self.slots, self.table, self.copy_stream = slots, table, copy_stream
         h = ctypes.c_void_p()
         rc = lib().moe_tier_create(ctypes.byref(self.dims), n_layers, self._host, _p(slots), slots_per_layer,
-                                   _p(table), None if copy_stream is None else _stream(copy_stream),
+                                   _p(table), None if copy_stream is None else _stream(copy_stream), int(policy),
                                    ctypes.byref(h))
         if rc != MOE_OK:
             raise MoeError(rc, "moe_tier_create")
@@ -320,6 +323,12 @@ class Tier:
 
     def prefetch(self, layer, experts, stream=None):
         self._call(lib().moe_tier_prefetch, layer, experts, stream)
+
+    def sync(self, stream=None):
+        """`stream` waits for every promotion enqueued so far."""
+        rc = lib().moe_tier_sync(self._h, None if self.copy_stream is None and stream is None else _stream(stream))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_tier_sync")
 
     def slot(self, layer, expert) -> int:
         return int(lib().moe_tier_slot(self._h, int(layer), int(expert)))

@@ -30,7 +30,7 @@ def _pinned_copy(packed: torch.Tensor) -> torch.Tensor:
 
 
 class TieredModel:
-    def __init__(self, dims, n_layers, slots_per_layer, seed):
+    def __init__(self, dims, n_layers, slots_per_layer, seed, policy=moe.MOE_TIER_LRU):
         self.dims, self.L, self.C = dims, n_layers, slots_per_layer
         self.layers = [moe.PackedLayer.from_layer(synth.make_layer(dims, ("tier", seed, l))) for l in range(n_layers)]
         E = dims.n_experts
@@ -41,7 +41,7 @@ class TieredModel:
         self.table = torch.zeros(n_layers * E, dtype=torch.int64, device=DEV)
         self.copy_stream = torch.cuda.Stream()
         self.tier = moe.Tier(dims, n_layers, ptrs, slots_per_layer, slots=self.slots if slots_per_layer else None,
-                             table=self.table, copy_stream=self.copy_stream)
+                             table=self.table, copy_stream=self.copy_stream, policy=policy)
 
     def forward(self, l, x, y, ws, ti):
         pl = self.layers[l]
@@ -127,4 +127,39 @@ def test_lru_promotions_race_with_queued_forwards():
                 assert tab[l * E + e] == want
             else:
                 assert tab[l * E + e] != 0 and not (m.slots.data_ptr() <= tab[l * E + e] < m.slots.data_ptr() + m.slots.numel())
+    m.tier.close()
+
+
+@pytest.mark.parametrize("policy", [moe.MOE_TIER_LRU, moe.MOE_TIER_HOT])
+def test_load_before_use_and_hot_set(policy):
+    """Each step routes first, reports its union, makes the compute stream
+    wait for the promotions (moe_tier_sync) and then runs the layer: outputs
+    equal the all-HBM layer bitwise; under LRU every reported expert is
+    resident when the layer runs (nothing is read over PCIe)."""
+    dims = synth.Dims(512, 256, 24, 4, 1, synth.INT4_ROW)
+    _log("tier load-before-use", policy)
+    C = 6
+    m = TieredModel(dims, 1, C, ("lbu", policy), policy=policy)
+    pl = m.layers[0]
+    for step in range(8):
+        T = 1 + step % 3
+        x = _step_inputs(dims, T, ("lbu", policy, step))
+        ws = moe.workspace(dims, T, DEV)
+        r = moe.moe_route(pl, x, ws=ws)
+        nu = int(r["n_unique"][0])
+        union = r["uniq_ids"][:nu].cpu().tolist()
+        m.tier.use(0, union)
+        m.tier.sync()
+        if policy == moe.MOE_TIER_LRU and len(union) <= C:
+            assert all(m.tier.slot(0, e) >= 0 for e in union)
+        y = torch.empty((T, dims.hidden), dtype=torch.float16, device=DEV)
+        ti = torch.empty((T, dims.top_k), dtype=torch.int32, device=DEV)
+        m.forward(0, x, y, ws, ti)
+        y_ref = moe.moe_w4a16_forward(pl, x)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), step
+        assert sorted(set(ti.cpu().numpy().ravel().tolist())) == union
+    st = m.tier.stats()
+    _log("  stats", st)
+    assert st["promotions"] > 0
     m.tier.close()

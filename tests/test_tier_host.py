@@ -17,45 +17,66 @@ def _fake_ptrs(n):
     return [256 * (i + 1) for i in range(n)]  # non-NULL, 256-byte aligned; never dereferenced in dry mode
 
 
-class LruModel:
-    """Per-layer LRU over C slots: a miss takes the lowest free slot, else
-    the slot of the least recently used expert; repeats within one call
-    count once."""
+class CacheModel:
+    """Per-layer cache over C slots.  A promotion takes the lowest free slot,
+    else the slot of the least recently used expert (LRU) or of the resident
+    with the lowest decayed use count, ties to the least recently used
+    (HOT); under HOT a reported miss is promoted only into a free slot or
+    when its count is above that resident's.  HOT counts: each report first
+    multiplies the layer's counts by 15/16, then adds one per reported
+    expert.  Repeats within one call count once."""
 
-    def __init__(self, L, C):
-        self.C = C
-        self.slot = [dict() for _ in range(L)]         # expert -> slot
-        self.order = [collections.OrderedDict() for _ in range(L)]  # expert, oldest first
+    def __init__(self, L, E, C, policy):
+        self.C, self.policy = C, policy
+        self.slot = [dict() for _ in range(L)]                          # expert -> slot
+        self.order = [collections.OrderedDict() for _ in range(L)]      # expert, least recent first
+        self.count = np.zeros((L, E), dtype=np.float32)
         self.stats = dict(hits=0, misses=0, promotions=0, evictions=0, prefetched=0)
 
-    def visit(self, l, experts, count):
-        for e in dict.fromkeys(experts):  # first occurrences, in order
+    def _victim(self, l):
+        used = set(self.slot[l].values())
+        free = [s for s in range(self.C) if s not in used]
+        if free:
+            return None, free[0]
+        if self.policy == moe.MOE_TIER_LRU:
+            v = next(iter(self.order[l]))
+        else:  # lowest count; among equal counts the least recently used
+            v = min(self.order[l], key=lambda e: (self.count[l, e], list(self.order[l]).index(e)))
+        return v, self.slot[l][v]
+
+    def visit(self, l, experts, use):
+        uniq = list(dict.fromkeys(experts))  # first occurrences, in order
+        if self.policy == moe.MOE_TIER_HOT and use:
+            self.count[l] *= np.float32(15.0 / 16.0)
+            for e in uniq:
+                self.count[l, e] += np.float32(1.0)
+        for e in uniq:
             if e in self.slot[l]:
                 self.order[l].move_to_end(e)
-                if count:
+                if use:
                     self.stats["hits"] += 1
                 continue
-            self.stats["misses" if count else "prefetched"] += 1
+            self.stats["misses" if use else "prefetched"] += 1
             if self.C == 0:
                 continue
-            used = set(self.slot[l].values())
-            free = [s for s in range(self.C) if s not in used]
-            if free:
-                s = free[0]
-            else:
-                victim, _ = self.order[l].popitem(last=False)
-                s = self.slot[l].pop(victim)
+            v, s = self._victim(l)
+            if self.policy == moe.MOE_TIER_HOT and use and v is not None and not self.count[l, e] > self.count[l, v]:
+                continue
+            if v is not None:
+                del self.order[l][v]
+                del self.slot[l][v]
                 self.stats["evictions"] += 1
             self.slot[l][e] = s
             self.order[l][e] = None
             self.stats["promotions"] += 1
 
 
+@pytest.mark.parametrize("policy", [moe.MOE_TIER_LRU, moe.MOE_TIER_HOT])
 @pytest.mark.parametrize("L,C,seed", [(1, 4, 0), (3, 4, 1), (2, 1, 2), (2, 16, 3), (2, 0, 4)])
-def test_lru_policy_matches_model(L, C, seed):
+def test_policy_matches_model(L, C, seed, policy):
     E = DIMS.n_experts
-    t = moe.Tier(DIMS, L, _fake_ptrs(L * E), C)
-    m = LruModel(L, C)
+    t = moe.Tier(DIMS, L, _fake_ptrs(L * E), C, policy=policy)
+    m = CacheModel(L, E, C, policy)
     rng = np.random.default_rng(seed)
     pop = rng.permutation(E)  # skewed popularity, so that hits happen
     for step in range(300):
@@ -79,6 +100,8 @@ def test_lru_policy_matches_model(L, C, seed):
         assert st["hits"] == 0 and st["promotions"] == 0
     else:
         assert st["hits"] > 0 and (st["evictions"] > 0 or C == E)
+    if policy == moe.MOE_TIER_HOT and 0 < C < E:  # a hot set promotes less than LRU on the same trace
+        assert st["promotions"] < st["misses"] + st["prefetched"]
     t.close()
 
 
@@ -92,21 +115,36 @@ def test_layers_do_not_share_slots():
     t.close()
 
 
+def test_hot_set_keeps_the_most_used():
+    """Two experts used on every report stay resident against a stream of
+    one-off experts; LRU on the same trace evicts them."""
+    E = DIMS.n_experts
+    for policy, kept in ((moe.MOE_TIER_HOT, True), (moe.MOE_TIER_LRU, False)):
+        t = moe.Tier(DIMS, 1, _fake_ptrs(E), 2, policy=policy)
+        for i in range(40):
+            t.use(0, [0, 1])
+            t.use(0, [2 + i % (E - 2)])
+            t.use(0, [2 + (i + 5) % (E - 2)])
+        assert (t.slot(0, 0) >= 0 and t.slot(0, 1) >= 0) == kept, policy
+        t.close()
+
+
 def test_bad_arguments():
     E = DIMS.n_experts
     L = moe.lib()
     d = moe._dims(DIMS)
     out = ctypes.c_void_p()
     ptrs = (ctypes.c_void_p * E)(*_fake_ptrs(E))
-    assert L.moe_tier_create(ctypes.byref(d), 1, ptrs, None, E + 1, None, None, ctypes.byref(out)) == moe.MOE_E_INVAL
-    assert L.moe_tier_create(ctypes.byref(d), 0, ptrs, None, 2, None, None, ctypes.byref(out)) == moe.MOE_E_INVAL
+    assert L.moe_tier_create(ctypes.byref(d), 1, ptrs, None, E + 1, None, None, 0, ctypes.byref(out)) == moe.MOE_E_INVAL
+    assert L.moe_tier_create(ctypes.byref(d), 0, ptrs, None, 2, None, None, 0, ctypes.byref(out)) == moe.MOE_E_INVAL
+    assert L.moe_tier_create(ctypes.byref(d), 1, ptrs, None, 2, None, None, 2, ctypes.byref(out)) == moe.MOE_E_INVAL
     bad = (ctypes.c_void_p * E)(*([257] + _fake_ptrs(E)[1:]))
-    assert L.moe_tier_create(ctypes.byref(d), 1, bad, None, 2, None, None, ctypes.byref(out)) == moe.MOE_E_INVAL
+    assert L.moe_tier_create(ctypes.byref(d), 1, bad, None, 2, None, None, 0, ctypes.byref(out)) == moe.MOE_E_INVAL
     # a table without a copy stream is neither dry nor complete
-    assert L.moe_tier_create(ctypes.byref(d), 1, ptrs, None, 0, ctypes.c_void_p(256), None,
+    assert L.moe_tier_create(ctypes.byref(d), 1, ptrs, None, 0, ctypes.c_void_p(256), None, 0,
                              ctypes.byref(out)) == moe.MOE_E_INVAL
     bad_dims = moe.MoeDims(100, 128, 16, 2, 1, 0, 0.0)
-    assert L.moe_tier_create(ctypes.byref(bad_dims), 1, ptrs, None, 2, None, None,
+    assert L.moe_tier_create(ctypes.byref(bad_dims), 1, ptrs, None, 2, None, None, 0,
                              ctypes.byref(out)) == moe.MOE_E_INVAL
     t = moe.Tier(DIMS, 2, _fake_ptrs(2 * E), 2)
     for layer, experts in ((2, [0]), (-1, [0]), (0, [E]), (0, [-1])):
@@ -115,4 +153,6 @@ def test_bad_arguments():
     assert t.slot(5, 0) == -1 and t.slot(0, E) == -1
     assert L.moe_tier_destroy(None) == moe.MOE_E_INVAL
     assert L.moe_tier_stats(None, None) == moe.MOE_E_INVAL
+    assert L.moe_tier_sync(None, None) == moe.MOE_E_INVAL
+    t.sync()  # dry mode: nothing to wait for
     t.close()
