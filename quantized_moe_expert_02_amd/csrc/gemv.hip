@@ -643,7 +643,8 @@ __device__ __forceinline__ void gu_finish(const DecArgs& a, GuScales gs, int rb,
 // K-segments [grp*nw, grp*nw + nw) of (slot s, row block rb), nw <= kWpg
 // wavefronts (the others only join the barriers).  With ngrp == 1 the
 // workgroup forms h; otherwise each group writes its sum as partial plane
-// grp and the last group to arrive adds the planes in order and forms h.
+// grp and the last workgroup to arrive (of all groups and token tiles)
+// adds the planes in order and forms h for every token of the slot.
 template <int FMT, int NT, int KT>
 __device__ __forceinline__ void gu_tile_group(const DecArgs& a, const uint16_t* __restrict__ x, const SlotInfo& si,
                                               int s, int rb, int grp, int ngrp, int nw, int nch, int i0,
@@ -683,16 +684,18 @@ __device__ __forceinline__ void gu_tile_group(const DecArgs& a, const uint16_t* 
 
 template <int FMT, int KT>
 __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __restrict__ x, int s, int rb, int grp,
-                                         int ngrp, int nw, int nch, GuLds<KT>& ls) {
+                                         int ngrp, int nw, int nch, int tile, int ntiles, GuLds<KT>& ls) {
   SlotInfo si;
   if (!get_slot(a, s, si)) return;  // uniform over the workgroup
   const GuScales gs = gu_scales<FMT>(a, si, rb);
-  for (int i0 = 0; i0 < si.n; i0 += KT) {
+  // token tiles tile, tile + ntiles, ... of the slot (several workgroups
+  // share a slot's tiles when ntiles > 1)
+  for (int i0 = tile * KT; i0 < si.n; i0 += KT * ntiles) {
     if (KT == 1 || si.n - i0 == 1) gu_tile_group<FMT, 1, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, gs, ls);
     else gu_tile_group<FMT, KT, KT>(a, x, si, s, rb, grp, ngrp, nw, nch, i0, gs, ls);
   }
   if (ngrp == 1 || threadIdx.x >= 64) return;
-  if (!arrive_last(a.gu_cnt + (size_t)s * (a.I / 64) + rb, (uint32_t)ngrp)) return;
+  if (!arrive_last(a.gu_cnt + (size_t)s * (a.I / 64) + rb, (uint32_t)(ngrp * ntiles))) return;
   const int lane = threadIdx.x & 63;
   for (int i = 0; i < si.n; ++i) {
     int tok, row;
@@ -847,10 +850,13 @@ __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint
     router_workgroup(a, ul);
     return;
   }
-  // shared expert: workgroup = (row block, group of kWpg K-segments)
-  const int nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw;
-  const int j = b - a.n_router_wg;
-  gu_group<FMT, KT>(a, x, 0, j / ngrp, j % ngrp, ngrp, nw, a.cpu_sgu, gl);
+  // shared expert: workgroup = (token tile, row block, group of kWpg
+  // K-segments); the tiles of one (row block, group) are n_rbg workgroups
+  // apart, a multiple of 8, so they run on one XCD and share its L2 copy
+  // of the weights
+  const int nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw, n_rbg = (a.I / 64) * ngrp;
+  const int j = b - a.n_router_wg, r = j % n_rbg;
+  gu_group<FMT, KT>(a, x, 0, r / ngrp, r % ngrp, ngrp, nw, a.cpu_sgu, j / n_rbg, (a.T + KT - 1) / KT, gl);
 }
 
 template <int FMT, int KT>
@@ -859,7 +865,7 @@ __global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_
   // workgroup = (slot, row block, group of kWpg K-segments)
   const int nw = min(kWpg, a.ks_gu), ngrp = a.ks_gu / nw, per_slot = (a.I / 64) * ngrp;
   const int r = blockIdx.x % per_slot;
-  gu_group<FMT, KT>(a, x, a.S + blockIdx.x / per_slot, r / ngrp, r % ngrp, ngrp, nw, a.cpu_gu, gl);
+  gu_group<FMT, KT>(a, x, a.S + blockIdx.x / per_slot, r / ngrp, r % ngrp, ngrp, nw, a.cpu_gu, 0, 1, gl);
 }
 
 template <int FMT, int KT>
@@ -872,7 +878,7 @@ __global__ __launch_bounds__(64 * kWpg) void k_dn_phase(DecArgs a) {
 template <int FMT, int KT>
 hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, const StageEvents& se) {
   const int nw = min(kWpg, a.ks_sgu);
-  const int sgu_wg = a.S * (a.I / 64) * (a.ks_sgu / nw);
+  const int sgu_wg = a.S * (a.I / 64) * (a.ks_sgu / nw) * ((a.T + KT - 1) / KT);
   const dim3 blk(64 * kWpg);
   launch_k(k_route_phase<FMT, KT>, dim3(a.n_router_wg + sgu_wg), blk, s, se.start(0), se.stop(0), a, x);
   const int gu_wg = (a.slots_max - a.S) * (a.I / 64) * (a.ks_gu / min(kWpg, a.ks_gu));
