@@ -332,6 +332,7 @@ TOPP_FORWARD_CASES = [
     ("prefill_topp_t40", synth.Dims(256, 128, 16, 4, 1, 0, top_p=0.5), 40),
     ("prefill_e2m1_topp_t129", synth.Dims(384, 384, 33, 3, 1, 1, top_p=0.7), 129),
     ("int2_topp", synth.Dims(256, 128, 8, 2, 1, 3, top_p=0.51), 4),
+    ("int8_prefill_topp_t40", synth.Dims(256, 256, 16, 4, 1, 2, top_p=0.5), 40),
 ]
 
 
@@ -354,7 +355,7 @@ def test_forward_top_p_matches_oracle(name, dims, T):
     assert_close(y, y_ref, name)
 
 
-@pytest.mark.parametrize("name", ["decode_b1", "decode_b8"])
+@pytest.mark.parametrize("name", ["decode_b1", "decode_b8", "int2_b8"])
 def test_forward_top_p_full_size(name):
     """Full-size decode layers with top-p 0.7: fewer experts streamed, every
     output element checked."""

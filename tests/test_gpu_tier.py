@@ -57,7 +57,7 @@ def _step_inputs(dims, T, tag):
     return synth.make_tokens(dims, T, tag).to(DEV)
 
 
-@pytest.mark.parametrize("wfmt", [synth.INT4_ROW, synth.E2M1_B16])
+@pytest.mark.parametrize("wfmt", [synth.INT4_ROW, synth.E2M1_B16, synth.INT8_ROW, synth.INT2_ROW])
 def test_all_experts_from_host_memory(wfmt):
     """slots_per_layer = 0: every routed expert is read over PCIe."""
     dims = synth.Dims(512, 256, 16, 4, 1, wfmt)
