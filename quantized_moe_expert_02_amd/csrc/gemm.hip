@@ -4,19 +4,28 @@
 // Each unique expert is applied to all of its tokens at once (the batch-wise
 // MoE union, "Show HN: 低速のコンピュータでGLM 5.2を動かす方法", hakusoku.com,
 // section 実装済み機能); its weights are decoded in registers, straight into
-// matrix-core operands, as exact binary16 values (int8/int4/int2 codes are
-// small integers; e2m1 x e4m3 has at most 6 significant bits) -- the in-register
-// decode of the Ornith engine ("GTX 1070向け35BパラメータMoEモデル推論エンジン公開",
-// section "VRAMとシステムメモリで重みを分割する設計") -- and multiplied on
-// v_mfma_f32_16x16x32_f16 with fp32 accumulation.  Row scales (integer
-// formats) or the tensor scale (e2m1) are applied in the epilogue, as is the
-// SwiGLU.
+// matrix-core operands -- the in-register decode of the Ornith engine ("GTX
+// 1070向け35BパラメータMoEモデル推論エンジン公開", section "VRAMとシステムメモリで
+// 重みを分割する設計") -- and multiplied on v_mfma_f32_16x16x32_f16 with fp32
+// accumulation:
+//   integer codes u = q + OFF (offset binary) are masked into binary16
+//     subnormals u * 2^(2j-24) (j = the field's bit position / 2 within its
+//     half) with no arithmetic; the activations are divided by 2^(2j) when
+//     they are staged, so every product is x * u * 2^-24, and the epilogue
+//     forms sum x q = 2^24 acc - OFF * sum x from per-token activation sums
+//     (the matrix cores keep subnormal inputs, checked on the hardware);
+//   e2m1 codes times their e4m3 block scale are exact binary16 values (at
+//     most 6 significant bits).
+// Row scales (integer formats) or the tensor scale (e2m1) are applied in the
+// epilogue, as is the SwiGLU.
 //
-//   k_expert_gemm<.., 2>:  tile = 64 tokens of one expert x 512 gate rows +
-//                          512 up rows -> h (binary16, one row per pair)
-//   k_expert_gemm<.., 1>:  tile = 64 tokens x 512 down rows -> per-pair fp32
-//                          outputs, already multiplied by the routing weight
+//   k_expert_gemm<.., 2, ..>:  tile = 64 tokens of one expert x 512 gate rows
+//                              + 512 up rows -> h (binary16, one row per pair)
+//   k_expert_gemm<.., 1, ..>:  tile = 64 tokens x 512 down rows -> per-pair
+//                              fp32 outputs, times the routing weight
 //   k_combine:  y[t] = sum over slots j (in slot order) + shared -> binary16
+#include <type_traits>
+
 #include "common.h"
 
 namespace moe {
@@ -31,16 +40,17 @@ typedef __attribute__((address_space(1))) const u32x4 guint4;
 constexpr int BM = kPrefillTileRows;  // tokens per tile
 
 // Per-format shape of one K-slice of the main loop: SC columns, WPS 16-byte
-// pieces (chunks of the packed layout) per lane and matrix, SC / 32 MFMA
-// K-steps; kDepth slices of weights in flight (a multiple of the activation
-// ring's depth, 2).
+// chunks of the packed layout per lane, row block and matrix, SC / 32 MFMA
+// K-steps.  Integer codes (offset binary, code = q + OFF) use the subnormal
+// decode; E2M1 codes are converted and scaled.
 template <int FMT>
 struct Slice {
   static constexpr int SC = FMT == MOE_W_INT2_ROW ? 64 : 32;
   static constexpr int WPS = FMT == MOE_W_INT8_ROW ? 2 : 1;
   static constexpr int STEPS = SC / 32;
   static constexpr int XP = SC + 8;  // halves per LDS token row (8 pad)
-  static constexpr int kDepth = WPS == 1 ? 6 : 2;
+  static constexpr bool SUB = FMT != MOE_W_E2M1_B16;
+  static constexpr int OFF = FMT == MOE_W_INT8_ROW ? 128 : FMT == MOE_W_INT4_ROW ? 8 : 2;
 };
 
 struct GemmArgs {
@@ -60,67 +70,6 @@ struct GemmArgs {
 };
 
 __device__ __forceinline__ half2_t as_h2(uint32_t v) { return __builtin_bit_cast(half2_t, v); }
-
-// Field masks held in VGPRs, so that each mask-and-insert below is one
-// v_and_or_b32 (a VOP3 instruction takes no literal on gfx9 and at most one
-// scalar operand; the magic constant takes that slot).
-struct DecMasks {
-  uint32_t m[4];
-};
-
-__device__ __forceinline__ uint32_t in_vgpr(uint32_t v) {
-  uint32_t r;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "s"(v));
-  return r;
-}
-
-template <int FMT>
-__device__ __forceinline__ DecMasks dec_masks() {
-  DecMasks k{};
-  if (FMT == MOE_W_INT4_ROW) {
-    k.m[0] = in_vgpr(0x000F000Fu);
-    k.m[1] = in_vgpr(0x00F000F0u);
-  } else if (FMT == MOE_W_INT8_ROW) {
-    k.m[0] = in_vgpr(0x00FF00FFu);
-  } else if (FMT == MOE_W_INT2_ROW) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) k.m[j] = in_vgpr(0x00030003u << (2 * j));
-  }
-  return k;
-}
-
-// int4 (device order, offset binary) -> 8 consecutive binary16 values.
-__device__ __forceinline__ half8_t dequant_int4(uint32_t d, const DecMasks& mk) {
-  const half2_t k1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
-  const half2_t k72 = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const uint32_t d8 = d >> 8;
-  const half2_t p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1032;
-  const half2_t p1 = as_h2((d & mk.m[1]) | 0x54005400u) + k72;
-  const half2_t p2 = as_h2((d8 & mk.m[0]) | 0x64006400u) + k1032;
-  const half2_t p3 = as_h2((d8 & mk.m[1]) | 0x54005400u) + k72;
-  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
-
-// int8 (bytes 0, 2 = columns 0, 1; bytes 1, 3 = columns 2, 3; offset
-// binary) -> 4 consecutive binary16 values: 1024 + u - 1152 = q.
-__device__ __forceinline__ void dequant_int8(uint32_t d, const DecMasks& mk, half2_t& p0, half2_t& p1) {
-  const half2_t k1152 = {(_Float16)-1152.0f, (_Float16)-1152.0f};
-  p0 = as_h2((d & mk.m[0]) | 0x64006400u) + k1152;
-  p1 = as_h2(((d >> 8) & mk.m[0]) | 0x64006400u) + k1152;
-}
-
-// int2 (column 2j in bits 2j, column 2j+1 in bits 16+2j, offset binary) ->
-// columns 8h .. 8h+7 of the dword's 16 as binary16: the field at bit 2j
-// lands in the mantissa of 1024, 256, 64 or 16 (unit in the last place
-// 2^-2j), and base + u - (base + 2) = q.
-__device__ __forceinline__ half8_t dequant_int2(uint32_t d, int h, const DecMasks& mk) {
-  const uint32_t e = h ? d >> 8 : d;
-  const half2_t p0 = as_h2((e & mk.m[0]) | 0x64006400u) + half2_t{(_Float16)-1026.0f, (_Float16)-1026.0f};
-  const half2_t p1 = as_h2((e & mk.m[1]) | 0x5C005C00u) + half2_t{(_Float16)-258.0f, (_Float16)-258.0f};
-  const half2_t p2 = as_h2((e & mk.m[2]) | 0x54005400u) + half2_t{(_Float16)-66.0f, (_Float16)-66.0f};
-  const half2_t p3 = as_h2((e & mk.m[3]) | 0x4C004C00u) + half2_t{(_Float16)-18.0f, (_Float16)-18.0f};
-  return half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-}
 
 // e2m1 codes (byte b = columns 2b, 2b+1) times a block scale -> 8 binary16.
 __device__ __forceinline__ half8_t dequant_e2m1(uint32_t d, half2_t s) {
@@ -156,55 +105,111 @@ __device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t&
   d3 = r23[1];
 }
 
-// One K-slice of a 64-row block in a wavefront -> the B operands of the
-// v_mfma_f32_16x16x32_f16 steps, b[step][q] for the 16-row group q: lane
-// 16g+n receives row 16q+n and eight columns that depend on the format (the
-// A operands are read from LDS to match, see a_operand):
-//   4-bit: one chunk, dword b = columns 8b..8b+7 -> lane group g takes
-//     columns 8g..8g+7;
-//   int8: two chunks, dword b = columns 4b..4b+3 of each -> lane group g
-//     takes columns 4g..4g+3 and 16+4g..16+4g+3;
-//   int2: one chunk of 64 columns, dword b = columns 16b..16b+15 -> lane
-//     group g takes columns 16g+8s .. 16g+8s+7 in step s.
-// E2M1: `sc` holds this lane's two block-scale bytes (columns 0-15, 16-31).
-template <int FMT>
-__device__ __forceinline__ void block_to_operands(const u32x4 (&w)[Slice<FMT>::WPS], uint32_t sc, const DecMasks& mk,
-                                                  half8_t (&b)[Slice<FMT>::STEPS][4]) {
-  uint32_t d0 = w[0].x, d1 = w[0].y, d2 = w[0].z, d3 = w[0].w;
-  transpose4(d0, d1, d2, d3);
-  const uint32_t d[4] = {d0, d1, d2, d3};
+// An activation piece: PH consecutive binary16 values of one token row
+// (PH = 4 or 8, starting at a multiple of PH), staged by one thread.
+template <int PH>
+struct Piece {
+  uint32_t w[PH / 2];
+};
+
+// Binary16 factors that put the activations of a piece on the scale of the
+// subnormal weight decode below: the column at position j of an 8-column
+// group decodes to u * 2^-24 * class(j), so its activation is divided by
+// class(j) (exactly, unless it becomes subnormal).  int4: classes 1, 1, 16,
+// 16 repeating every four columns; int2: 1, 1, 4, 4, 16, 16, 64, 64.
+template <int FMT, int PH>
+__device__ __forceinline__ Piece<PH> prescale(Piece<PH> v) {
+  auto mul = [](uint32_t p, float f) {
+    return __builtin_bit_cast(uint32_t, as_h2(p) * half2_t{(_Float16)f, (_Float16)f});
+  };
   if (FMT == MOE_W_INT4_ROW) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) b[0][q] = dequant_int4(d[q], mk);
-  } else if (FMT == MOE_W_INT8_ROW) {
-    uint32_t f0 = w[Slice<FMT>::WPS - 1].x, f1 = w[Slice<FMT>::WPS - 1].y, f2 = w[Slice<FMT>::WPS - 1].z,
-             f3 = w[Slice<FMT>::WPS - 1].w;
-    transpose4(f0, f1, f2, f3);
-    const uint32_t f[4] = {f0, f1, f2, f3};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      half2_t p0, p1, p2, p3;
-      dequant_int8(d[q], mk, p0, p1);
-      dequant_int8(f[q], mk, p2, p3);
-      b[0][q] = half8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    }
+    for (int k = 1; k < PH / 2; k += 2) v.w[k] = mul(v.w[k], 1.0f / 16);
   } else if (FMT == MOE_W_INT2_ROW) {
+    static_assert(FMT != MOE_W_INT2_ROW || PH == 8, "int2 pieces are whole 8-column groups");
+    v.w[1] = mul(v.w[1], 1.0f / 4);
+    v.w[PH / 2 - 2] = mul(v.w[PH / 2 - 2], 1.0f / 16);
+    v.w[PH / 2 - 1] = mul(v.w[PH / 2 - 1], 1.0f / 64);
+  }
+  return v;
+}
+
+// Sum of the values of a piece, in fp32.
+template <int PH>
+__device__ __forceinline__ float piece_sum(Piece<PH> v) {
+  const half2_t one = {(_Float16)1.0f, (_Float16)1.0f};
+  float acc = 0.f;
 #pragma unroll
-    for (int st = 0; st < Slice<FMT>::STEPS; ++st)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) b[st][q] = dequant_int2(d[q], st, mk);
+  for (int k = 0; k < PH / 2; ++k) acc = __builtin_amdgcn_fdot2(as_h2(v.w[k]), one, acc, false);
+  return acc;
+}
+
+// One K-slice of a 64-row block, rearranged for the MFMA B operands: after
+// the transposes, lane 16g+n holds in d[q] (and f[q] for int8) the dword of
+// row 16q+n that MFMA lane group g needs:
+//   4-bit: one chunk, dword b = columns 8b..8b+7 -> group g takes columns
+//     8g..8g+7;
+//   int8: two chunks, dword b = columns 4b..4b+3 of each -> group g takes
+//     columns 4g..4g+3 and 16+4g..16+4g+3;
+//   int2: one chunk of 64 columns, dword b = columns 16b..16b+15 -> group g
+//     takes columns 16g+8s .. 16g+8s+7 in step s.
+// E2M1: s[q] holds the block-scale byte of those columns.
+struct RawBlock {
+  uint32_t d[4], f[4], s[4];
+};
+
+// A copy the compiler cannot fold: the transposes below work in place, and
+// copying first ends the life of the loaded registers here, so that the next
+// load can reuse them (otherwise the loop would copy every load result at its
+// back edge, after waiting for it).
+__device__ __forceinline__ uint32_t fresh(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
+template <int FMT>
+__device__ __forceinline__ RawBlock to_raw(const u32x4 (&w)[Slice<FMT>::WPS], uint32_t sc) {
+  RawBlock r;
+  r.d[0] = fresh(w[0].x), r.d[1] = fresh(w[0].y), r.d[2] = fresh(w[0].z), r.d[3] = fresh(w[0].w);
+  transpose4(r.d[0], r.d[1], r.d[2], r.d[3]);
+  if (FMT == MOE_W_INT8_ROW) {
+    constexpr int P = Slice<FMT>::WPS - 1;
+    r.f[0] = fresh(w[P].x), r.f[1] = fresh(w[P].y), r.f[2] = fresh(w[P].z), r.f[3] = fresh(w[P].w);
+    transpose4(r.f[0], r.f[1], r.f[2], r.f[3]);
+  }
+  if (FMT == MOE_W_E2M1_B16) {
+    r.s[0] = sc & 0xFF, r.s[1] = sc & 0xFF, r.s[2] = (sc >> 8) & 0xFF, r.s[3] = (sc >> 8) & 0xFF;
+    transpose4(r.s[0], r.s[1], r.s[2], r.s[3]);
+  }
+  return r;
+}
+
+// B operand of MFMA step `st` for the 16-row group q.  Integer codes u
+// (offset binary) become binary16 subnormals by masking alone: a field whose
+// lowest bit sits at bit 2j of its half is u * 2^(2j-24) (the activation
+// was divided by 2^(2j) to match, see prescale); the offset is removed in
+// the epilogue.  E2M1: code times block scale, exactly (at most 6 significant
+// bits).
+template <int FMT>
+__device__ __forceinline__ half8_t b_operand(const RawBlock& r, int q, int st) {
+  if (FMT == MOE_W_INT4_ROW) {
+    const uint32_t d = r.d[q], e = d >> 8;
+    return __builtin_bit_cast(half8_t, u32x4{d & 0x000F000Fu, d & 0x00F000F0u, e & 0x000F000Fu, e & 0x00F000F0u});
+  } else if (FMT == MOE_W_INT8_ROW) {
+    const uint32_t d = r.d[q], f = r.f[q];
+    return __builtin_bit_cast(half8_t,
+                              u32x4{d & 0x00FF00FFu, (d >> 8) & 0x00FF00FFu, f & 0x00FF00FFu, (f >> 8) & 0x00FF00FFu});
+  } else if (FMT == MOE_W_INT2_ROW) {
+    const uint32_t e = st ? r.d[q] >> 8 : r.d[q];
+    return __builtin_bit_cast(half8_t, u32x4{e & 0x00030003u, e & 0x000C000Cu, e & 0x00300030u, e & 0x00C000C0u});
   } else {
-    uint32_t t0 = sc & 0xFF, t1 = sc & 0xFF, t2 = (sc >> 8) & 0xFF, t3 = (sc >> 8) & 0xFF;
-    transpose4(t0, t1, t2, t3);
-    b[0][0] = dequant_e2m1(d[0], e4m3_half2(t0));
-    b[0][1] = dequant_e2m1(d[1], e4m3_half2(t1));
-    b[0][2] = dequant_e2m1(d[2], e4m3_half2(t2));
-    b[0][3] = dequant_e2m1(d[3], e4m3_half2(t3));
+    return dequant_e2m1(r.d[q], e4m3_half2(r.s[q]));
   }
 }
 
 // A operand of MFMA step `st` for token row `r` of an LDS slice, matching
-// block_to_operands' columns for lane group g.
+// b_operand's columns for lane group g.
 template <int FMT>
 __device__ __forceinline__ half8_t a_operand(const _Float16* row, int g, int st) {
   if (FMT == MOE_W_INT8_ROW) {
@@ -235,23 +240,38 @@ __device__ __forceinline__ bool tile_token(const GemmArgs& a, const SlotEntry& s
 }
 
 // Grouped GEMM over one tile of BM tokens of one expert.  512 threads = 8
-// wavefronts; wavefront w owns the 64-row block rb = 8*group + w of each
-// of the NM matrices (gate and up for NM = 2, down for NM = 1) and all BM
-// tokens.  Per 32-column slice: each wavefront streams its NM weight blocks
-// (one 128-bit load per lane each) and decodes them into MFMA operands in
-// registers; the tile's activation rows (gathered by token) pass through a
-// double-buffered LDS slice shared by the eight wavefronts.
+// wavefronts; wavefront w owns the 64-row block rb = 8*group + w of each of
+// the NM matrices (gate and up for NM = 2, down for NM = 1) and all BM
+// tokens.  Per K-slice: each wavefront streams its NM weight blocks (one
+// 128-bit load per lane and chunk, DEPTH slices ahead) and decodes them into
+// B operands just before their MFMAs; the tile's activation rows (gathered
+// by token) pass through three LDS slices shared by the workgroup: slice c+2
+// is written and slice c+1's A operands are read while slice c is
+// multiplied, one barrier per slice.
 //   NM == 2: K = H, activations x, epilogue: row scales, SwiGLU -> h.
 //   NM == 1: K = I, activations h, epilogue: row scale, routing weight -> part.
-constexpr int kGemmWaves = 8;  // wavefronts per workgroup, 64 rows each
+// Integer formats accumulate sum x * u * 2^-24 over codes u = q + OFF; the
+// epilogue forms sum x q = 2^24 acc - OFF * sum x from the tile's per-token
+// activation sums.
+constexpr int kGemmWaves = 8;
 
-template <int FMT, int NM>
+template <int FMT, int NM, int DEPTH>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int nx) {
   typedef Slice<FMT> SL;
-  constexpr int SC = SL::SC, WPS = SL::WPS, XP = SL::XP;
-  __shared__ __attribute__((aligned(16))) _Float16 sx[2][BM][XP];
+  constexpr int NT = 64 * kGemmWaves;
+  constexpr int SC = SL::SC, WPS = SL::WPS, XP = SL::XP, STEPS = SL::STEPS;
+  constexpr int PH = SC * BM / NT;  // halves per thread and slice (every thread stages one piece)
+  constexpr int PPR = SC / PH;      // pieces per token row of a slice
+  static_assert(PH == 4 || PH == 8, "activation piece of 8 or 16 bytes");
+  static_assert(DEPTH % 2 == 0, "the activation ring slot is c % 2");
+  static_assert((128 / SC) % DEPTH == 0, "K is a multiple of 128, so DEPTH divides the slice count");
+  typedef Piece<PH> P;
+  // slice c+1's A operands are read during slice c, except for int2, whose
+  // 64-column slices need twice the A registers
+  constexpr bool kPrefetchA = STEPS == 1;
+  __shared__ __attribute__((aligned(16))) _Float16 sx[3][BM][XP];
   __shared__ int s_act[BM], s_out[BM];
-  __shared__ float s_w[BM];
+  __shared__ float s_w[BM], s_sum[BM];
   // XCD-aware order: workgroups are spread round-robin over the 8 XCDs, so
   // map block b to tile 8*(l/nx) + b%8 and row group l%nx with l = b/8: all
   // row groups of one token tile run on one XCD and share its L2 copy of the
@@ -276,14 +296,24 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   }
   __syncthreads();
   const uint16_t* act = (NM == 2) ? a.x : a.h;
-  const int nch = K / SC;  // slices
-  // this thread's 16-byte share of an activation slice: token tid/(SC/8),
-  // columns 8*(tid%(SC/8)) (threads past BM*SC/8 only compute)
-  constexpr int XQ = SC / 8;
-  const bool xload = tid < XQ * BM;
-  const int xm = (tid / XQ) & (BM - 1), xq = tid % XQ;
-  const int xrow = xload ? s_act[xm] : -1;
-  const uint16_t* xsrc = act + (size_t)(xrow < 0 ? 0 : xrow) * K + 8 * xq;
+  const int nch = K / SC;  // slices (at least 2: K >= 128)
+  // this thread's activation piece: token xm, columns PH*xq .. +PH-1 of a slice
+  const int xm = tid / PPR, xq = tid % PPR;
+  const int xrow = s_act[xm];
+  const bool xv = xrow >= 0;
+  const P* xsrc = reinterpret_cast<const P*>(act + (size_t)(xv ? xrow : 0) * K + PH * xq);  // row 0 stands in for padding
+  const int xoff = xm * XP + PH * xq;
+  float xsum = 0.f;
+  auto load_x = [&](int c) -> P { return xsrc[(size_t)c * PPR]; };
+  auto stage = [&](P v, _Float16* buf, bool live) {
+    if (!xv) v = P{};
+    if (SL::SUB) {
+      const float s = piece_sum<PH>(v);
+      xsum += live ? s : 0.f;
+      v = prescale<FMT, PH>(v);
+    }
+    *reinterpret_cast<P*>(buf + xoff) = v;
+  };
   // weights: lane's 16 bytes of block (rb, chunk c) of matrix m; a slice is
   // WPS chunks, nch * WPS chunks per row
   const guint4* wsrc;
@@ -298,12 +328,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   auto load_w = [&](int c, int m, int p) -> u32x4 {
     return __builtin_nontemporal_load(wsrc + ((size_t)(c * WPS + p) * NM + m) * 64);
   };
-  auto load_s = [&](int c, int m) -> uint32_t {
-    const uint8_t* p = ssrc + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3);
-    return (uint32_t)p[0] | ((uint32_t)p[1] << 8);
-  };
-  auto load_x = [&](int c) -> u32x4 {
-    return xrow < 0 ? u32x4{0, 0, 0, 0} : *reinterpret_cast<const u32x4*>(xsrc + SC * c);
+  auto load_s = [&](int c, int m) -> uint32_t {  // the two scale bytes of the slice, one 16-bit global load
+    typedef __attribute__((address_space(1))) const uint16_t gu16;
+    return *(gu16*)(ssrc + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3));
   };
 
   f32x4 acc[NM][4][4];  // [matrix][row group q][token group mt]
@@ -314,79 +341,137 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) acc[m][q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Weights stream through a ring of kDepth register slices (loads issued
-  // kDepth slices ahead); activations through a double-buffered LDS slice.
-  constexpr int kDepth = SL::kDepth;
-  u32x4 ring[kDepth][NM][WPS];
-  uint32_t sring[kDepth][NM];
-#pragma unroll
-  for (int j = 0; j < kDepth; ++j)
-#pragma unroll
-    for (int m = 0; m < NM; ++m) {
-      sring[j][m] = 0;
-      if (active && j < nch) {
-#pragma unroll
-        for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(j, m, p);
-        if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(j, m);
-      }
-    }
-  // activation slices: register ring kXDepth deep feeding the LDS double buffer
-  constexpr int kXDepth = 2;
-  static_assert(kDepth % kXDepth == 0, "xring slot j % kXDepth must hold slice c + 1");
-  u32x4 xring[kXDepth];
-#pragma unroll
-  for (int j = 0; j < kXDepth; ++j) xring[j] = (j + 1 < nch) ? load_x(j + 1) : u32x4{0, 0, 0, 0};
-  if (xload) *reinterpret_cast<u32x4*>(&sx[0][xm][8 * xq]) = load_x(0);
-  __syncthreads();
+  u32x4 ring[DEPTH][NM][WPS];
+  uint32_t sring[DEPTH][NM];
+  P xring[2];
+  half8_t av[STEPS][4];
   const int n = lane & 15, g = lane >> 4;
-  const DecMasks mk = dec_masks<FMT>();
-  for (int c0 = 0; c0 < nch; c0 += kDepth) {
+  // The loop body is straight-line code (loads past the last slice re-read
+  // it and go unused), so that the load counters stay exact across slices.
+  auto run = [&](auto ACTIVE, auto MTC) {
+    constexpr int MT = decltype(MTC)::value;  // 16-token groups of the tile that hold tokens
+    // prologue loads in the order of the loop's refills (activation slice
+    // j+2, then weight slice j), so that the load counters the loop waits on
+    // are the same on entry as in steady state
+    const P v0 = load_x(0), v1 = load_x(1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < kDepth; ++j) {
-      const int c = c0 + j;
-      if (c >= nch) break;
-      // slice c+1 sits in xring[j % kXDepth]; refill it with slice c+1+kXDepth
-      const u32x4 xn = xring[j % kXDepth];
-      if (c + 1 + kXDepth < nch) xring[j % kXDepth] = load_x(c + 1 + kXDepth);
-      if (active) {
-        u32x4 wv[NM][WPS];
-        uint32_t sv[NM];
-#pragma unroll
-        for (int m = 0; m < NM; ++m) {
-#pragma unroll
-          for (int p = 0; p < WPS; ++p) wv[m][p] = ring[j][m][p];
-          sv[m] = sring[j][m];
-          if (c + kDepth < nch) {
-#pragma unroll
-            for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(c + kDepth, m, p);
-            if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(c + kDepth, m);
-          }
-        }
-        half8_t av[SL::STEPS][4];
-#pragma unroll
-        for (int st = 0; st < SL::STEPS; ++st)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt) av[st][mt] = a_operand<FMT>(&sx[c & 1][16 * mt + n][0], g, st);
+    for (int j = 0; j < DEPTH; ++j) {
+      if (j < 2) xring[j] = load_x(j + 2 < nch ? j + 2 : nch - 1);
+      if (ACTIVE) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
-          half8_t b[SL::STEPS][4];
-          block_to_operands<FMT>(wv[m], sv[m], mk, b);
+          const int cj = j < nch ? j : nch - 1;
 #pragma unroll
-          for (int st = 0; st < SL::STEPS; ++st)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-              for (int mt = 0; mt < 4; ++mt)
-                acc[m][q][mt] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][mt], b[st][q], acc[m][q][mt], 0, 0, 0);
+          for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cj, m, p);
+          sring[j][m] = FMT == MOE_W_E2M1_B16 ? load_s(cj, m) : 0u;
         }
       }
-      if (xload && c + 1 < nch) *reinterpret_cast<u32x4*>(&sx[(c + 1) & 1][xm][8 * xq]) = xn;
-      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     }
+    stage(v0, &sx[0][0][0], true);
+    stage(v1, &sx[1][0][0], true);
+    __syncthreads();
+    if (kPrefetchA) {
+#pragma unroll
+      for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) av[st][mt] = a_operand<FMT>(&sx[0][16 * mt + n][0], g, st);
+    }
+    int b1 = 1, b2 = 2;  // LDS slices of c+1 and c+2
+    for (int c0 = 0; c0 < nch; c0 += DEPTH) {
+#pragma unroll
+      for (int j = 0; j < DEPTH; ++j) {
+        const int c = c0 + j;
+        // each ring slot is consumed (copied out) before it is refilled, so
+        // that the refill lands in the same registers
+        stage(xring[j & 1], &sx[b2][0][0], c + 2 < nch);
+        __builtin_amdgcn_sched_barrier(0);
+        xring[j & 1] = load_x(c + 4 < nch ? c + 4 : nch - 1);
+        half8_t avn[STEPS][4];
+        if (kPrefetchA) {
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) avn[st][mt] = a_operand<FMT>(&sx[b1][16 * mt + n][0], g, st);
+        } else {
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) av[st][mt] = a_operand<FMT>(&sx[b1 == 0 ? 2 : b1 - 1][16 * mt + n][0], g, st);
+        }
+        if (ACTIVE) {
+          const int cn = c + DEPTH < nch ? c + DEPTH : nch - 1;
+          auto refill = [&]() {
+#pragma unroll
+            for (int m = 0; m < NM; ++m) {
+#pragma unroll
+              for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cn, m, p);
+              if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(cn, m);
+            }
+          };
+          auto multiply = [&](const RawBlock& rw, int m) {
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const half8_t b = b_operand<FMT>(rw, q, st);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  acc[m][q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][mt], b, acc[m][q][mt], 0, 0, 0);
+              }
+          };
+          // transpose every matrix (which ends the slot's registers), refill
+          // the slot, then multiply
+          RawBlock rw[NM];
+#pragma unroll
+          for (int m = 0; m < NM; ++m) rw[m] = to_raw<FMT>(ring[j][m], sring[j][m]);
+          __builtin_amdgcn_sched_barrier(0);
+          refill();
+          // the loads above issue before the matrix work below
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int m = 0; m < NM; ++m) multiply(rw[m], m);
+          // the barrier below stays after the matrix work
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+        if (kPrefetchA) {
+#pragma unroll
+          for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) av[st][mt] = avn[st][mt];
+        }
+        b1 = b2;
+        b2 = b2 == 2 ? 0 : b2 + 1;
+      }
+    }
+  };
+  // the loop is specialised on the number of 16-token groups that hold
+  // tokens, so that a partly filled tile skips the matrix work of its empty
+  // groups (their accumulators stay zero; the epilogue skips padding tokens)
+  typedef std::true_type on;
+  const int ng = (min(se.n - m0, BM) + 15) >> 4;
+  if (!active)
+    run(std::false_type{}, std::integral_constant<int, 1>{});
+  else if (ng <= 1)
+    run(on{}, std::integral_constant<int, 1>{});
+  else if (ng == 2)
+    run(on{}, std::integral_constant<int, 2>{});
+  else if (ng == 3)
+    run(on{}, std::integral_constant<int, 3>{});
+  else
+    run(on{}, std::integral_constant<int, 4>{});
+  if (SL::SUB) {  // per-token activation sums: the PPR pieces of a token sit in adjacent lanes
+    float s = xsum;
+#pragma unroll
+    for (int o = 1; o < PPR; o <<= 1) s += __shfl_xor(s, o);
+    if (xq == 0) s_sum[xm] = s;
+    __syncthreads();
   }
   if (!active) return;
   // epilogue: lane (n, g) holds tokens 16 mt + 4 g + i of row 64 rb + 16 q + n
+  constexpr float kSub = 16777216.0f;  // 2^24
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = rb * 64 + 16 * q + n;
@@ -407,7 +492,13 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
           const int mm = 16 * mt + 4 * g + i;
           const int orow = s_out[mm];
           if (orow < 0) continue;
-          const float gv = acc[0][q][mt][i] * sgv, uv = acc[NM - 1][q][mt][i] * suv;
+          float ga = acc[0][q][mt][i], ua = acc[NM - 1][q][mt][i];
+          if (SL::SUB) {
+            const float off = SL::OFF * s_sum[mm];
+            ga = ga * kSub - off;
+            ua = ua * kSub - off;
+          }
+          const float gv = ga * sgv, uv = ua * suv;
           a.h[(size_t)orow * a.I + row] = __builtin_bit_cast(uint16_t, (_Float16)(silu(gv) * uv));
         }
     } else {
@@ -423,7 +514,9 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
           const int mm = 16 * mt + 4 * g + i;
           const int orow = s_out[mm];
           if (orow < 0) continue;
-          a.part[(size_t)orow * a.H + row] = s_w[mm] * (sd * acc[0][q][mt][i]);
+          float da = acc[0][q][mt][i];
+          if (SL::SUB) da = da * kSub - SL::OFF * s_sum[mm];
+          a.part[(size_t)orow * a.H + row] = s_w[mm] * (sd * da);
         }
     }
   }
@@ -473,11 +566,12 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
     launch_k(gu, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
     launch_k(dn, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
   };
+  // ring depth: 4 slices of 32 columns, 2 of 64 (int2) or of 2 chunks (int8)
   switch (d.wfmt) {
-    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2>, k_expert_gemm<MOE_W_INT4_ROW, 1>); break;
-    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2>, k_expert_gemm<MOE_W_INT8_ROW, 1>); break;
-    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1>); break;
-    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2>, k_expert_gemm<MOE_W_E2M1_B16, 1>); break;
+    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4>, k_expert_gemm<MOE_W_INT4_ROW, 1, 4>); break;
+    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2, 2>, k_expert_gemm<MOE_W_INT8_ROW, 1, 2>); break;
+    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2>); break;
+    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2>); break;
   }
   launch_k(k_combine, dim3((p.H + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
   return hipGetLastError();
