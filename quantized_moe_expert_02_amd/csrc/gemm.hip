@@ -522,16 +522,34 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   }
 }
 
-// y[t][c] = sum_j part[t*k + j][c] (slot order) + part[T*k + t][c].
+// y[t][c] = sum_j part[t*k + j][c] (slot order) + part[T*k + t][c].  A
+// thread owns 2 columns (measured faster than 1 or 4); a token's slot rows
+// and its shared row are requested before they are added (a slot dropped by
+// top-p has topk_idx < 0: its row is read but not added).
 __global__ __launch_bounds__(256) void k_combine(GemmArgs a) {
   const int t = blockIdx.y;
-  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int c = (blockIdx.x * 256 + threadIdx.x) * 2;
   if (c >= a.H) return;
-  float acc = 0.f;
-  for (int j = 0; j < a.k; ++j)
-    if (a.topk_idx[t * a.k + j] >= 0) acc += a.part[((size_t)t * a.k + j) * a.H + c];  // < 0: dropped by top-p
-  if (a.S) acc += a.part[((size_t)a.T * a.k + t) * a.H + c];
-  a.y[(size_t)t * a.H + c] = __builtin_bit_cast(uint16_t, (_Float16)acc);
+  uint32_t keep = 0;  // slots kept (k <= 32)
+  for (int j = 0; j < a.k; ++j) keep |= (uint32_t)(a.topk_idx[t * a.k + j] >= 0) << j;
+  const size_t row = a.H / 2;  // float2 per partial row
+  const float2* pt = reinterpret_cast<const float2*>(a.part + (size_t)t * a.k * a.H + c);
+  const float2 sh = a.S ? reinterpret_cast<const float2*>(a.part + ((size_t)a.T * a.k + t) * a.H + c)[0] : float2{0.f, 0.f};
+  float2 acc = {0.f, 0.f};
+  for (int j0 = 0; j0 < a.k; j0 += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = pt[(size_t)min(j0 + i, a.k - 1) * row];
+    __builtin_amdgcn_sched_barrier(0);  // all eight loads in flight before the first add
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const bool use = j0 + i < a.k && ((keep >> (j0 + i)) & 1u);
+      const float2 s = acc + v[i];
+      acc = use ? s : acc;
+    }
+  }
+  acc += sh;
+  *reinterpret_cast<uint32_t*>(a.y + (size_t)t * a.H + c) = __builtin_bit_cast(uint32_t, half2_t{(_Float16)acc.x, (_Float16)acc.y});
 }
 
 }  // namespace
@@ -573,7 +591,7 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
     case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2>); break;
     default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2>); break;
   }
-  launch_k(k_combine, dim3((p.H + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
+  launch_k(k_combine, dim3((p.H / 2 + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
   return hipGetLastError();
 }
 

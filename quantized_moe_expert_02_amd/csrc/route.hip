@@ -162,82 +162,82 @@ __global__ __launch_bounds__(256) void k_union_count(RouteArgs a) {
   for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.ucnt[(size_t)c * a.E + e] = __popc(s_mask[e]);
 }
 
-// Pass 2 (one block of 1024 threads): per-expert prefix over chunks, then
-// the prefix over experts gives the union arrays and each (chunk, expert)
-// base offset.
-__global__ __launch_bounds__(1024) void k_union_scan(RouteArgs a) {
-  __shared__ int s_tot[kMaxExperts];
-  __shared__ int s_pre[kMaxExperts];
-  __shared__ int s_prs[kMaxExperts];
-  __shared__ const uint8_t* s_ptr[kMaxExperts];
-  const int tid = threadIdx.x;
-  if (a.slots)
-    for (int e = tid; e < a.E; e += blockDim.x) s_ptr[e] = (const uint8_t*)a.experts[e];
-  // pass 1: per-expert totals (16 independent loads in flight per thread)
-  for (int e = tid; e < a.E; e += blockDim.x) {
-    int run = 0;
+// Exclusive prefix of v over a block of kScanThreads threads (every thread
+// calls it), and the block total.  s_wave: kScanThreads / 64 ints of LDS.
+constexpr int kScanThreads = 1024;
+__device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int inc = wave_inclusive_scan(v);
+  if (lane == 63) s_wave[w] = inc;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kScanThreads / 64; ++i) {
+    const int s = s_wave[i];
+    base += i < w ? s : 0;
+    tot += s;
+  }
+  total = tot;
+  return base + inc - v;
+}
+
+// Pass 2 (one block, thread e = expert e): per-expert totals over the
+// chunks; block-wide prefix sums give each expert's pair offset, its place
+// in the union and its first grouped-GEMM tile, so every thread writes its
+// own expert's entries; then each (chunk, expert) base offset.
+__global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
+  __shared__ int s_wave[3][kScanThreads / 64];
+  static_assert(kMaxExperts <= kScanThreads, "one thread per expert");
+  const int e = threadIdx.x;
+  int tot = 0;  // pairs of expert e (16 independent loads in flight)
+  if (e < a.E)
     for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
       int v[16];
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = (c0 + i < a.n_chunks) ? a.ucnt[(size_t)(c0 + i) * a.E + e] : 0;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) run += v[i];
+      for (int i = 0; i < 16; ++i) tot += v[i];
     }
-    s_tot[e] = run;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int off = 0, nu = 0;
-    for (int e = 0; e < a.E; ++e) {
-      s_pre[e] = off;
-      s_prs[e] = nu;
-      if (s_tot[e] > 0) {
-        a.uniq_ids[nu] = e;
-        a.uniq_off[nu] = off;
-        if (a.slots) {
-          SlotEntry sl;
-          sl.base = s_ptr[e];
-          sl.n = s_tot[e];
-          sl.p0 = off;
-          a.slots[a.S + nu] = sl;
-        }
-        ++nu;
+  const int used = tot > 0 ? 1 : 0;
+  const int ntl = (tot + kPrefillTileRows - 1) / kPrefillTileRows;
+  int off_all, nu_all, nt_all;
+  const int off = block_exclusive_scan(tot, s_wave[0], off_all);
+  const int u = block_exclusive_scan(used, s_wave[1], nu_all);
+  const int tb = block_exclusive_scan(ntl, s_wave[2], nt_all);
+  // grouped-GEMM tiles: the shared expert's first, then the union in order
+  const int nsh = a.S ? (a.T + kPrefillTileRows - 1) / kPrefillTileRows : 0;
+  if (used) {
+    a.uniq_ids[u] = e;
+    a.uniq_off[u] = off;
+    if (a.slots) {
+      SlotEntry sl;
+      sl.base = (const uint8_t*)a.experts[e];
+      sl.n = tot;
+      sl.p0 = off;
+      a.slots[a.S + u] = sl;
+    }
+    if (a.tiles)
+      for (int i = 0; i < ntl; ++i) {
+        a.tiles[2 * (nsh + tb + i)] = a.S + u;
+        a.tiles[2 * (nsh + tb + i) + 1] = i * kPrefillTileRows;
       }
-      off += s_tot[e];
+  }
+  if (a.tiles)
+    for (int i = e; i < nsh; i += kScanThreads) {
+      a.tiles[2 * i] = 0;
+      a.tiles[2 * i + 1] = i * kPrefillTileRows;
     }
-    *a.n_unique = nu;
-    a.uniq_off[nu] = off;
-    s_prs[0] = nu;
+  if (e == 0) {
+    *a.n_unique = nu_all;
+    a.uniq_off[nu_all] = off_all;
     if (a.slots && a.S) write_slot(a, 0, -1, a.T, -1);
-    if (a.tiles) {
-      // grouped-GEMM tiles: shared expert first, then the union in order
-      int nt = 0;
-      if (a.S)
-        for (int m0 = 0; m0 < a.T; m0 += kPrefillTileRows) {
-          a.tiles[2 * nt] = 0;
-          a.tiles[2 * nt + 1] = m0;
-          ++nt;
-        }
-      int u = 0;
-      for (int e = 0; e < a.E; ++e) {
-        if (s_tot[e] == 0) continue;
-        for (int m0 = 0; m0 < s_tot[e]; m0 += kPrefillTileRows) {
-          a.tiles[2 * nt] = a.S + u;
-          a.tiles[2 * nt + 1] = m0;
-          ++nt;
-        }
-        ++u;
-      }
-      *a.n_tiles = nt;
-    }
+    if (a.tiles) *a.n_tiles = nsh + nt_all;
   }
-  __syncthreads();
   if (a.slots)
-    for (int sl = a.S + s_prs[0] + tid; sl < a.slots_max; sl += blockDim.x) write_slot(a, sl, 0, 0, 0);
-  __syncthreads();
-  // pass 2: base of each (chunk, expert) = expert base + earlier chunks' counts
-  for (int e = tid; e < a.E; e += blockDim.x) {
-    int run = s_pre[e];
+    for (int sl = a.S + nu_all + e; sl < a.slots_max; sl += kScanThreads) write_slot(a, sl, 0, 0, 0);
+  // base of each (chunk, expert) = expert base + earlier chunks' counts
+  if (e < a.E) {
+    int run = off;
     for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
       int v[16];
 #pragma unroll
@@ -317,7 +317,7 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
   }
   hipLaunchKernelGGL(k_topk, dim3((p.T + 3) / 4), dim3(256), 0, s, a);
   hipLaunchKernelGGL(k_union_count, dim3(a.n_chunks), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL(k_union_scan, dim3(1), dim3(kScanThreads), 0, s, a);
   launch_k(k_union_scatter, dim3(a.n_chunks), dim3(256), s, nullptr, ev_stop, a);
   return hipGetLastError();
 }
