@@ -89,7 +89,7 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   const size_t Tk = (size_t)T * q.k;
   const size_t cap = std::max<size_t>(1, std::min<size_t>(q.E, Tk));
   // z plus the K-split partial logits of the batched router
-  q.z_off = off; off = up256(off + (size_t)T * q.E * 8 * 5);
+  q.z_off = off; off = up256(off + (size_t)T * q.E * 8 * kZPlanes);
   q.idx_off = off; off = up256(off + Tk * 4);
   q.w_off = off; off = up256(off + Tk * 4);
   q.nu_off = off; off = up256(off + 4);

@@ -83,6 +83,7 @@ constexpr int kDecodeMaxTokens = 16;   // GEMV path for T <= this
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
 constexpr int kPrefillTileRows = 64;   // tokens per grouped-GEMM tile
+constexpr int kZPlanes = 9;            // fp64 logit planes: z, then up to 8 K-split partials
 
 // Upper bound on grouped-GEMM tiles (slot, first token) for T tokens.
 inline int prefill_max_tiles(int T, int k, int E, int S) {

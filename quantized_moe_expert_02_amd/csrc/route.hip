@@ -56,74 +56,123 @@ __device__ __forceinline__ void write_slot(const RouteArgs& a, int slot, int exp
 
 // ---- large batches -------------------------------------------------------
 
-// fp64 logits for large batches: block (tile of 64 tokens, tile of 64
+// fp64 logits for large batches on the matrix cores (v_mfma_f64_16x16x4_f64,
+// D = A·B + C with A 16x4, B 4x16, D 16x16 fp64): block (128 tokens, 64
 // experts, K-split ks) accumulates columns [ks*Kc, (ks+1)*Kc) into a partial
-// sum per (token, expert); partials are added in K-split order by k_topk.
-// Each thread owns 4 tokens x 4 experts; operands are staged in LDS as fp32
-// (binary16 -> fp32 is exact) and widened to fp64 for the FMA.
-constexpr int LT = 64, LE = 64, LK = 32;
-constexpr int kLogitSplit = 4;
+// sum per (token, expert); partials are added in K-split order by
+// k_logits_sum.  Wavefront w owns tokens 32w .. 32w+31 (two 16-token groups)
+// x the 64 experts (four 16-expert groups).  K runs in chunks of 16 columns;
+// MFMA step s of a chunk gives lane group g column 4g + s, so a lane loads 4
+// consecutive binary16 activations and 4 consecutive fp32 weights per group
+// and chunk, and widens them to fp64 (exact).  Lane layout: A[i][k] and
+// B[k][j] in lane i (or j) + 16k; D[i][j] in lane j + 16*(i % 4), element
+// i / 4 (checked on the hardware).
+constexpr int kLogitSplit = 8;
+constexpr int LGT = 128, LGE = 64;
+static_assert(kLogitSplit + 1 <= kZPlanes, "z holds the logits and the K-split partials");
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// A copy the compiler cannot fold (ends the life of a loaded register before
+// its refill, so that the refill reuses it).
+__device__ __forceinline__ uint32_t fresh_u32(uint32_t v) {
+  uint32_t r;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(v));
+  return r;
+}
+
 __global__ __launch_bounds__(256) void k_logits_tiled(RouteArgs a) {
-  __shared__ __attribute__((aligned(16))) float sx[LK][LT];
-  __shared__ __attribute__((aligned(16))) float sw[LK][LE];
-  const int t0 = blockIdx.x * LT, e0 = blockIdx.y * LE;
-  const int kc = a.H / kLogitSplit;
-  const int kbeg = blockIdx.z * kc;
-  const int tid = threadIdx.x;
-  const int tt = (tid & 15) * 4;  // token offset in tile
-  const int te = (tid >> 4) * 4;  // expert offset in tile
-  double acc[4][4] = {};
-  // staging: thread loads 8 consecutive columns of one row (x: 64 rows; w: 64 rows)
-  const int sr = tid >> 2, sc8 = (tid & 3) * 8;
-  for (int k0 = kbeg; k0 < kbeg + kc; k0 += LK) {
-    {
-      const int t = t0 + sr;
-      float v[8] = {};
-      if (t < a.T) {
-        const uint4 xv = *reinterpret_cast<const uint4*>(a.x + (size_t)t * a.H + k0 + sc8);
-        const uint32_t w4[4] = {xv.x, xv.y, xv.z, xv.w};
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int n = lane & 15, g = lane >> 4;
+  const int t0 = blockIdx.x * LGT + wave * 32, e0 = blockIdx.y * LGE;
+  const int kc = a.H / kLogitSplit;  // a multiple of 16 (H is a multiple of 128)
+  const int kb = blockIdx.z * kc + 4 * g;
+  // this lane's rows (clamped into range; results outside are not stored)
+  const uint2* xr[2];
+  const float4* wr[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[i] & 0xFFFF));
-          v[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w4[i] >> 16));
-        }
-      }
+  for (int mg = 0; mg < 2; ++mg) {
+    const int tt = min(t0 + 16 * mg + n, a.T - 1);
+    xr[mg] = reinterpret_cast<const uint2*>(a.x + (size_t)tt * a.H + kb);
+  }
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sx[sc8 + i][sr] = v[i];
-      const int e = e0 + sr;
-      float u[8] = {};
-      if (e < a.E) {
-        const float4 w0 = *reinterpret_cast<const float4*>(a.Wr + (size_t)e * a.H + k0 + sc8);
-        const float4 w1 = *reinterpret_cast<const float4*>(a.Wr + (size_t)e * a.H + k0 + sc8 + 4);
-        u[0] = w0.x; u[1] = w0.y; u[2] = w0.z; u[3] = w0.w;
-        u[4] = w1.x; u[5] = w1.y; u[6] = w1.z; u[7] = w1.w;
-      }
+  for (int ng = 0; ng < 4; ++ng) {
+    const int ee = min(e0 + 16 * ng + n, a.E - 1);
+    wr[ng] = reinterpret_cast<const float4*>(a.Wr + (size_t)ee * a.H + kb);
+  }
+  const int nch = kc / 16;
+  f64x4 acc[2][4];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) sw[sc8 + i][sr] = u[i];
+  for (int mg = 0; mg < 2; ++mg)
+#pragma unroll
+    for (int ng = 0; ng < 4; ++ng) acc[mg][ng] = f64x4{0.0, 0.0, 0.0, 0.0};
+  // two chunks in flight; chunk c of a row is 4 uint2 / 4 float4 further on
+  uint2 xv[2][2];
+  float4 wv[2][4];
+  auto load = [&](int slot, int c) {
+#pragma unroll
+    for (int mg = 0; mg < 2; ++mg) xv[slot][mg] = xr[mg][4 * c];
+#pragma unroll
+    for (int ng = 0; ng < 4; ++ng) wv[slot][ng] = wr[ng][4 * c];
+  };
+  // widen slot `slot` to fp64 operands (copies first, so the slot can be refilled)
+  auto widen = [&](int slot, double (&xa)[2][4], double (&wb)[4][4]) {
+#pragma unroll
+    for (int mg = 0; mg < 2; ++mg) {
+      const uint32_t lo = fresh_u32(xv[slot][mg].x), hi = fresh_u32(xv[slot][mg].y);
+      xa[mg][0] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(lo & 0xFFFF));
+      xa[mg][1] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(lo >> 16));
+      xa[mg][2] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(hi & 0xFFFF));
+      xa[mg][3] = (double)(float)__builtin_bit_cast(_Float16, (uint16_t)(hi >> 16));
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < LK; ++c) {
-      const float4 xv = *reinterpret_cast<const float4*>(&sx[c][tt]);
-      const float4 wv = *reinterpret_cast<const float4*>(&sw[c][te]);
-      const double xd[4] = {xv.x, xv.y, xv.z, xv.w};
-      const double wd[4] = {wv.x, wv.y, wv.z, wv.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fma(xd[i], wd[j], acc[i][j]);
+    for (int ng = 0; ng < 4; ++ng) {
+      wb[ng][0] = (double)__builtin_bit_cast(float, fresh_u32(__builtin_bit_cast(uint32_t, wv[slot][ng].x)));
+      wb[ng][1] = (double)__builtin_bit_cast(float, fresh_u32(__builtin_bit_cast(uint32_t, wv[slot][ng].y)));
+      wb[ng][2] = (double)__builtin_bit_cast(float, fresh_u32(__builtin_bit_cast(uint32_t, wv[slot][ng].z)));
+      wb[ng][3] = (double)__builtin_bit_cast(float, fresh_u32(__builtin_bit_cast(uint32_t, wv[slot][ng].w)));
     }
-    __syncthreads();
+  };
+  auto multiply = [&](const double (&xa)[2][4], const double (&wb)[4][4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int mg = 0; mg < 2; ++mg)
+#pragma unroll
+        for (int ng = 0; ng < 4; ++ng)
+          acc[mg][ng] = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[mg][s], wb[ng][s], acc[mg][ng], 0, 0, 0);
+  };
+  load(0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  load(1, nch > 1 ? 1 : 0);
+  __builtin_amdgcn_sched_barrier(0);
+  const int nfull = nch & ~1;  // whole pairs; an odd last chunk waits in slot 0
+  for (int c0 = 0; c0 < nfull; c0 += 2) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      double xa[2][4], wb[4][4];
+      widen(j, xa, wb);
+      __builtin_amdgcn_sched_barrier(0);
+      const int cn = c0 + j + 2;
+      load(j, cn < nch ? cn : nch - 1);  // past the end: re-read the last chunk, unused
+      __builtin_amdgcn_sched_barrier(0);
+      multiply(xa, wb);
+    }
+  }
+  if (nch & 1) {
+    double xa[2][4], wb[4][4];
+    widen(0, xa, wb);
+    multiply(xa, wb);
   }
   double* zp = a.z + (size_t)blockIdx.z * a.T * a.E;
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + tt + i;
-    if (t >= a.T) continue;
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + te + j;
-      if (e < a.E) zp[(size_t)t * a.E + e] = acc[i][j];
-    }
-  }
+#pragma unroll
+  for (int mg = 0; mg < 2; ++mg)
+#pragma unroll
+    for (int ng = 0; ng < 4; ++ng)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tt = t0 + 16 * mg + 4 * r + g, ee = e0 + 16 * ng + n;
+        if (tt < a.T && ee < a.E) zp[(size_t)tt * a.E + ee] = acc[mg][ng][r];
+      }
 }
 
 // Adds the K-split partial logits (in split order) and the bias: z[t][e].
@@ -310,7 +359,7 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
   {
     RouteArgs b = a;
     b.z = r.z + (size_t)p.T * p.E;  // K-split partials live after z
-    launch_k(k_logits_tiled, dim3((p.T + LT - 1) / LT, (p.E + LE - 1) / LE, kLogitSplit), dim3(256), s, ev_start,
+    launch_k(k_logits_tiled, dim3((p.T + LGT - 1) / LGT, (p.E + LGE - 1) / LGE, kLogitSplit), dim3(256), s, ev_start,
              nullptr, b);
     const size_t n = (size_t)p.T * p.E;
     hipLaunchKernelGGL(k_logits_sum, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, a);
