@@ -253,6 +253,57 @@ def test_forward_prefill_matches_oracle(name, dims, T):
     assert_close(y, y_ref, name)
 
 
+@pytest.mark.parametrize("wfmt", [synth.INT4_ROW, synth.E2M1_B16, synth.INT8_ROW, synth.INT2_ROW])
+@pytest.mark.parametrize("T", [20, 40, 70, 129])
+def test_prefill_concentrated_routing(wfmt, T):
+    """Every token routes to the same two experts (zero router weights, a bias
+    on experts 3 and 5), so the union is two experts of T tokens each plus the
+    shared expert: the grouped GEMM runs tiles with 1 to 4 filled 16-token
+    groups (T = 20: 2; 40: 3; 70: 4 and 1; 129: 4, 4 and 1) in every weight
+    format."""
+    dims = synth.Dims(256, 128, 8, 2, 1, wfmt)
+    _log("prefill concentrated", dims, T)
+    layer = synth.make_layer(dims, ("conc", wfmt))
+    layer.router_w = torch.zeros_like(layer.router_w)
+    bias = torch.zeros(dims.n_experts, dtype=torch.float32)
+    bias[3], bias[5] = 2.0, 1.0
+    layer.router_b = bias
+    x = synth.make_tokens(dims, T, ("conc", wfmt, T))
+    r = oracle_route(layer, x)
+    assert (r.topk_idx == np.array([3, 5])).all()
+    y_ref = oracle.forward(layer, x)
+    pl = moe.PackedLayer.from_layer(layer)
+    ti = torch.empty((T, dims.top_k), dtype=torch.int32, device=DEV)
+    y = moe.moe_w4a16_forward(pl, x.to(DEV), topk_idx=ti)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
+    assert_close(y, y_ref, f"concentrated wfmt={wfmt} T={T}")
+
+
+def test_prefill_max_experts():
+    """1024 experts (the largest E), top-8, 300 tokens: the batched router
+    (fp64 logits in 128-token x 64-expert blocks) and the union's block-wide
+    scan, which gives every wavefront of its workgroup experts to place;
+    routing for every token and the layer output against the oracle."""
+    dims = synth.Dims(256, 128, 1024, 8, 1, synth.INT4_ROW)
+    T = 300
+    _log("prefill max experts", dims, T)
+    layer = synth.make_layer(dims, "emax")
+    x = synth.make_tokens(dims, T, "emax")
+    r = oracle_route(layer, x)
+    assert min_topk_gap(r, dims.top_k) > 1e-9
+    assert len(r.uniq_ids) > 900  # the union spans most experts
+    y_ref = oracle.forward(layer, x)
+    pl = moe.PackedLayer.from_layer(layer)
+    ti = torch.empty((T, dims.top_k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((T, dims.top_k), dtype=torch.float32, device=DEV)
+    y = moe.moe_w4a16_forward(pl, x.to(DEV), topk_idx=ti, topk_w=tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
+    np.testing.assert_allclose(tw.cpu().numpy(), r.topk_w, rtol=1e-6)
+    assert_close(y, y_ref, "emax")
+
+
 def test_prefill_full_size_sampled():
     """2048 tokens through the full decode-size layer with a Zipf-skewed router
     bias: routing checked for every token, outputs on a seeded sample."""
