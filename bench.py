@@ -478,7 +478,8 @@ def main():
     if not args.no_secondary:
         for name, L, steps in (("decode_b8", 8, 128), ("decode_b1_topp", 8, 512), ("e2m1_b1", 32, 512),
                                ("e2m1_b4", 32, 256), ("int8_b1", 8, 512), ("int2_b1", 8, 512),
-                               ("int2_b8", 8, 128), ("prefill_2048", 2, 8)):
+                               ("int2_b8", 8, 128), ("prefill_2048", 2, 8),
+                               ("prefill_2048_uniform", 2, 8)):
             try:
                 c2, r2, _ = run_workload(name, L, steps, 32, stage_reps=2)
                 secondary.append(r2)
