@@ -100,7 +100,8 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.ucnt_off = off; off = up256(off + nch * q.E * 4);
   q.ubase_off = off; off = up256(off + nch * q.E * 4);
   q.tiles_off = off; off = up256(off + (size_t)prefill_max_tiles(T, q.k, q.E, q.S) * 8);
-  q.ntiles_off = off; off = up256(off + 4);
+  q.tiles_dn_off = off; off = up256(off + (size_t)prefill_max_tiles(T, q.k, q.E, q.S, kDownTileRows) * 8);
+  q.ntiles_off = off; off = up256(off + 8);
   q.slots_off = off; off = up256(off + (size_t)q.slots_max * sizeof(SlotEntry));
   q.h_off = off; off = up256(off + (size_t)q.rows_total * q.I * 2);
   if (q.decode) {
@@ -136,6 +137,7 @@ Route route_ptrs(const Plan& p, void* ws) {
   r.ubase = (int32_t*)(b + p.ubase_off);
   r.slots = (SlotEntry*)(b + p.slots_off);
   r.tiles = (int32_t*)(b + p.tiles_off);
+  r.tiles_dn = (int32_t*)(b + p.tiles_dn_off);
   r.n_tiles = (int32_t*)(b + p.ntiles_off);
   r.counter = (uint32_t*)ws + p.c_route;
   return r;

@@ -82,14 +82,15 @@ inline Layout layout_of(const moe_dims_t& d) {
 constexpr int kDecodeMaxTokens = 16;   // GEMV path for T <= this
 constexpr int kMaxTopK = 32;
 constexpr int kMaxExperts = 1024;
-constexpr int kPrefillTileRows = 64;   // tokens per grouped-GEMM tile
+constexpr int kPrefillTileRows = 64;   // tokens per gate/up grouped-GEMM tile
+constexpr int kDownTileRows = 128;     // tokens per down grouped-GEMM tile
 constexpr int kZPlanes = 9;            // fp64 logit planes: z, then up to 8 K-split partials
 
-// Upper bound on grouped-GEMM tiles (slot, first token) for T tokens.
-inline int prefill_max_tiles(int T, int k, int E, int S) {
+// Upper bound on grouped-GEMM tiles (slot, first token) of B tokens for T
+// tokens.
+inline int prefill_max_tiles(int T, int k, int E, int S, int B = kPrefillTileRows) {
   const long P = (long)T * k;
   const long U = P < E ? P : E;
-  const long B = kPrefillTileRows;
   return (int)((S ? (T + B - 1) / B : 0) + (P + B - 1) / B + U);
 }
 
@@ -104,7 +105,7 @@ struct Plan {
   size_t sync_bytes;
   // byte offsets
   size_t z_off, idx_off, w_off, nu_off, ids_off, off_off, pairs_off;
-  size_t ucnt_off, ubase_off, tiles_off, ntiles_off, slots_off;
+  size_t ucnt_off, ubase_off, tiles_off, tiles_dn_off, ntiles_off, slots_off;
   size_t h_off, p_gu_off, p_dn_off;
   size_t total;
 };
@@ -132,8 +133,9 @@ struct Route {
   int32_t* ucnt;    // union: per-chunk counts
   int32_t* ubase;   // union: per-chunk bases
   SlotEntry* slots; // [slots_max]
-  int32_t* tiles;   // [max tiles][2]: (slot, first token) of each grouped-GEMM tile
-  int32_t* n_tiles; // [1]
+  int32_t* tiles;    // [max tiles][2]: (slot, first token) of each gate/up tile (kPrefillTileRows tokens)
+  int32_t* tiles_dn; // the same for down tiles (kDownTileRows tokens)
+  int32_t* n_tiles;  // [2]: gate/up tiles, down tiles
   uint32_t* counter;
 };
 

@@ -21,8 +21,9 @@
 //
 //   k_expert_gemm<.., 2, ..>:  tile = 64 tokens of one expert x 512 gate rows
 //                              + 512 up rows -> h (binary16, one row per pair)
-//   k_expert_gemm<.., 1, ..>:  tile = 64 tokens x 512 down rows -> per-pair
-//                              fp32 outputs, times the routing weight
+//   k_expert_gemm<.., 1, ..>:  tile = 128 tokens (int2: 64) x 512 down rows
+//                              -> per-pair fp32 outputs, times the routing
+//                              weight
 //   k_combine:  y[t] = sum over slots j (in slot order) + shared -> binary16
 #include <type_traits>
 
@@ -36,8 +37,6 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(1))) const u32x4 guint4;
-
-constexpr int BM = kPrefillTileRows;  // tokens per tile
 
 // Per-format shape of one K-slice of the main loop: SC columns, WPS 16-byte
 // chunks of the packed layout per lane, row block and matrix, SC / 32 MFMA
@@ -56,8 +55,9 @@ struct Slice {
 struct GemmArgs {
   const SlotEntry* slots;
   const int32_t* pairs;
-  const int32_t* tiles;      // [tile] = (slot, m0) pairs
-  const int32_t* n_tiles;    // [1]
+  const int32_t* tiles;      // gate/up tiles: [tile] = (slot, m0) pairs
+  const int32_t* tiles_dn;   // down tiles
+  const int32_t* n_tiles;    // [2]: gate/up tiles, down tiles
   const float* topk_w;
   const int32_t* topk_idx;
   const uint16_t* x;         // [T][H]
@@ -106,7 +106,7 @@ __device__ __forceinline__ void transpose4(uint32_t& d0, uint32_t& d1, uint32_t&
 }
 
 // An activation piece: PH consecutive binary16 values of one token row
-// (PH = 4 or 8, starting at a multiple of PH), staged by one thread.
+// (PH = 8 or 16, starting at a multiple of PH), staged by one thread.
 template <int PH>
 struct Piece {
   uint32_t w[PH / 2];
@@ -115,8 +115,9 @@ struct Piece {
 // Binary16 factors that put the activations of a piece on the scale of the
 // subnormal weight decode below: the column at position j of an 8-column
 // group decodes to u * 2^-24 * class(j), so its activation is divided by
-// class(j) (exactly, unless it becomes subnormal).  int4: classes 1, 1, 16,
-// 16 repeating every four columns; int2: 1, 1, 4, 4, 16, 16, 64, 64.
+// class(j) (exactly, unless it becomes subnormal).  Pair k of a piece (PH
+// halves, starting at a multiple of 8 for int2): int4 class 16 for odd k;
+// int2 class 4^(k % 4).
 template <int FMT, int PH>
 __device__ __forceinline__ Piece<PH> prescale(Piece<PH> v) {
   auto mul = [](uint32_t p, float f) {
@@ -126,10 +127,10 @@ __device__ __forceinline__ Piece<PH> prescale(Piece<PH> v) {
 #pragma unroll
     for (int k = 1; k < PH / 2; k += 2) v.w[k] = mul(v.w[k], 1.0f / 16);
   } else if (FMT == MOE_W_INT2_ROW) {
-    static_assert(FMT != MOE_W_INT2_ROW || PH == 8, "int2 pieces are whole 8-column groups");
-    v.w[1] = mul(v.w[1], 1.0f / 4);
-    v.w[PH / 2 - 2] = mul(v.w[PH / 2 - 2], 1.0f / 16);
-    v.w[PH / 2 - 1] = mul(v.w[PH / 2 - 1], 1.0f / 64);
+    static_assert(FMT != MOE_W_INT2_ROW || PH % 8 == 0, "int2 pieces are whole 8-column groups");
+#pragma unroll
+    for (int k = 0; k < PH / 2; ++k)
+      if (k % 4) v.w[k] = mul(v.w[k], k % 4 == 1 ? 1.0f / 4 : k % 4 == 2 ? 1.0f / 16 : 1.0f / 64);
   }
   return v;
 }
@@ -239,55 +240,62 @@ __device__ __forceinline__ bool tile_token(const GemmArgs& a, const SlotEntry& s
   return true;
 }
 
-// Grouped GEMM over one tile of BM tokens of one expert.  512 threads = 8
-// wavefronts; wavefront w owns the 64-row block rb = 8*group + w of each of
-// the NM matrices (gate and up for NM = 2, down for NM = 1) and all BM
-// tokens.  Per K-slice: each wavefront streams its NM weight blocks (one
-// 128-bit load per lane and chunk, DEPTH slices ahead) and decodes them into
-// B operands just before their MFMAs; the tile's activation rows (gathered
-// by token) pass through three LDS slices shared by the workgroup: slice c+2
-// is written and slice c+1's A operands are read while slice c is
-// multiplied, one barrier per slice.
-//   NM == 2: K = H, activations x, epilogue: row scales, SwiGLU -> h.
-//   NM == 1: K = I, activations h, epilogue: row scale, routing weight -> part.
-// Integer formats accumulate sum x * u * 2^-24 over codes u = q + OFF; the
-// epilogue forms sum x q = 2^24 acc - OFF * sum x from the tile's per-token
-// activation sums.
+// Grouped GEMM over the tokens of one expert.  512 threads = 8 wavefronts;
+// wavefront w owns the 64-row block rb = 8*group + w of each of the NM
+// matrices and all BT tokens of its tile:
+//   NM == 2 (gate and up, K = H, activations x): BT = 64, one half of a
+//     128-token tile; epilogue: row scales, SwiGLU -> h.
+//   NM == 1 (down, K = I, activations h): BT = 128; epilogue: row scale,
+//     routing weight -> part.
+// (accumulators: NM x 64 rows x BT tokens = 128 per lane either way.)  Per
+// K-slice: each wavefront streams its NM weight blocks (one 128-bit load per
+// lane and chunk, DEPTH slices ahead) and decodes them into B operands just
+// before their MFMAs; the tile's activation rows (gathered by token) pass
+// through three LDS slices shared by the workgroup: slice c+2 is written and
+// slice c+1's A operands are read while slice c is multiplied, one barrier
+// per slice.  Integer formats accumulate sum x * u * 2^-24 over codes u = q +
+// OFF; the epilogue forms sum x q = 2^24 acc - OFF * sum x from the tile's
+// per-token activation sums.
 constexpr int kGemmWaves = 8;
 
 template <int FMT, int NM, int DEPTH>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int nx) {
   typedef Slice<FMT> SL;
+  // tokens per tile: 64 for gate/up (two matrices' accumulators) and for
+  // int2 (two K-steps of A operands), else 128
+  constexpr int BT = (NM == 2 || Slice<FMT>::STEPS == 2) ? kPrefillTileRows : kDownTileRows;
+  constexpr int GMAX = BT / 16;              // 16-token groups per tile
   constexpr int NT = 64 * kGemmWaves;
   constexpr int SC = SL::SC, WPS = SL::WPS, XP = SL::XP, STEPS = SL::STEPS;
-  constexpr int PH = SC * BM / NT;  // halves per thread and slice (every thread stages one piece)
+  constexpr int PH = SC * BT / NT;  // halves per thread and slice (every thread stages one piece)
   constexpr int PPR = SC / PH;      // pieces per token row of a slice
-  static_assert(PH == 4 || PH == 8, "activation piece of 8 or 16 bytes");
-  static_assert(DEPTH % 2 == 0, "the activation ring slot is c % 2");
+  static_assert(PH == 4 || PH == 8 || PH == 16, "activation piece of 8, 16 or 32 bytes");
+  // activation slices wait XR slices in registers before they are staged
+  // (one for 32-byte pieces, whose slices carry twice the matrix work)
+  constexpr int XR = PH == 16 ? 1 : 2;
+  static_assert(DEPTH % XR == 0, "the activation ring slot is c % XR");
   static_assert((128 / SC) % DEPTH == 0, "K is a multiple of 128, so DEPTH divides the slice count");
   typedef Piece<PH> P;
-  // slice c+1's A operands are read during slice c, except for int2, whose
-  // 64-column slices need twice the A registers
-  constexpr bool kPrefetchA = STEPS == 1;
-  __shared__ __attribute__((aligned(16))) _Float16 sx[3][BM][XP];
-  __shared__ int s_act[BM], s_out[BM];
-  __shared__ float s_w[BM], s_sum[BM];
+  __shared__ __attribute__((aligned(16))) _Float16 sx[3][BT][XP];
+  __shared__ int s_act[BT], s_out[BT];
+  __shared__ float s_w[BT], s_sum[BT];
   // XCD-aware order: workgroups are spread round-robin over the 8 XCDs, so
   // map block b to tile 8*(l/nx) + b%8 and row group l%nx with l = b/8: all
   // row groups of one token tile run on one XCD and share its L2 copy of the
   // tile's activations.
+  const int32_t* tl = BT == kPrefillTileRows ? a.tiles : a.tiles_dn;
   const int bid = blockIdx.x, xcd = bid & 7, loc = bid >> 3;
   const int tile = 8 * (loc / nx) + xcd;
   const int ngrp = loc % nx;
-  if (tile >= *a.n_tiles) return;
-  const int slot = a.tiles[2 * tile], m0 = a.tiles[2 * tile + 1];
+  if (tile >= a.n_tiles[BT == kPrefillTileRows ? 0 : 1]) return;
+  const int slot = tl[2 * tile], m0 = tl[2 * tile + 1];
   const SlotEntry se = a.slots[slot];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = (NM == 2) ? a.H : a.I;
   const int R = (NM == 2) ? a.I : a.H;  // rows per matrix
   const int rb = ngrp * kGemmWaves + wave;
   const bool active = rb * 64 < R;
-  if (tid < BM) {
+  if (tid < BT) {
     int ar = -1, orow = -1;
     const bool ok = tile_token(a, se, m0 + tid, ar, orow);
     s_act[tid] = ok ? (NM == 2 ? ar : orow) : -1;  // activation row (x row, or h row = output row of GU)
@@ -333,23 +341,31 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     return *(gu16*)(ssrc + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3));
   };
 
-  f32x4 acc[NM][4][4];  // [matrix][row group q][token group mt]
+  f32x4 acc[NM][4][GMAX];  // [matrix][row group q][token group mt]
 #pragma unroll
   for (int m = 0; m < NM; ++m)
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) acc[m][q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mt = 0; mt < GMAX; ++mt) acc[m][q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   u32x4 ring[DEPTH][NM][WPS];
   uint32_t sring[DEPTH][NM];
-  P xring[2];
-  half8_t av[STEPS][4];
+  P xring[XR];
+  half8_t av[GMAX], av1[GMAX];  // A operands of K-steps 0 and 1 (int2)
   const int n = lane & 15, g = lane >> 4;
+  auto read_a = [&](half8_t (&dst)[GMAX], int buf, int st, auto MTC) {
+#pragma unroll
+    for (int mt = 0; mt < decltype(MTC)::value; ++mt) dst[mt] = a_operand<FMT>(&sx[buf][16 * mt + n][0], g, st);
+  };
   // The loop body is straight-line code (loads past the last slice re-read
   // it and go unused), so that the load counters stay exact across slices.
   auto run = [&](auto ACTIVE, auto MTC) {
     constexpr int MT = decltype(MTC)::value;  // 16-token groups of the tile that hold tokens
+    // slice c+1's A operands are read during slice c, except where they
+    // would not fit beside the accumulators (int2: two K-steps per slice;
+    // more than 4 token groups)
+    constexpr bool kPrefetchA = STEPS == 1 && MT <= 4;
     // prologue loads in the order of the loop's refills (activation slice
     // j+2, then weight slice j), so that the load counters the loop waits on
     // are the same on entry as in steady state
@@ -357,7 +373,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < DEPTH; ++j) {
-      if (j < 2) xring[j] = load_x(j + 2 < nch ? j + 2 : nch - 1);
+      if (j < XR) xring[j] = load_x(j + 2 < nch ? j + 2 : nch - 1);
       if (ACTIVE) {
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
@@ -372,12 +388,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     stage(v0, &sx[0][0][0], true);
     stage(v1, &sx[1][0][0], true);
     __syncthreads();
-    if (kPrefetchA) {
-#pragma unroll
-      for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) av[st][mt] = a_operand<FMT>(&sx[0][16 * mt + n][0], g, st);
-    }
+    if (kPrefetchA) read_a(av, 0, 0, MTC);
     int b1 = 1, b2 = 2;  // LDS slices of c+1 and c+2
     for (int c0 = 0; c0 < nch; c0 += DEPTH) {
 #pragma unroll
@@ -385,62 +396,52 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
         const int c = c0 + j;
         // each ring slot is consumed (copied out) before it is refilled, so
         // that the refill lands in the same registers
-        stage(xring[j & 1], &sx[b2][0][0], c + 2 < nch);
+        stage(xring[j % XR], &sx[b2][0][0], c + 2 < nch);
         __builtin_amdgcn_sched_barrier(0);
-        xring[j & 1] = load_x(c + 4 < nch ? c + 4 : nch - 1);
-        half8_t avn[STEPS][4];
+        xring[j % XR] = load_x(c + 2 + XR < nch ? c + 2 + XR : nch - 1);
+        const int b0 = b1 == 0 ? 2 : b1 - 1;  // LDS slice of c
+        half8_t avn[GMAX];
         if (kPrefetchA) {
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) avn[st][mt] = a_operand<FMT>(&sx[b1][16 * mt + n][0], g, st);
+          read_a(avn, b1, 0, MTC);
         } else {
-#pragma unroll
-          for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) av[st][mt] = a_operand<FMT>(&sx[b1 == 0 ? 2 : b1 - 1][16 * mt + n][0], g, st);
+          read_a(av, b0, 0, MTC);
+          if (STEPS == 2) read_a(av1, b0, 1, MTC);
         }
         if (ACTIVE) {
           const int cn = c + DEPTH < nch ? c + DEPTH : nch - 1;
-          auto refill = [&]() {
-#pragma unroll
-            for (int m = 0; m < NM; ++m) {
-#pragma unroll
-              for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cn, m, p);
-              if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(cn, m);
-            }
-          };
-          auto multiply = [&](const RawBlock& rw, int m) {
-#pragma unroll
-            for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                const half8_t b = b_operand<FMT>(rw, q, st);
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt)
-                  acc[m][q][mt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(av[st][mt], b, acc[m][q][mt], 0, 0, 0);
-              }
-          };
           // transpose every matrix (which ends the slot's registers), refill
           // the slot, then multiply
           RawBlock rw[NM];
 #pragma unroll
           for (int m = 0; m < NM; ++m) rw[m] = to_raw<FMT>(ring[j][m], sring[j][m]);
           __builtin_amdgcn_sched_barrier(0);
-          refill();
+#pragma unroll
+          for (int m = 0; m < NM; ++m) {
+#pragma unroll
+            for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cn, m, p);
+            if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(cn, m);
+          }
           // the loads above issue before the matrix work below
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int m = 0; m < NM; ++m) multiply(rw[m], m);
+          for (int m = 0; m < NM; ++m)
+#pragma unroll
+            for (int st = 0; st < STEPS; ++st)
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const half8_t b = b_operand<FMT>(rw[m], q, st);
+#pragma unroll
+                for (int mt = 0; mt < MT; ++mt)
+                  acc[m][q][mt] =
+                      __builtin_amdgcn_mfma_f32_16x16x32_f16(st ? av1[mt] : av[mt], b, acc[m][q][mt], 0, 0, 0);
+              }
           // the barrier below stays after the matrix work
           __builtin_amdgcn_sched_barrier(0);
         }
         __syncthreads();
         if (kPrefetchA) {
 #pragma unroll
-          for (int st = 0; st < STEPS; ++st)
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) av[st][mt] = avn[st][mt];
+          for (int mt = 0; mt < MT; ++mt) av[mt] = avn[mt];
         }
         b1 = b2;
         b2 = b2 == 2 ? 0 : b2 + 1;
@@ -448,10 +449,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     }
   };
   // the loop is specialised on the number of 16-token groups that hold
-  // tokens, so that a partly filled tile skips the matrix work of its empty
-  // groups (their accumulators stay zero; the epilogue skips padding tokens)
+  // tokens (1-4, and 6 or 8 in 128-token tiles), so that a partly filled
+  // tile skips the matrix work of its empty groups (their accumulators stay
+  // zero; the epilogue skips padding tokens)
   typedef std::true_type on;
-  const int ng = (min(se.n - m0, BM) + 15) >> 4;
+  const int ng = (min(se.n - m0, BT) + 15) >> 4;
   if (!active)
     run(std::false_type{}, std::integral_constant<int, 1>{});
   else if (ng <= 1)
@@ -460,8 +462,12 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
     run(on{}, std::integral_constant<int, 2>{});
   else if (ng == 3)
     run(on{}, std::integral_constant<int, 3>{});
-  else
+  else if (GMAX == 4 || ng == 4)
     run(on{}, std::integral_constant<int, 4>{});
+  else if (ng <= 6)
+    run(on{}, std::integral_constant<int, GMAX == 8 ? 6 : 4>{});
+  else
+    run(on{}, std::integral_constant<int, GMAX>{});
   if (SL::SUB) {  // per-token activation sums: the PPR pieces of a token sit in adjacent lanes
     float s = xsum;
 #pragma unroll
@@ -472,6 +478,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   if (!active) return;
   // epilogue: lane (n, g) holds tokens 16 mt + 4 g + i of row 64 rb + 16 q + n
   constexpr float kSub = 16777216.0f;  // 2^24
+  const int gn = (min(se.n - m0, BT) + 15) >> 4;  // token groups that can hold tokens
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     const int row = rb * 64 + 16 * q + n;
@@ -486,10 +493,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
         suv = g3[1];
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < GMAX; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int mm = 16 * mt + 4 * g + i;
+          if (mt >= gn) continue;
           const int orow = s_out[mm];
           if (orow < 0) continue;
           float ga = acc[0][q][mt][i], ua = acc[NM - 1][q][mt][i];
@@ -508,10 +516,11 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
       else
         sd = reinterpret_cast<const float*>(se.base + a.L.g3_off)[2];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < GMAX; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int mm = 16 * mt + 4 * g + i;
+          if (mt >= gn) continue;
           const int orow = s_out[mm];
           if (orow < 0) continue;
           float da = acc[0][q][mt][i];
@@ -562,6 +571,7 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   a.slots = r.slots;
   a.pairs = r.pairs;
   a.tiles = r.tiles;
+  a.tiles_dn = r.tiles_dn;
   a.n_tiles = r.n_tiles;
   a.topk_w = r.topk_w;
   a.topk_idx = r.topk_idx;
@@ -579,16 +589,17 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   const int mt8 = (prefill_max_tiles(p.T, p.k, p.E, p.S) + 7) / 8 * 8;
   const int rows_per_wg = 64 * kGemmWaves;
   const int nx_gu = (p.I + rows_per_wg - 1) / rows_per_wg, nx_dn = (p.H + rows_per_wg - 1) / rows_per_wg;
+  const int mt8_dn = (prefill_max_tiles(p.T, p.k, p.E, p.S, kDownTileRows) + 7) / 8 * 8;
   const dim3 blk(64 * kGemmWaves);
-  auto gemms = [&](auto gu, auto dn) {
+  auto gemms = [&](auto gu, auto dn, int dn_rows = kDownTileRows) {
     launch_k(gu, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
-    launch_k(dn, dim3(mt8 * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
+    launch_k(dn, dim3((dn_rows == kDownTileRows ? mt8_dn : mt8) * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
   };
-  // ring depth: 4 slices of 32 columns, 2 of 64 (int2) or of 2 chunks (int8)
+  // ring depth: 4 slices for the int4 gate/up, 2 otherwise
   switch (d.wfmt) {
-    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4>, k_expert_gemm<MOE_W_INT4_ROW, 1, 4>); break;
+    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4>, k_expert_gemm<MOE_W_INT4_ROW, 1, 2>); break;
     case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2, 2>, k_expert_gemm<MOE_W_INT8_ROW, 1, 2>); break;
-    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2>); break;
+    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2>, kPrefillTileRows); break;
     default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2>); break;
   }
   launch_k(k_combine, dim3((p.H / 2 + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);

@@ -38,8 +38,9 @@ struct RouteArgs {
   int n_chunks;
   // slot table and grouped-GEMM tile list (forward only)
   SlotEntry* slots;
-  int32_t* tiles;
-  int32_t* n_tiles;
+  int32_t* tiles;     // gate/up tiles (kPrefillTileRows tokens)
+  int32_t* tiles_dn;  // down tiles (kDownTileRows tokens)
+  int32_t* n_tiles;   // [2]
   int slots_max;
   const void* const* experts;
   const void* shared;
@@ -232,10 +233,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& tot
 
 // Pass 2 (one block, thread e = expert e): per-expert totals over the
 // chunks; block-wide prefix sums give each expert's pair offset, its place
-// in the union and its first grouped-GEMM tile, so every thread writes its
-// own expert's entries; then each (chunk, expert) base offset.
+// in the union and its first tile in each grouped-GEMM tile list, so every
+// thread writes its own expert's entries; then each (chunk, expert) base
+// offset.
 __global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
-  __shared__ int s_wave[3][kScanThreads / 64];
+  __shared__ int s_wave[4][kScanThreads / 64];
   static_assert(kMaxExperts <= kScanThreads, "one thread per expert");
   const int e = threadIdx.x;
   int tot = 0;  // pairs of expert e (16 independent loads in flight)
@@ -248,13 +250,15 @@ __global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
       for (int i = 0; i < 16; ++i) tot += v[i];
     }
   const int used = tot > 0 ? 1 : 0;
-  const int ntl = (tot + kPrefillTileRows - 1) / kPrefillTileRows;
-  int off_all, nu_all, nt_all;
+  const int ntl = (tot + kPrefillTileRows - 1) / kPrefillTileRows, ntd = (tot + kDownTileRows - 1) / kDownTileRows;
+  int off_all, nu_all, nt_all, nd_all;
   const int off = block_exclusive_scan(tot, s_wave[0], off_all);
   const int u = block_exclusive_scan(used, s_wave[1], nu_all);
   const int tb = block_exclusive_scan(ntl, s_wave[2], nt_all);
+  const int db = block_exclusive_scan(ntd, s_wave[3], nd_all);
   // grouped-GEMM tiles: the shared expert's first, then the union in order
   const int nsh = a.S ? (a.T + kPrefillTileRows - 1) / kPrefillTileRows : 0;
+  const int nshd = a.S ? (a.T + kDownTileRows - 1) / kDownTileRows : 0;
   if (used) {
     a.uniq_ids[u] = e;
     a.uniq_off[u] = off;
@@ -265,22 +269,35 @@ __global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
       sl.p0 = off;
       a.slots[a.S + u] = sl;
     }
-    if (a.tiles)
+    if (a.tiles) {
       for (int i = 0; i < ntl; ++i) {
         a.tiles[2 * (nsh + tb + i)] = a.S + u;
         a.tiles[2 * (nsh + tb + i) + 1] = i * kPrefillTileRows;
       }
+      for (int i = 0; i < ntd; ++i) {
+        a.tiles_dn[2 * (nshd + db + i)] = a.S + u;
+        a.tiles_dn[2 * (nshd + db + i) + 1] = i * kDownTileRows;
+      }
+    }
   }
-  if (a.tiles)
+  if (a.tiles) {
     for (int i = e; i < nsh; i += kScanThreads) {
       a.tiles[2 * i] = 0;
       a.tiles[2 * i + 1] = i * kPrefillTileRows;
     }
+    for (int i = e; i < nshd; i += kScanThreads) {
+      a.tiles_dn[2 * i] = 0;
+      a.tiles_dn[2 * i + 1] = i * kDownTileRows;
+    }
+  }
   if (e == 0) {
     *a.n_unique = nu_all;
     a.uniq_off[nu_all] = off_all;
     if (a.slots && a.S) write_slot(a, 0, -1, a.T, -1);
-    if (a.tiles) *a.n_tiles = nsh + nt_all;
+    if (a.tiles) {
+      a.n_tiles[0] = nsh + nt_all;
+      a.n_tiles[1] = nshd + nd_all;
+    }
   }
   if (a.slots)
     for (int sl = a.S + nu_all + e; sl < a.slots_max; sl += kScanThreads) write_slot(a, sl, 0, 0, 0);
@@ -352,6 +369,7 @@ hipError_t launch_route(const moe_dims_t& d, const Plan& p, const moe_weights_t&
   a.S = p.S;
   a.slots = with_slots ? r.slots : nullptr;
   a.tiles = with_slots ? r.tiles : nullptr;
+  a.tiles_dn = with_slots ? r.tiles_dn : nullptr;
   a.n_tiles = r.n_tiles;
   a.slots_max = p.slots_max;
   a.experts = w.experts;
