@@ -394,6 +394,7 @@ struct UnionLds {
   int base[kMaxExperts];       // first pair of each expert
   int pe[kDecodeMaxTokens * kMaxTopK];
   const uint8_t* ep[kMaxExperts];  // packed expert pointers, staged by the caller
+  RankSlots<1> rank[kWpg];         // top-k scratch of each wavefront
 };
 
 // Lane l owns experts [l*per, l*per + per).
@@ -451,6 +452,37 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
     const int t = p / a.k;
     a.pairs[ls.base[e] + __popc(ls.mask[e] & ((1u << t) - 1u))] = p;
   }
+}
+
+// The same outputs for a single token, whose k slots name distinct experts:
+// slot j (kept, pe[j] >= 0) is pair j, and its expert's place in the union
+// is the number of kept slots with a smaller expert.  Run by one wavefront,
+// from registers: one LDS read and the stores.
+__device__ __forceinline__ void union_one(const DecArgs& a, UnionLds& ls) {
+  const int lane = threadIdx.x & 63;
+  const int k = a.k;
+  const int e = lane < k ? ls.pe[lane] : -1;
+  int r = 0;
+  for (int j = 0; j < k; ++j) {
+    const int ej = __builtin_amdgcn_readlane(e, j);
+    r += (ej >= 0 && ej < e) ? 1 : 0;
+  }
+  const int nu = __popcll(__ballot(e >= 0));
+  if (e >= 0) {
+    a.uniq_ids[r] = e;
+    a.uniq_off[r] = r;
+    SlotEntry se;
+    se.base = ls.ep[e];
+    se.n = 1;
+    se.p0 = r;
+    a.slots[a.S + r] = se;
+    a.pairs[r] = lane;
+  }
+  if (lane == 0) {
+    *a.n_unique = nu;
+    a.uniq_off[nu] = nu;
+  }
+  for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
 }
 
 // ---- router unit: fp64 partial logits of expert e over one column segment --
@@ -543,9 +575,12 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
   const int t0 = wave * tpw, t1 = min(a.T, t0 + tpw);
   for (int t = t0; t < t1; ++t)
     topk_tokens(a.z + (size_t)t * a.E, a.rsplit, (size_t)a.T * a.E, a.rbias, a.E, a.k, a.top_p, 1,
-                a.topk_idx + t * a.k, a.topk_w + t * a.k, ls.pe + t * a.k);
+                a.topk_idx + t * a.k, a.topk_w + t * a.k, ls.pe + t * a.k, ls.rank[wave]);
   __syncthreads();
-  if (wave == 0) union_step(a, ls);
+  if (wave == 0) {
+    if (a.T == 1) union_one(a, ls);
+    else union_step(a, ls);
+  }
 }
 
 // ---- gate/up: one (slot, 64-row block) per workgroup --------------------------

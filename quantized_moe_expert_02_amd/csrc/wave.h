@@ -224,6 +224,14 @@ __device__ void topk_any(const double* zrow, int nz, size_t zstride, const float
 }
 
 
+// LDS scratch of one wavefront's top-k: the winner of round j writes its
+// key and expert to slot j, and lane j reads them back after the rounds.
+template <int NT>
+struct RankSlots {
+  uint64_t key[NT][kMaxTopK];
+  int e[NT][kMaxTopK];
+};
+
 // Top-k of NT tokens at once by one wavefront (the NT rank searches are
 // independent chains, so interleaving them hides their latency).  Same
 // result as topk_wave per token.  Token t's logit of expert e is the sum of
@@ -232,12 +240,15 @@ __device__ void topk_any(const double* zrow, int nz, size_t zstride, const float
 // kernel and published before this wavefront read them.  Each lane first
 // sorts the kPer logits it holds (descending; equal logits keep ascending
 // expert order), then each of the k rounds takes the wave-wide largest head
-// (ties to the lower expert index) and the winning lane pops it.  Outputs
-// are written with device-coherent stores: idx_out[t * k + j], w_out[...],
-// and slot_expert[t * k + j] (LDS) if set.
+// (ties to the lower expert index): the lane holding it recognises itself
+// from the wave-wide maximum, records it in slot j of rs and pops it, so a
+// round's dependent chain is the reduction, one compare and the pop.
+// Outputs are written with device-coherent stores: idx_out[t * k + j],
+// w_out[...], and slot_expert[t * k + j] (LDS) if set.
 template <int kPer, int NT>
 __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
-                                           float top_p, int32_t* idx_out, float* w_out, int* slot_expert) {
+                                           float top_p, int32_t* idx_out, float* w_out, int* slot_expert,
+                                           RankSlots<NT>& rs) {
   const int lane = threadIdx.x & (kWave - 1);
   double v[NT][kPer];
 #pragma unroll
@@ -295,13 +306,6 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
         idx[t][i] = sw ? i1 : i0;
         idx[t][i + 1] = sw ? i0 : i1;
       }
-  uint64_t my_key[NT];
-  int my_e[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    my_key[t] = 0;
-    my_e[t] = -1;
-  }
   for (int j = 0; j < k; ++j) {
     uint32_t hmax[NT];
 #pragma unroll
@@ -309,25 +313,17 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       const uint32_t hi = (uint32_t)(key[t][0] >> 32);
-      const uint64_t cand = __ballot(hi == hmax[t]);
-      int win;
-      if (__popcll(cand) == 1) {
-        win = __ffsll((unsigned long long)cand) - 1;
-      } else {  // equal high words: compare the low words, then the expert index
+      bool win = hi == hmax[t];
+      if (__popcll(__ballot(win)) != 1) {  // equal high words: compare the low words, then the expert index
         const uint32_t lo = (uint32_t)key[t][0];
-        const uint32_t lmax = wave_max_u32(hi == hmax[t] ? lo : 0u);
-        const bool c2 = (hi == hmax[t]) && (lo == lmax);
+        const uint32_t lmax = wave_max_u32(win ? lo : 0u);
+        const bool c2 = win && (lo == lmax);
         const uint32_t best_inv = wave_max_u32(c2 ? ~(uint32_t)idx[t][0] : 0u);
-        win = (int)(~best_inv) & (kWave - 1);
+        win = c2 && (uint32_t)idx[t][0] == ~best_inv;  // expert indices are distinct: one lane
       }
-      const uint64_t wk = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(key[t][0] >> 32), win) << 32) |
-                          (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)key[t][0], win);
-      const int we = __builtin_amdgcn_readlane(idx[t][0], win);
-      if (lane == j) {
-        my_key[t] = wk;
-        my_e[t] = we;
-      }
-      if (lane == win) {
+      if (win) {
+        rs.key[t][j] = key[t][0];
+        rs.e[t][j] = idx[t][0];
 #pragma unroll
         for (int i = 0; i < kPer - 1; ++i) {
           key[t][i] = key[t][i + 1];
@@ -336,6 +332,17 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
         key[t][kPer - 1] = 0;
       }
     }
+  }
+  // this wavefront's LDS writes above complete before its reads below
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_wave_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  uint64_t my_key[NT];
+  int my_e[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    my_key[t] = lane < k ? rs.key[t][lane] : 0ull;
+    my_e[t] = lane < k ? rs.e[t][lane] : -1;
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
@@ -359,24 +366,20 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
 template <int kPer>
 __device__ __forceinline__ void topk_tokens_per(const double* z, int nz, size_t zstride, const float* bias, int E,
                                                 int k, float top_p, int T, int32_t* idx_out, float* w_out,
-                                                int* slot_expert) {
-  constexpr int NT = 1;
-  int t0 = 0;
-  for (; t0 + NT <= T; t0 += NT)
-    topk_multi<kPer, NT>(z + (size_t)t0 * E, nz, zstride, bias, E, k, top_p, idx_out + t0 * k, w_out + t0 * k,
-                         slot_expert + t0 * k);
-  for (; t0 < T; ++t0)
+                                                int* slot_expert, RankSlots<1>& rs) {
+  for (int t0 = 0; t0 < T; ++t0)
     topk_multi<kPer, 1>(z + (size_t)t0 * E, nz, zstride, bias, E, k, top_p, idx_out + t0 * k, w_out + t0 * k,
-                        slot_expert + t0 * k);
+                        slot_expert + t0 * k, rs);
 }
 
 __device__ __forceinline__ void topk_tokens(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
-                                            float top_p, int T, int32_t* idx_out, float* w_out, int* slot_expert) {
-  if (E <= 64) topk_tokens_per<1>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
-  else if (E <= 128) topk_tokens_per<2>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
-  else if (E <= 256) topk_tokens_per<4>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
-  else if (E <= 512) topk_tokens_per<8>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
-  else topk_tokens_per<16>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert);
+                                            float top_p, int T, int32_t* idx_out, float* w_out, int* slot_expert,
+                                            RankSlots<1>& rs) {
+  if (E <= 64) topk_tokens_per<1>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
+  else if (E <= 128) topk_tokens_per<2>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
+  else if (E <= 256) topk_tokens_per<4>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
+  else if (E <= 512) topk_tokens_per<8>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
+  else topk_tokens_per<16>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
 }
 
 // Every lane ends with the wave-wide fp64 sum, added in a fixed butterfly order.
