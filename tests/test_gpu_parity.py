@@ -150,6 +150,40 @@ def test_forward_full_size_matches_oracle(name):
     _log(f"  {name}: U={r.n_unique} rel_l2={rel:.2e} max_abs={mx:.2e}")
 
 
+# Single-token layers at the decode layer's I = 2048 in every weight format,
+# with and without a shared expert, k from 1 to 16, with and without top-p
+# (the batch union is the token's kept slots: the one-token route tail).
+ONE_TOKEN_CASES = [
+    ("int4_s1_k8", synth.Dims(1024, 2048, 32, 8, 1, synth.INT4_ROW)),
+    ("e2m1_s1_k8", synth.Dims(1024, 2048, 32, 8, 1, synth.E2M1_B16)),
+    ("int8_s0_k16", synth.Dims(1024, 2048, 32, 16, 0, synth.INT8_ROW)),
+    ("int2_s1_k15", synth.Dims(1024, 2048, 64, 15, 1, synth.INT2_ROW)),
+    ("int4_s0_k1", synth.Dims(512, 2048, 4, 1, 0, synth.INT4_ROW)),
+    ("e2m1_s0_k3_topp", synth.Dims(1024, 2048, 32, 3, 0, synth.E2M1_B16, top_p=0.5)),
+    ("int4_s1_k8_topp", synth.Dims(1024, 2048, 64, 8, 1, synth.INT4_ROW, top_p=0.6)),
+    ("int8_s1_k6_topp", synth.Dims(512, 2048, 16, 6, 1, synth.INT8_ROW, top_p=0.5)),
+    ("int4_s1_k16", synth.Dims(512, 2048, 32, 16, 1, synth.INT4_ROW)),
+]
+
+
+@pytest.mark.parametrize("name,dims", ONE_TOKEN_CASES)
+def test_forward_one_token_matches_oracle(name, dims):
+    _log("one token", name, dims)
+    layer = synth.make_layer(dims, ("dn1", name))
+    x = synth.make_tokens(dims, 1, ("dn1", name))
+    r = oracle_route(layer, x)
+    assert min_topk_gap(r, dims.top_k) > 1e-9
+    if dims.top_p:
+        assert (r.topk_idx < 0).any()
+    y_ref = oracle.forward(layer, x)
+    pl = moe.PackedLayer.from_layer(layer)
+    ti = torch.empty((1, dims.top_k), dtype=torch.int32, device=DEV)
+    y = moe.moe_w4a16_forward(pl, x.to(DEV), topk_idx=ti)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
+    assert_close(y, y_ref, name)
+
+
 def test_forward_deterministic_and_batch_invariant():
     dims = synth.Dims(1024, 256, 64, 4, 1, 0)
     layer = synth.make_layer(dims, "det")
