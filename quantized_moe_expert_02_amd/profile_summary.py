@@ -7,6 +7,10 @@
       HBM traffic per launch of kernel K from a FETCH_SIZE run and a WRITE_SIZE run (rocprofv3 --pmc,
       --output-format csv), each scaled by what the same counter reads for the plain copy kernel that
       `bench.py --calibrate-copy-mb N` runs first (N MB read and N MB written per launch)
+  python -m quantized_moe_expert_02_amd.profile_summary mfma PMC_DIR --kernel K --workload W --command C
+      fp16 matrix-core work per launch of the kernels whose names contain K, from one rocprofv3 --pmc run of
+      the derived metrics MfmaFlopsF16 (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512) and MfmaUtil (matrix-core busy
+      cycles over GRBM_GUI_ACTIVE x SIMDs)
 """
 from __future__ import annotations
 
@@ -101,6 +105,24 @@ def traffic(args) -> None:
     print(f"source_sha256 = {sha}")
 
 
+def mfma(args) -> None:
+    flops = _counter(args.path, "MfmaFlopsF16")
+    util = _counter(args.path, "MfmaUtil")
+    names = sorted(k for k in flops if args.kernel in k)
+    if not names:
+        sys.exit(f"kernel matching {args.kernel!r} not found; kernels: {sorted(flops)[:20]}")
+    print(f"# fp16 matrix-core work per launch, {args.workload}: rocprofv3 --pmc MfmaFlopsF16 MfmaUtil")
+    print(f"# command: {args.command}")
+    print("# executed flops count every issued v_mfma (the padding of partly filled 16-token groups included);")
+    print("# MfmaUtil = matrix-core busy cycles / (GRBM_GUI_ACTIVE x SIMDs) over the dispatch, in %")
+    print(f"{'dispatches':>10} {'gflop_per_launch':>17} {'mfma_util_pct':>14}  kernel")
+    for k in names:
+        f = flops[k]
+        u = util.get(k, [])
+        um = sum(u) / len(u) if u else float("nan")
+        print(f"{len(f):10d} {sum(f) / len(f) / 1e9:17.2f} {um:14.2f}  {k[:110]}")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -116,8 +138,13 @@ def main() -> None:
     b.add_argument("--workload", required=True)
     b.add_argument("--source", required=True)
     b.add_argument("--command", required=True)
+    c = sub.add_parser("mfma")
+    c.add_argument("path")
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--command", required=True)
     args = ap.parse_args()
-    stats(args) if args.mode == "stats" else traffic(args)
+    {"stats": stats, "traffic": traffic, "mfma": mfma}[args.mode](args)
 
 
 if __name__ == "__main__":
