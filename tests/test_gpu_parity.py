@@ -163,6 +163,9 @@ ONE_TOKEN_CASES = [
     ("int4_s1_k8_topp", synth.Dims(1024, 2048, 64, 8, 1, synth.INT4_ROW, top_p=0.6)),
     ("int8_s1_k6_topp", synth.Dims(512, 2048, 16, 6, 1, synth.INT8_ROW, top_p=0.5)),
     ("int4_s1_k16", synth.Dims(512, 2048, 32, 16, 1, synth.INT4_ROW)),
+    # 1000 experts (16 per lane in the ranking) and the largest k
+    ("int4_e1000_k32", synth.Dims(512, 256, 1000, 32, 1, synth.INT4_ROW)),
+    ("e2m1_e1000_k32_topp", synth.Dims(512, 256, 1000, 32, 0, synth.E2M1_B16, top_p=0.6)),
 ]
 
 
