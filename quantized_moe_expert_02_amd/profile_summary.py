@@ -11,6 +11,9 @@
       fp16 matrix-core work per launch of the kernels whose names contain K, from one rocprofv3 --pmc run of
       the derived metrics MfmaFlopsF16 (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512) and MfmaUtil (matrix-core busy
       cycles over GRBM_GUI_ACTIVE x SIMDs)
+  python -m quantized_moe_expert_02_amd.profile_summary counters PMC_DIR --kernel K --title T --command C
+      mean value per dispatch of every counter of one rocprofv3 --pmc run, for the kernels whose names
+      contain K
 """
 from __future__ import annotations
 
@@ -123,6 +126,26 @@ def mfma(args) -> None:
         print(f"{len(f):10d} {sum(f) / len(f) / 1e9:17.2f} {um:14.2f}  {k[:110]}")
 
 
+def counters(args) -> None:
+    f = _find(args.path, "*counter_collection.csv")
+    vals = {}
+    with open(f) as fh:
+        for row in csv.DictReader(fh):
+            k = _short(row["Kernel_Name"])
+            if args.kernel in k:
+                vals.setdefault(k, {}).setdefault(row["Counter_Name"], []).append(float(row["Counter_Value"]))
+    if not vals:
+        sys.exit(f"kernel matching {args.kernel!r} not found")
+    print(f"# {args.title}")
+    print(f"# command: {args.command}")
+    print("# mean counter value per dispatch")
+    for k in sorted(vals):
+        print(k[:110])
+        for c in sorted(vals[k]):
+            v = vals[k][c]
+            print(f"  {c:28s} {sum(v) / len(v):16.4g}   ({len(v)} dispatches)")
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -143,8 +166,13 @@ def main() -> None:
     c.add_argument("--kernel", required=True)
     c.add_argument("--workload", required=True)
     c.add_argument("--command", required=True)
+    e = sub.add_parser("counters")
+    e.add_argument("path")
+    e.add_argument("--kernel", required=True)
+    e.add_argument("--title", required=True)
+    e.add_argument("--command", required=True)
     args = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "mfma": mfma}[args.mode](args)
+    {"stats": stats, "traffic": traffic, "mfma": mfma, "counters": counters}[args.mode](args)
 
 
 if __name__ == "__main__":
