@@ -438,8 +438,8 @@ def main():
                          "traffic counters taken over the run can be scaled against a kernel of known traffic")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (the layer's EP/TP sharding "
-              "is described in DESIGN.md but not built). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (expert- and tensor-parallel "
+              "sharding of the layer is a design, not code). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     torch.cuda.init()
     moe.lib()
