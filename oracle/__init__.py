@@ -48,9 +48,9 @@ def lib():
         L.oracle_e4m3_values.argtypes = [P, i64, P]
         L.oracle_dequant.argtypes = [i32, P, P, ctypes.c_float, i32, i32, P]
         L.oracle_dequant.restype = i32
-        L.oracle_route.argtypes = [P, ctypes.c_double, P, i32, P, P, P, P, P, P, P, P, P]
+        L.oracle_route.argtypes = [P, ctypes.c_float, P, i32, P, P, P, P, P, P, P, P, P]
         L.oracle_route.restype = i32
-        L.oracle_forward.argtypes = [P, ctypes.c_double, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P, i32]
+        L.oracle_forward.argtypes = [P, ctypes.c_float, P, P, P, P, P, P, P, P, P, P, i32, P, i32, P, i32]
         L.oracle_forward.restype = i32
         L.oracle_max_threads.restype = i32
         _lib = L
@@ -143,7 +143,9 @@ class Route:
 
 
 def route(dims, x, router_w, router_b, want_z: bool = True, top_p: Optional[float] = None) -> Route:
-    """Routing and union; top_p defaults to dims.top_p (0: plain top-k)."""
+    """Routing and union; top_p defaults to dims.top_p (0: plain top-k).  The
+    threshold is the layer's binary32 parameter (rounded to binary32 here, as
+    the C ABI's moe_dims_t.top_p is a float)."""
     if top_p is None:
         top_p = float(getattr(dims, "top_p", 0.0))
     d = np.asarray(dims.as_tuple() if hasattr(dims, "as_tuple") else dims, dtype=np.int32)

@@ -167,41 +167,20 @@ void expert_ffn(const Dims& d, const Expert& ex, const double* x, double* hbuf, 
   }
 }
 
-// Adaptive top-p over the k ranked slots ("Show HN: 低速のコンピュータでGLM
-// 5.2を動かす方法", hakusoku.com, section 実装済み機能: the --topp option that
+// Adaptive expert top-p ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法",
+// hakusoku.com, section 実行・チューニングパラメータ: the --topp option, which
 // keeps experts until their cumulative weight reaches p).  Reading taken:
-// keep the shortest prefix of the k slots whose cumulative renormalised
-// weight reaches p, then renormalise over the kept slots.  The decision
-// (an integer) is taken in the GPU path's precision, binary32: s_j =
-// 1 / (1 + exp(-z_j)) from the logit rounded to binary32, their sum over the
-// slots as a pairwise tree over 64 lanes (slots beyond k are zero), w_j =
-// s_j / sum, then the prefix sums in slot order compared with p rounded to
-// binary32.  Returns the number of kept slots, m (k when p <= 0 or p >= 1).
-int top_p_keep(const double* zk, int k, double top_p) {
-  if (!(top_p > 0.0 && top_p < 1.0)) return k;
-  float v[64];
-  for (int j = 0; j < 64; ++j) {
-    if (j < k) {
-      const float zf = (float)zk[j];
-      v[j] = 1.0f / (1.0f + std::exp(-zf));
-    } else {
-      v[j] = 0.0f;
-    }
-  }
-  float s[64];
-  std::memcpy(s, v, sizeof s);
-  for (int width = 1; width < 64; width *= 2)  // butterfly: every lane holds the same tree sum
-    for (int j = 0; j < 64; j += 2 * width)
-      for (int i = j; i < j + width; ++i) {
-        const float sum = v[i] + v[i + width];
-        v[i] = sum;
-        v[i + width] = sum;
-      }
-  const float tot = v[0];
-  const float p = (float)top_p;
-  float cum = 0.0f;
+// w holds the k renormalised weights of the ranked slots, in slot order;
+// keep the shortest prefix whose cumulative weight reaches p, i.e. the
+// smallest m with w_0 + ... + w_{m-1} >= p, summed in double in slot
+// order.  p is the layer's binary32 parameter, widened exactly.  Returns m
+// (k when p <= 0 or p >= 1, or when no prefix reaches p).
+int top_p_keep(const double* w, int k, float top_p) {
+  if (!(top_p > 0.0f && top_p < 1.0f)) return k;
+  const double p = (double)top_p;
+  double cum = 0.0;
   for (int j = 0; j < k; ++j) {
-    cum += s[j] / tot;
+    cum += w[j];
     if (cum >= p) return j + 1;
   }
   return k;
@@ -214,7 +193,7 @@ int top_p_keep(const double* zk, int k, double top_p) {
 // weights are renormalised to sum to one, w_j = s_j / sum s.  With adaptive
 // top-p only the first m slots are kept (top_p_keep) and renormalised over
 // those; slots j >= m get index -1 and weight 0.
-void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const float* b, double top_p,
+void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const float* b, float top_p,
                  int* idx, double* w, double* z) {
   std::vector<double> xd(d.H);
   for (int h = 0; h < d.H; ++h) xd[h] = fp16_value(xrow[h]);
@@ -230,17 +209,23 @@ void route_token(const Dims& d, const uint16_t* xrow, const float* Wr, const flo
     if (z[a] != z[c]) return z[a] > z[c];
     return a < c;
   });
-  std::vector<double> zk(d.k);
-  for (int j = 0; j < d.k; ++j) zk[j] = z[order[j]];
-  const int m = top_p_keep(zk.data(), d.k, top_p);
+  // sigmoid scores of the k ranked slots, renormalised to sum to one
+  std::vector<double> s(d.k), wk(d.k);
   double ssum = 0.0;
-  std::vector<double> s(d.k);
-  for (int j = 0; j < m; ++j) {
-    idx[j] = order[j];
-    s[j] = 1.0 / (1.0 + std::exp(-zk[j]));
+  for (int j = 0; j < d.k; ++j) {
+    s[j] = 1.0 / (1.0 + std::exp(-z[order[j]]));
     ssum += s[j];
   }
-  for (int j = 0; j < m; ++j) w[j] = s[j] / ssum;
+  for (int j = 0; j < d.k; ++j) wk[j] = s[j] / ssum;
+  // adaptive top-p keeps the first m slots; their weights are renormalised
+  // over the kept slots
+  const int m = top_p_keep(wk.data(), d.k, top_p);
+  double msum = 0.0;
+  for (int j = 0; j < m; ++j) msum += s[j];
+  for (int j = 0; j < m; ++j) {
+    idx[j] = order[j];
+    w[j] = s[j] / msum;
+  }
   for (int j = m; j < d.k; ++j) {
     idx[j] = -1;
     w[j] = 0.0;
@@ -293,12 +278,13 @@ int oracle_dequant(int32_t fmt, const uint8_t* q, const void* s, float g, int32_
 // Routing and the batch union.
 //   dims: int32[6] = {H, I, E, k, has_shared, fmt}
 //   x: binary16 bits [T][H]; Wr: fp32 [E][H]; b: fp32 [E] or NULL
-//   top_p: adaptive top-p threshold (0 keeps all k slots)
+//   top_p: adaptive top-p threshold, the layer's binary32 parameter (0 keeps
+//   all k slots)
 //   outputs: topk_idx int32 [T][k], topk_w fp32 [T][k], z fp64 [T][E] (nullable),
 //   n_unique int32[1], uniq_ids int32[min(E,T*k)], uniq_off int32[min(E,T*k)+1],
 //   pairs int32[T*k] (pair id t*k+j of the kept slots, grouped by expert
 //   ascending, tokens ascending; uniq_off[n_unique] = number of kept pairs).
-int oracle_route(const int32_t* dims, double top_p, const uint16_t* x, int32_t T, const float* Wr, const float* b,
+int oracle_route(const int32_t* dims, float top_p, const uint16_t* x, int32_t T, const float* Wr, const float* b,
                  int32_t* topk_idx, float* topk_w, double* z_out, int32_t* n_unique, int32_t* uniq_ids,
                  int32_t* uniq_off, int32_t* pairs) {
   const Dims d = to_dims(dims);
@@ -341,7 +327,7 @@ int oracle_route(const int32_t* dims, double top_p, const uint16_t* x, int32_t T
 //   tensor scales (gate, up, down), or NULL meaning 1.0.
 //   y: fp64 [n_list][H].  Returns 0, or -1 on bad arguments, -2 when a
 //   selected expert pointer is NULL.
-int oracle_forward(const int32_t* dims, double top_p, const void* const* qg, const void* const* sg, const void* const* qu,
+int oracle_forward(const int32_t* dims, float top_p, const void* const* qg, const void* const* sg, const void* const* qu,
                    const void* const* su, const void* const* qd, const void* const* sd, const float* g3,
                    const float* Wr, const float* b, const uint16_t* x, int32_t T, const int32_t* token_list,
                    int32_t n_list, double* y, int32_t n_threads) {

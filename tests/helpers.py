@@ -46,15 +46,16 @@ def min_topk_gap(r, k):
 
 
 def top_p_margin(r, k, p):
-    """Smallest distance, over tokens and slots, between p and a prefix sum
-    of the binary32 slot weights that adaptive top-p compares with it (the
-    GPU and the oracle may round the sigmoid differently by an ulp, so cases
-    must keep clear of the threshold).  r: a plain top-k oracle route (z set)."""
+    """Smallest distance, over tokens and slots, between p (the layer's
+    binary32 threshold) and a prefix sum of the renormalised slot weights in
+    fp64.  The GPU and the oracle take the kept-slot decision in fp64, but
+    their exp and summation order may differ in the last bits, so cases must
+    keep clear of the threshold.  r: a plain top-k oracle route (z set)."""
+    p32 = float(np.float32(p))
     margin = np.inf
     for t in range(r.topk_idx.shape[0]):
-        zs = r.z[t, r.topk_idx[t]].astype(np.float32)
-        s = (np.float32(1.0) / (np.float32(1.0) + np.exp(-zs))).astype(np.float32)
-        tot = np.float32(s.astype(np.float64).sum())
-        cum = np.cumsum((s / tot).astype(np.float64))
-        margin = min(margin, float(np.min(np.abs(cum - p))))
+        zs = r.z[t, r.topk_idx[t]].astype(np.float64)
+        s = 1.0 / (1.0 + np.exp(-zs))
+        cum = np.cumsum(s / s.sum())
+        margin = min(margin, float(np.min(np.abs(cum - p32))))
     return margin

@@ -190,6 +190,31 @@ def test_dequant_matches_independent_decode(orc, fmt):
         assert np.array_equal(got, _np_dequant(layer, 1, which))
 
 
+@pytest.mark.parametrize("fmt", ALL_FMTS)
+def test_dequant_every_code_matches_independent_decode(orc, fmt):
+    """The crafted layer that writes every code of a format (int4 -8, int8
+    -128, every e4m3 block scale including zero and the subnormals,
+    binary16-subnormal row scales): the oracle's weights equal the
+    independent numpy/torch decode on every matrix."""
+    dims = synth.Dims(128, 128, 16, 16, 1, fmt)
+    layer = synth.make_code_sweep_layer(dims, ("sweep-pin", fmt))
+    for e in range(layer.n_stored):
+        for m, which in enumerate(("gate", "up", "down")):
+            rows, cols = (128, 128)
+            got = orc.dequant(fmt, getattr(layer, "q_" + which)[e], getattr(layer, "s_" + which)[e],
+                              float(layer.g3[e, m]), rows, cols)
+            assert np.array_equal(got, _np_dequant(layer, e, which)), (e, which)
+    if fmt == synth.E2M1_B16:
+        codes = set()
+        for which in ("gate", "up", "down"):
+            codes |= set(getattr(layer, "s_" + which).flatten().tolist())
+        assert len(codes) == 254 and 0x7F not in codes and 0xFF not in codes
+    else:
+        s = layer.s_gate.float()
+        if fmt == synth.INT8_ROW:
+            assert bool((s < 2.0 ** -14).any()), "some binary16-subnormal row scales"
+
+
 # ---- routing -------------------------------------------------------------
 def _tiny_route_layer(E, k, H=64, seed=0, bias=False):
     dims = synth.Dims(H, 32, E, k, 1, synth.INT4_ROW)
@@ -358,31 +383,22 @@ def test_token_permutation_equivariance(orc):
 
 
 # ---- adaptive top-p (prefix rule) -------------------------------------------
+# "Show HN: 低速のコンピュータでGLM 5.2を動かす方法", section 実行・チューニングパラメータ
+# (--topp 0.7, adaptive expert top-p); the shortest-prefix rule is the reading taken.
 def _np_keep(z_slots: np.ndarray, k: int, p: float):
-    """Kept-slot count by the rule, in binary32 as the GPU path takes it:
-    sigmoid of the binary32 logit, a pairwise tree sum over 64 lanes, the
-    weights' prefix sums in slot order against p.  Also returns the smallest
-    distance of a prefix sum from p (cases closer than 1e-5 are skipped)."""
-    if not (0.0 < p < 1.0):
+    """Kept-slot count by the rule, stated independently in fp64 numpy: the
+    ranked slots' sigmoid scores (scipy's expit), renormalised to sum to one,
+    cumulated in slot order (np.cumsum); the count is one more than the first
+    index whose cumulative weight reaches p (the layer's binary32 p).  Also
+    returns the smallest distance of a prefix sum from p."""
+    p32 = float(np.float32(p))
+    if not (0.0 < p32 < 1.0):
         return k, 1.0
-    s = np.zeros(64, dtype=np.float32)
-    s[:k] = (np.float32(1.0) / (np.float32(1.0) + np.exp(-z_slots.astype(np.float32)))).astype(np.float32)
-    v = s.copy()
-    width = 1
-    while width < 64:
-        v = (v.reshape(-1, 2, width)[:, 0, :] + v.reshape(-1, 2, width)[:, 1, :]).astype(np.float32)
-        v = np.repeat(v[:, None, :], 2, axis=1).reshape(-1)
-        width *= 2
-    tot = v[0]
-    cum = np.float32(0.0)
-    margin = 1.0
-    m = k
-    for j in range(k):
-        cum = np.float32(cum + np.float32(s[j] / tot))
-        margin = min(margin, abs(float(cum) - p))
-        if cum >= np.float32(p) and m == k:
-            m = j + 1
-    return m, margin
+    s = expit(np.asarray(z_slots, dtype=np.float64))
+    cum = np.cumsum(s / s.sum())
+    reach = np.nonzero(cum >= p32)[0]
+    m = int(reach[0]) + 1 if reach.size else k
+    return m, float(np.min(np.abs(cum - p32)))
 
 
 @pytest.mark.parametrize("E,k,bias,p", [(10, 4, False, 0.5), (10, 4, True, 0.7), (8, 3, False, 0.4),
@@ -410,19 +426,22 @@ def test_top_p_keeps_shortest_prefix(orc, E, k, bias, p):
 
 
 def test_top_p_equal_logits_exact_counts(orc):
-    """Equal router rows give equal logits, so every weight is exactly 1/k
-    (k = 8: 0.125) and the prefix sums are exact: p picks the count."""
+    """Zero router weights give every expert the logit 0, so every score is
+    exactly 1/2, ties go to the lower index (experts 0..k-1), every
+    renormalised weight is exactly 1/k (k = 8: 0.125) and every prefix sum is
+    exact: p alone picks the count, including p exactly on a prefix sum
+    (0.625, 0.75: "reaches" means >=)."""
     E, k = 12, 8
     dims = synth.Dims(64, 32, E, k, 1, synth.INT4_ROW)
-    rw, _ = synth.make_router(dims, ("eq", E))
-    rw = rw[:1].repeat(E, 1).contiguous()
+    rw = torch.zeros((E, 64), dtype=torch.float32)
     x = synth.make_tokens(dims, 2, ("eq", E))
     for p, m in [(0.625, 5), (0.626, 6), (0.7, 6), (0.75, 6), (0.7500001, 7), (1e-6, 1), (0.9999, 8)]:
         r = orc.route(dims, x, rw, None, top_p=p)
         for t in range(2):
             assert list(r.topk_idx[t, :m]) == list(range(m)), (p, r.topk_idx[t])
-            assert np.all(r.topk_idx[t, m:] == -1)
-            np.testing.assert_allclose(r.topk_w[t, :m], np.full(m, 1.0 / m), rtol=1e-7)
+            assert np.all(r.topk_idx[t, m:] == -1), (p, r.topk_idx[t])
+            assert np.all(r.topk_w[t, :m] == np.float32(1.0 / m)), (p, r.topk_w[t])
+        assert _np_keep(np.zeros(k), k, p)[0] == m
 
 
 def test_top_p_zero_and_one_keep_all_slots(orc):
