@@ -117,7 +117,14 @@ size_t moe_workspace_bytes(const moe_dims_t* d, int32_t T);
 size_t moe_workspace_sync_bytes(const moe_dims_t* d);
 
 /* Canonical expert -> packed device layout (a byte permutation; the values
- * are unchanged).  Canonical inputs, all row-major on the device, with
+ * are unchanged).  It plays the role of the offline weight converter of the
+ * Colibrì engine ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法",
+ * hakusoku.com, section 実装済み機能, the FP8 -> int4 offline conversion
+ * tool), minus the quantisation: the codes and scales are given.  Run once
+ * per expert when the weights are loaded, not per call.  Errors: MOE_E_INVAL
+ * for a null or misaligned pointer (16 B; packed_out 256 B; g3 4 B),
+ * MOE_E_UNSUPPORTED / MOE_E_INVAL for dims outside the supported set,
+ * MOE_E_HIP if a launch fails.  Canonical inputs, all row-major on the device, with
  * b = 8 (INT8_ROW), 2 (INT2_ROW) or 4 (the others) bits per code:
  *   q_gate, q_up: uint8 [I][H*b/8]; q_down: uint8 [H][I*b/8];
  *     4-bit codes: element 2j in the low nibble of byte j, element 2j+1 in
@@ -140,14 +147,17 @@ int moe_unpack(const moe_dims_t* d, const void* packed, void* q_gate, void* s_ga
 /* Router and batch union for T tokens (x: binary16 [T][H]).
  * Logits are accumulated in fp64: z[t][e] = b[e] + sum_h x[t][h]*Wr[e][h].
  * Experts are ranked by (z descending, index ascending); the first k are
- * kept in that order.  w[t][j] = sigmoid(z_j) / sum_j' sigmoid(z_j').
- * Adaptive top-p ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法",
- * hakusoku.com, section 実装済み機能, the top-p expert option), when
+ * kept in that order.  w[t][j] = sigmoid(z_j) / sum_j' sigmoid(z_j'),
+ * formed in fp64 and rounded to fp32.
+ * Adaptive expert top-p ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法",
+ * hakusoku.com, section 実行・チューニングパラメータ, the --topp option), when
  * 0 < d->top_p < 1: only the shortest prefix of the k slots whose
- * cumulative weight reaches top_p is kept (the decision is taken in
- * binary32: sigmoid of the binary32 logit, a pairwise sum over the slots,
- * prefix sums in slot order), and the kept weights are renormalised over
- * the kept slots; dropped slots get topk_idx = -1 and topk_w = 0.
+ * cumulative weight (fp64, summed in slot order) reaches top_p is kept, and
+ * the kept weights are renormalised over the kept slots; dropped slots get
+ * topk_idx = -1 and topk_w = 0.
+ * Batches of T <= moe_decode_max_tokens() are routed by the same router
+ * workgroups as the GEMV path of moe_w4a16_forward, larger ones by the
+ * batched router of the grouped-GEMM path.
  * Outputs:
  *   topk_idx int32 [T][k], topk_w fp32 [T][k];
  *   n_unique int32 [1]: distinct experts chosen by the batch;

@@ -226,8 +226,9 @@ int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, in
   r.uniq_ids = uniq_ids;
   r.uniq_off = uniq_off;
   r.pairs = pairs;
-  if (launch_route(*d, p, *w, x, r, false, (hipStream_t)stream) != hipSuccess) return MOE_E_HIP;
-  return MOE_OK;
+  const hipError_t e = p.decode ? launch_decode_route(*d, p, *w, x, r, ws, (hipStream_t)stream)
+                               : launch_route(*d, p, *w, x, r, false, (hipStream_t)stream);
+  return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
 static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,

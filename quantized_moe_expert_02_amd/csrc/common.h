@@ -168,6 +168,10 @@ inline void launch_k(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_
   else hipLaunchKernelGGL(kernel, grid, block, 0, s, args...);
 }
 
+// Routing and union for T <= kDecodeMaxTokens (moe_route): the router
+// workgroups of the decode path's routing launch, without the slot table.
+hipError_t launch_decode_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
+                               const Route& r, void* ws, hipStream_t s);
 // The whole layer for T <= kDecodeMaxTokens in three launches: route +
 // shared gate/up, routed gate/up, down (stages 0, 1, 2).
 hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
@@ -181,8 +185,11 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
 // not coherent with each other for ordinary stores, and a device-scope fence
 // writes back and invalidates the whole L2.  Data handed between workgroups
 // is therefore written and read with device-scope relaxed atomic accesses
-// (which the hardware keeps coherent), and a unit publishes its arrival only
-// after all of its stores have completed (s_waitcnt 0).
+// (st_dev / ld_dev, which bypass the XCD-private cache state and stay
+// coherent across XCDs), and a unit publishes its arrival only after all of
+// its stores have completed (s_waitcnt 0).  A reader issues its ld_dev loads
+// only after the arrival that tells it the data is complete.  No plain load
+// ever reads data written by another workgroup of the same launch.
 // ---------------------------------------------------------------------------
 template <typename T>
 __device__ __forceinline__ void st_dev(T* p, T v) {

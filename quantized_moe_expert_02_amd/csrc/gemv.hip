@@ -272,8 +272,9 @@ __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const 
 // "Last" is decided by device-scope arrival counters, which that unit
 // returns to zero, so every call starts from zeroed counters.  Data handed
 // to another workgroup of the same launch is written with device-coherent
-// stores and read after the arrival that publishes it (common.h); the launch
-// boundaries order the phases, so no unit ever waits for another.
+// stores and read with device-coherent loads after the arrival that
+// publishes it (common.h); the launch boundaries order the phases, so no
+// unit ever waits for another.
 // ===========================================================================
 
 constexpr int kWpg = 4;           // wavefronts per workgroup
@@ -315,6 +316,7 @@ struct DecArgs {
   int rsplit, seg4;   // router units per expert, 16-byte columns per router unit
   int n_router;       // E * rsplit
   int n_router_wg;    // workgroups of router units
+  int with_slots;     // forward: also write the slot table (moe_route: no)
 };
 
 struct SlotInfo {
@@ -428,11 +430,13 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
       if (c > 0) {
         a.uniq_ids[up] = e;
         a.uniq_off[up] = uc;
-        SlotEntry se;
-        se.base = ls.ep[e];
-        se.n = c;
-        se.p0 = uc;
-        a.slots[a.S + up] = se;
+        if (a.with_slots) {
+          SlotEntry se;
+          se.base = ls.ep[e];
+          se.n = c;
+          se.p0 = uc;
+          a.slots[a.S + up] = se;
+        }
         ++up;
       }
       uc += c;
@@ -444,7 +448,8 @@ __device__ __forceinline__ void union_step(const DecArgs& a, UnionLds& ls) {
     *a.n_unique = nu;
     a.uniq_off[nu] = tot & 0xFFFF;
   }
-  for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
+  if (a.with_slots)
+    for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
   wave_lds_sync();
   for (int p = lane; p < P; p += 64) {
     const int e = ls.pe[p];
@@ -471,18 +476,21 @@ __device__ __forceinline__ void union_one(const DecArgs& a, UnionLds& ls) {
   if (e >= 0) {
     a.uniq_ids[r] = e;
     a.uniq_off[r] = r;
-    SlotEntry se;
-    se.base = ls.ep[e];
-    se.n = 1;
-    se.p0 = r;
-    a.slots[a.S + r] = se;
+    if (a.with_slots) {
+      SlotEntry se;
+      se.base = ls.ep[e];
+      se.n = 1;
+      se.p0 = r;
+      a.slots[a.S + r] = se;
+    }
     a.pairs[r] = lane;
   }
   if (lane == 0) {
     *a.n_unique = nu;
     a.uniq_off[nu] = nu;
   }
-  for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
+  if (a.with_slots)
+    for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
 }
 
 // ---- router unit: fp64 partial logits of expert e over one column segment --
@@ -569,7 +577,7 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
   // The last wavefront stages the expert pointers the union needs in LDS
   // (wavefront 0, which ranks the first token, does not wait for them).
-  if (wave == kWpg - 1)
+  if (wave == kWpg - 1 && a.with_slots)
     for (int e = lane; e < a.E; e += 64) ls.ep[e] = (const uint8_t*)a.experts[e];
   const int tpw = (a.T + kWpg - 1) / kWpg;
   const int t0 = wave * tpw, t1 = min(a.T, t0 + tpw);
@@ -742,8 +750,8 @@ __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __res
       for (int q = 0; q < 8; ++q) {
         if (q0 + q < ngrp) {
           const float* pr = a.p_gu + (((size_t)(q0 + q) * a.rows_total + row) * 2) * a.I + 64 * rb + lane;
-          pg[q] = pr[0];
-          pu[q] = pr[a.I];
+          pg[q] = ld_dev(pr);
+          pu[q] = ld_dev(pr + a.I);
         }
       }
 #pragma unroll
@@ -863,7 +871,7 @@ __device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rbg, DnLds<
       for (int jj = 0; jj < 8; ++jj) {
         const int j = j0 + jj;
         const int row = (j < a.k) ? t * a.k + j : a.T * a.k + t;
-        o[jj] = (j < a.k + a.S) ? a.p_dn[(size_t)row * a.H + r] : 0.f;
+        o[jj] = (j < a.k + a.S) ? ld_dev(a.p_dn + (size_t)row * a.H + r) : 0.f;
         ej[jj] = (j < a.k && a.top_p_on) ? a.topk_idx[t * a.k + j] : 0;
         wj[jj] = (j < a.k) ? a.topk_w[t * a.k + j] : 1.f;
       }
@@ -892,6 +900,13 @@ __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint
   const int nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw, n_rbg = (a.I / 64) * ngrp;
   const int j = b - a.n_router_wg, r = j % n_rbg;
   gu_group<FMT, KT>(a, x, 0, r / ngrp, r % ngrp, ngrp, nw, a.cpu_sgu, j / n_rbg, (a.T + KT - 1) / KT, gl);
+}
+
+// moe_route on small batches: the router workgroups of k_route_phase alone
+// (no shared expert, no slot table).
+__global__ __launch_bounds__(64 * kWpg) void k_route_only(DecArgs a) {
+  __shared__ UnionLds ul;
+  router_workgroup(a, ul);
 }
 
 template <int FMT, int KT>
@@ -923,10 +938,8 @@ hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, con
   return hipGetLastError();
 }
 
-}  // namespace
-
-hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
-                         const Route& r, void* ws, uint16_t* y, hipStream_t s, const StageEvents& se) {
+DecArgs dec_args(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x, const Route& r,
+                 void* ws, uint16_t* y, bool with_slots) {
   DecArgs a{};
   a.Wr = w.router_w;
   a.rbias = w.router_b;
@@ -972,6 +985,22 @@ hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t
   a.seg4 = (n4 + a.rsplit - 1) / a.rsplit;
   a.n_router = p.E * a.rsplit;
   a.n_router_wg = (a.n_router + kWpg - 1) / kWpg;
+  a.with_slots = with_slots ? 1 : 0;
+  return a;
+}
+
+}  // namespace
+
+hipError_t launch_decode_route(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
+                               const Route& r, void* ws, hipStream_t s) {
+  const DecArgs a = dec_args(d, p, w, x, r, ws, nullptr, false);
+  hipLaunchKernelGGL(k_route_only, dim3(a.n_router_wg), dim3(64 * kWpg), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, const uint16_t* x,
+                         const Route& r, void* ws, uint16_t* y, hipStream_t s, const StageEvents& se) {
+  const DecArgs a = dec_args(d, p, w, x, r, ws, y, true);
   // a single token never needs the two-token tiles, which cost registers
   switch (d.wfmt) {
     case MOE_W_INT4_ROW:

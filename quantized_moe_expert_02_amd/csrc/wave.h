@@ -58,22 +58,6 @@ __device__ __forceinline__ double from_order_key(uint64_t k) {
   return __builtin_bit_cast(double, u);
 }
 
-// Adaptive top-p over the k ranked slots held by lanes 0..k-1 (s: binary32
-// sigmoid of the slot's logit, 0 on lanes >= k; tot: its wave-wide sum).
-// Returns the number of kept slots: the shortest prefix whose cumulative
-// weight s_j / tot, summed in slot order in binary32, reaches p (k when p
-// is 0 or >= 1).
-__device__ __forceinline__ int top_p_keep(float s, float tot, int k, float p) {
-  if (!(p > 0.0f && p < 1.0f)) return k;
-  const float w = s / tot;
-  float cum = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    cum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), j));
-    if (cum >= p) return j + 1;
-  }
-  return k;
-}
-
 // Every lane ends with the wave-wide fp32 sum, added as a pairwise tree
 // (lanes 2i and 2i+1 first, then pairs of pairs, ...), the same on every lane.
 __device__ __forceinline__ float wave_sum_f32(float v) {
@@ -84,6 +68,57 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   v += __builtin_bit_cast(float, partner<16>(__builtin_bit_cast(int, v)));
   v += __builtin_bit_cast(float, partner<32>(__builtin_bit_cast(int, v)));
   return v;
+}
+
+// Every lane ends with the wave-wide fp64 sum, added in a fixed butterfly order.
+__device__ __forceinline__ double wave_sum(double v) {
+  v += partner_d<1>(v);
+  v += partner_d<2>(v);
+  v += partner_d<4>(v);
+  v += partner_d<8>(v);
+  v += partner_d<16>(v);
+  v += partner_d<32>(v);
+  return v;
+}
+
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Routing weights of the k ranked slots, slot j held by lane j (z: its fp64
+// logit; lanes >= k hold nothing).  In fp64: s = sigmoid(z), w = s / sum(s)
+// over the kept slots, rounded to fp32 at the end.  Adaptive expert top-p
+// ("Show HN: 低速のコンピュータでGLM 5.2を動かす方法", hakusoku.com, section
+// 実行・チューニングパラメータ, the --topp option), for 0 < top_p < 1: the kept
+// slots are the shortest prefix whose cumulative weight s_j / sum(s), summed
+// in slot order, reaches top_p (the reading taken); the others are dropped.
+// Returns the kept count m (k without top-p) and this lane's weight (0 for
+// lanes >= m).
+struct SlotWeight {
+  int m;
+  float w;
+};
+__device__ __forceinline__ SlotWeight slot_weights(double z, int k, float top_p) {
+  const int lane = threadIdx.x & 63;
+  const double s = lane < k ? 1.0 / (1.0 + exp(-z)) : 0.0;
+  double tot = wave_sum(s);
+  int m = k;
+  if (top_p > 0.0f && top_p < 1.0f) {
+    const double p = (double)top_p, w = s / tot;
+    double cum = 0.0;
+    for (int j = 0; j < k; ++j) {
+      cum += readlane_d(w, j);
+      if (cum >= p) {
+        m = j + 1;
+        break;
+      }
+    }
+    if (m < k) tot = wave_sum(lane < m ? s : 0.0);
+  }
+  return SlotWeight{m, lane < m ? (float)(s / tot) : 0.0f};
 }
 
 // Inclusive prefix sum over the lanes (lane l gets v_0 + ... + v_l): row
@@ -123,8 +158,7 @@ __device__ __forceinline__ void wave_argmax_key(uint64_t& key, int& idx) {
 // Top-k of one token's logits by one wavefront: k rounds of a wave-wide
 // argmax over the experts not yet taken.  Lane l holds experts l + 64 i.
 // Writes idx/w for slots 0..k-1 and the chosen experts to slot_expert.
-// The routing weights are formed in fp32: sigmoid of the fp64 logit, then
-// renormalised over the kept slots.
+// The routing weights are formed by slot_weights (fp64).
 // The logit of expert e is zrow[e], or with kCoherent the sum of nz partial
 // logits zrow[s * zstride + e] (s ascending) plus bias[e] when bias is set.
 template <int kPer, bool kCoherent>
@@ -150,7 +184,7 @@ __device__ void topk_wave(const double* zrow, int nz, size_t zstride, const floa
 #pragma unroll
         for (int s = 0; s < PG; ++s) {
           const int e = lane + i * kWave;
-          if (e < E && s0 + s < nz) zs[i][s] = zrow[(s0 + s) * zstride + e];
+          if (e < E && s0 + s < nz) zs[i][s] = ld_dev(zrow + (s0 + s) * zstride + e);
         }
 #pragma unroll
       for (int i = 0; i < kPer; ++i)
@@ -194,14 +228,10 @@ __device__ void topk_wave(const double* zrow, int nz, size_t zstride, const floa
       my_e = bi;
     }
   }
-  const double my_z = from_order_key(my_key);
-  const float s = (lane < k) ? 1.0f / (1.0f + expf(-(float)my_z)) : 0.0f;
-  float tot = wave_sum_f32(s);
-  const int m = top_p_keep(s, tot, k, top_p);
-  if (m < k) tot = wave_sum_f32(lane < m ? s : 0.0f);
+  const SlotWeight sw = slot_weights(from_order_key(my_key), k, top_p);
   if (lane < k) {
-    const int32_t e_out = lane < m ? my_e : -1;
-    const float w = lane < m ? s / tot : 0.0f;
+    const int32_t e_out = lane < sw.m ? my_e : -1;
+    const float w = sw.w;
     if (kCoherent) {
       st_dev(idx_out + lane, e_out);
       st_dev(w_out + lane, w);
@@ -267,7 +297,7 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
 #pragma unroll
         for (int i = 0; i < kPer; ++i) {
           const int e = lane + i * kWave;
-          zs[s][t][i] = (e < E && s0 + s < nz) ? z[(s0 + s) * zstride + (size_t)t * E + e] : 0.0;
+          zs[s][t][i] = (e < E && s0 + s < nz) ? ld_dev(z + (s0 + s) * zstride + (size_t)t * E + e) : 0.0;
         }
 #pragma unroll
     for (int s = 0; s < PG; ++s)
@@ -346,15 +376,11 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
   }
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const double my_z = from_order_key(my_key[t]);
-    const float s = (lane < k) ? 1.0f / (1.0f + expf(-(float)my_z)) : 0.0f;
-    float tot = wave_sum_f32(s);
-    const int m = top_p_keep(s, tot, k, top_p);
-    if (m < k) tot = wave_sum_f32(lane < m ? s : 0.0f);
+    const SlotWeight sw = slot_weights(from_order_key(my_key[t]), k, top_p);
     if (lane < k) {
-      const int32_t e_out = lane < m ? my_e[t] : -1;
+      const int32_t e_out = lane < sw.m ? my_e[t] : -1;
       st_dev(idx_out + t * k + lane, e_out);
-      st_dev(w_out + t * k + lane, lane < m ? s / tot : 0.0f);
+      st_dev(w_out + t * k + lane, sw.w);
       if (slot_expert) slot_expert[t * k + lane] = e_out;
     }
   }
@@ -380,17 +406,6 @@ __device__ __forceinline__ void topk_tokens(const double* z, int nz, size_t zstr
   else if (E <= 256) topk_tokens_per<4>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
   else if (E <= 512) topk_tokens_per<8>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
   else topk_tokens_per<16>(z, nz, zstride, bias, E, k, top_p, T, idx_out, w_out, slot_expert, rs);
-}
-
-// Every lane ends with the wave-wide fp64 sum, added in a fixed butterfly order.
-__device__ __forceinline__ double wave_sum(double v) {
-  v += partner_d<1>(v);
-  v += partner_d<2>(v);
-  v += partner_d<4>(v);
-  v += partner_d<8>(v);
-  v += partner_d<16>(v);
-  v += partner_d<32>(v);
-  return v;
 }
 
 }  // namespace moe

@@ -341,9 +341,43 @@ def test_prefill_max_experts():
     assert_close(y, y_ref, "emax")
 
 
+def _prefill_sample(r, T, k, n_total=288, seed=11):
+    """Tokens of prefill_2048 to compare with the oracle, chosen from the
+    oracle's own union so that they cover the grouped GEMM's tile kinds:
+    tokens of gate/up tiles with a single filled 16-token group, of full
+    64-token gate/up tiles, every token of the heaviest expert's last
+    partial gate/up tile, the first and last token of its last partial
+    128-token down tile, then a seeded random fill (which also spreads over
+    the shared expert's 64-token tiles)."""
+    rng = np.random.default_rng(seed)
+    per_expert = []
+    for u in range(r.n_unique):
+        toks = (r.pairs[r.uniq_off[u]:r.uniq_off[u + 1]] // k).tolist()
+        per_expert.append(toks)
+    tiles = [(u, toks[i:i + 64]) for u, toks in enumerate(per_expert) for i in range(0, len(toks), 64)]
+    one_group = [tl for tl in tiles if len(tl[1]) <= 16]
+    full = [tl for tl in tiles if len(tl[1]) == 64]
+    heavy = max(range(len(per_expert)), key=lambda u: len(per_expert[u]))
+    ht = per_expert[heavy]
+    last_gu = ht[(len(ht) - 1) // 64 * 64:]
+    last_dn = ht[(len(ht) - 1) // 128 * 128:]
+    pick = set(last_gu) | {last_dn[0], last_dn[-1]}
+    for i in rng.permutation(len(one_group))[:48]:
+        pick.add(int(rng.choice(one_group[i][1])))
+    for i in rng.permutation(len(full))[:24]:
+        pick |= {full[i][1][0], full[i][1][-1]}
+    rest = [t for t in rng.permutation(T).tolist() if t not in pick]
+    pick |= set(rest[:max(0, n_total - len(pick))])
+    info = dict(one_group_tiles=len(one_group), full_tiles=len(full), heavy_tokens=len(ht),
+                heavy_last_gu=len(last_gu), heavy_last_dn=len(last_dn))
+    return sorted(int(t) for t in pick), one_group, full, last_gu, last_dn, info
+
+
+@pytest.mark.timeout(600)
 def test_prefill_full_size_sampled():
     """2048 tokens through the full decode-size layer with a Zipf-skewed router
-    bias: routing checked for every token, outputs on a seeded sample."""
+    bias: routing checked for every token; outputs of >= 256 tokens that
+    cover every tile kind of the grouped GEMMs checked against the oracle."""
     _log("prefill full size")
     layer, x = synth.workload("prefill_2048", device=DEV)
     r = oracle_route(layer, x)
@@ -357,7 +391,15 @@ def test_prefill_full_size_sampled():
     assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
     np.testing.assert_allclose(tw.cpu().numpy(), r.topk_w, rtol=1e-6)
     assert torch.isfinite(y).all()
-    sample = sorted(np.random.default_rng(11).choice(T, size=24, replace=False).tolist())
+    sample, one_group, full, last_gu, last_dn, info = _prefill_sample(r, T, k)
+    _log(f"  sample of {len(sample)} tokens; tiles: {info}")
+    assert len(sample) >= 256
+    assert one_group and full and 0 < len(last_gu) < 64 and len(last_dn) < 128
+    ss = set(sample)
+    assert sum(1 for tl in one_group if ss & set(tl[1])) >= 16
+    assert sum(1 for tl in full if ss & set(tl[1])) >= 8
+    assert set(last_gu) <= ss and last_dn[0] in ss and last_dn[-1] in ss
+    assert len({t // 64 for t in sample}) == T // 64  # every shared-expert tile
     y_ref = oracle_y(layer, x, tokens=sample)
     rel, mx = assert_close(y[sample], y_ref, "prefill_2048 sample")
     _log(f"  prefill_2048: U={r.n_unique} max tokens/expert={np.bincount(r.topk_idx.ravel()).max()} "
@@ -411,6 +453,27 @@ def test_route_top_p_matches_oracle(dims, T):
     out = moe.moe_route(layer, x.to(DEV))
     torch.cuda.synchronize()
     _check_route(out, r, T, dims.top_k)
+
+
+@pytest.mark.parametrize("T", [2, 20])
+def test_route_top_p_exact_boundaries(T):
+    """Zero router weights: every logit is 0, every score exactly 1/2, ties go
+    to the lower index, and the renormalised weights (1/8) and their prefix
+    sums are exact, so p alone decides the kept count, also with p exactly
+    on a prefix sum (0.625, 0.75: "reaches" is >=).  T = 2 runs the decode
+    path's router, T = 20 the batched one."""
+    E, k = 12, 8
+    _log("route top-p exact boundaries", T)
+    x = synth.make_tokens(synth.Dims(256, 128, E, k, 1, 0), T, ("topp-exact", T))
+    rw = torch.zeros((E, 256), dtype=torch.float32)
+    for p, m in [(0.625, 5), (0.626, 6), (0.7, 6), (0.75, 6), (0.7500001, 7), (1e-6, 1), (0.9999, 8)]:
+        dims = synth.Dims(256, 128, E, k, 1, 0, top_p=p)
+        r = oracle.route(dims, x, rw, None)
+        assert np.all((r.topk_idx >= 0).sum(axis=1) == m), p
+        layer = moe.PackedLayer(dims, torch.zeros((E + 1, 256), dtype=torch.uint8, device=DEV), rw.to(DEV), None)
+        out = moe.moe_route(layer, x.to(DEV))
+        torch.cuda.synchronize()
+        _check_route(out, r, T, k)
 
 
 TOPP_FORWARD_CASES = [
