@@ -79,7 +79,7 @@ WORKLOADS = {
     "tiny": dict(dims=Dims(256, 128, 8, 2, 1, INT4_ROW), tokens=4),
     "decode_b1": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=1),
     "decode_b8": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW), tokens=8),
-    # adaptive expert top-p 0.7 (hakusoku.com story 8412, section 実装済み機能)
+    # adaptive expert top-p 0.7 (hakusoku.com story 8412, section 実行・チューニングパラメータ)
     "decode_b1_topp": dict(dims=Dims(6144, 2048, 256, 8, 1, INT4_ROW, top_p=0.7), tokens=1),
     "e2m1_b1": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=1),
     "e2m1_b4": dict(dims=Dims(2048, 512, 256, 8, 1, E2M1_B16), tokens=4),
@@ -243,6 +243,81 @@ def make_layer(dims: Dims, seed_tag, device="cpu", zipf: float = 0.0) -> Layer:
     qg, sg, qu, su, qd, sd, g3 = make_experts(dims, n, (seed_tag, "experts"), device=device)
     rw, rb = make_router(dims, seed_tag, device=device, zipf=zipf)
     return Layer(dims, qg, sg, qu, su, qd, sd, g3, rw, rb)
+
+
+# ---- crafted codes: every stored code value --------------------------------
+# The random encoders above never emit some codes (int4 -8, int8 -128: they
+# scale by amax/7 and amax/127) and pin the e2m1 block scales near the top of
+# the e4m3 range.  The layers below write codes directly, so that every code
+# of a format appears: integer codes cycle through all 2^bits two's-complement
+# values along each row (from a seeded random offset per row); e2m1 codes
+# cycle through all 16 codes inside every 16-column block; e2m1 block scales cycle
+# through one e4m3 binade ("band": exponent field b, both signs, every
+# mantissa) per matrix, so that all 254 finite e4m3 codes -- zero and the
+# subnormals (b = 0) included -- appear across a layer's matrices, each in a
+# matrix where its blocks carry the weight.  Row scales (integer formats)
+# cycle through factors 1/16 .. 2 of a base chosen so that the weights have a
+# spread near 0.02 (int8 rows at 1/16 get binary16-subnormal scales); the
+# e2m1 tensor scale g of a matrix brings its band to the same spread.
+_ROW_FACTORS = (1.0 / 16, 0.25, 0.5, 1.0, 1.5, 2.0)
+_CODE_SPREAD = {INT4_ROW: 4.6, INT8_ROW: 74.0, INT2_ROW: 1.1}
+
+
+def e4m3_band_codes(b: int):
+    """The finite e4m3 codes with exponent field b (0..15), both signs."""
+    pos = [(b << 3) | m for m in range(8) if not (b == 15 and m == 7)]
+    return pos + [0x80 | c for c in pos]
+
+
+def _sweep_fields(rows: int, cols: int, n: int, seed_tag) -> torch.Tensor:
+    """Row r holds (c + o_r) mod n along its columns, o_r a seeded random
+    offset: every row walks the whole code cycle, and rows are not periodic
+    (a periodic pattern lets the down projection cancel exactly)."""
+    off = torch.randint(0, n, (rows, 1), generator=_gen("cpu", seed_tag, "sweep"))
+    c = torch.arange(cols).unsqueeze(0)
+    return ((c + off) % n).to(torch.int64)
+
+
+def _pack_fields(u: torch.Tensor, wfmt: int) -> torch.Tensor:
+    """Unsigned fields (two's-complement bit patterns) -> canonical bytes."""
+    if wfmt == INT8_ROW:
+        return u.to(torch.uint8).contiguous()
+    if wfmt == INT2_ROW:
+        c = u.to(torch.uint8)
+        return (c[..., 0::4] | (c[..., 1::4] << 2) | (c[..., 2::4] << 4) | (c[..., 3::4] << 6)).contiguous()
+    return pack_nibbles(u)
+
+
+def make_code_sweep_layer(dims: Dims, seed_tag, band_of=None) -> Layer:
+    """A layer whose stored codes cover every value of its format (see above).
+    band_of(e, m) picks the e4m3 band of matrix m (0 gate, 1 up, 2 down) of
+    expert e (default (3e + m) mod 16).  The router is the usual random one."""
+    H, I = dims.hidden, dims.inter
+    n = dims.n_experts + (1 if dims.has_shared else 0)
+    if band_of is None:
+        band_of = lambda e, m: (3 * e + m) % 16  # noqa: E731
+    qs, ss = [[], [], []], [[], [], []]
+    g3 = torch.ones((n, 3), dtype=torch.float32)
+    for e in range(n):
+        for m, (rows, cols) in enumerate(((I, H), (I, H), (H, I))):
+            if dims.wfmt in ROW_SCALED:
+                nb = 1 << code_bits(dims.wfmt)
+                qs[m].append(_pack_fields(_sweep_fields(rows, cols, nb, (seed_tag, e, m, "q")), dims.wfmt))
+                base = 0.02 / _CODE_SPREAD[dims.wfmt]
+                f = torch.tensor([_ROW_FACTORS[(r + e + m) % len(_ROW_FACTORS)] for r in range(rows)])
+                ss[m].append((base * f).to(torch.float16))
+            else:
+                qs[m].append(_pack_fields(_sweep_fields(rows, cols, 16, (seed_tag, e, m, "q")), dims.wfmt))
+                band = e4m3_band_codes(band_of(e, m))
+                idx = _sweep_fields(rows, cols // 16, len(band), (seed_tag, e, m, "s"))
+                sc = torch.tensor(band, dtype=torch.uint8)[idx]
+                mags = torch.tensor(band, dtype=torch.uint8).view(torch.float8_e4m3fn).float().abs()
+                typ = float(mags[mags > 0].mean())
+                g3[e, m] = 0.02 / (2.25 * typ)  # 2.25: mean |e2m1| over the 16 codes
+                ss[m].append(sc.contiguous())
+    rw, rb = make_router(dims, (seed_tag, "router"))
+    st = [torch.stack(v) for v in ss]
+    return Layer(dims, torch.stack(qs[0]), st[0], torch.stack(qs[1]), st[1], torch.stack(qs[2]), st[2], g3, rw, rb)
 
 
 def make_tokens(dims: Dims, T: int, seed_tag, device="cpu") -> torch.Tensor:
