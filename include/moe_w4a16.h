@@ -199,6 +199,25 @@ int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, cons
                                uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* ws,
                                size_t ws_bytes, void* stream, void* const* events, int32_t n_events);
 
+/* moe_w4a16_forward for callers that cannot allocate memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments (minus the workspace), same kernels, same results as
+ * moe_w4a16_forward.  The scratch memory is a fixed array of
+ * MOE_NOALLOC_SCRATCH_BYTES in the library's device code, which every GPU
+ * the library runs on holds until the process ends; the call allocates
+ * nothing.  Each call first clears the array's completion counters with a
+ * small fill kernel on `stream`, then runs the layer.
+ * Limit: a call with moe_workspace_bytes(d, T) > MOE_NOALLOC_SCRATCH_BYTES
+ * returns MOE_E_WORKSPACE and launches nothing (the 6144 x 2048, 256-expert
+ * top-8 int4 layer with a shared expert fits up to T = 121).
+ * Every call on one GPU uses that GPU's single array: calls that overlap in
+ * time on one GPU (several streams or host threads) race and give undefined
+ * results; serialise them, e.g. on one stream.  Other errors as
+ * moe_w4a16_forward. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int moe_w4a16_forward_noalloc(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
+                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* stream);
+
 /* Largest T served by the GEMV path of moe_w4a16_forward. */
 int32_t moe_decode_max_tokens(void);
 

@@ -22,10 +22,12 @@ MOE_W_INT4_ROW, MOE_W_E2M1_B16, MOE_W_INT8_ROW, MOE_W_INT2_ROW = 0, 1, 2, 3
 _CODE_BITS = {MOE_W_INT4_ROW: 4, MOE_W_E2M1_B16: 4, MOE_W_INT8_ROW: 8, MOE_W_INT2_ROW: 2}
 
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
-           "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_decode_max_tokens",
+           "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_w4a16_forward_noalloc",
+           "moe_decode_max_tokens",
            "moe_status_string", "moe_tier_create", "moe_tier_destroy", "moe_tier_use", "moe_tier_prefetch",
            "moe_tier_slot", "moe_tier_stats", "moe_tier_sync")
 MOE_TIER_LRU, MOE_TIER_HOT = 0, 1
+MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/moe_w4a16.h
 
 
 class MoeDims(ctypes.Structure):
@@ -79,6 +81,8 @@ def lib():
         L.moe_w4a16_forward.restype = ctypes.c_int
         L.moe_w4a16_forward_profiled.argtypes = [D, W, P, i32, P, P, P, P, sz, P, P, i32]
         L.moe_w4a16_forward_profiled.restype = ctypes.c_int
+        L.moe_w4a16_forward_noalloc.argtypes = [D, W, P, i32, P, P, P, P]
+        L.moe_w4a16_forward_noalloc.restype = ctypes.c_int
         L.moe_decode_max_tokens.restype = i32
         L.moe_tier_create.argtypes = [D, i32, P, P, i32, P, P, i32, ctypes.POINTER(P)]
         L.moe_tier_create.restype = ctypes.c_int
@@ -257,6 +261,24 @@ def moe_w4a16_forward(layer: PackedLayer, x: torch.Tensor, y: Optional[torch.Ten
                                  _p(ws), ws.numel(), _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w4a16_forward")
+    return y
+
+
+def moe_w4a16_forward_noalloc(layer: PackedLayer, x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                              topk_idx: Optional[torch.Tensor] = None, topk_w: Optional[torch.Tensor] = None,
+                              stream=None) -> torch.Tensor:
+    """moe_w4a16_forward without a workspace: the library's fixed per-GPU
+    scratch array serves instead (the call allocates nothing on the device;
+    pass `y` to allocate nothing here either)."""
+    d = _dims(layer.dims)
+    T = x.shape[0]
+    if y is None:
+        y = torch.empty((T, d.hidden), dtype=torch.float16, device=x.device)
+    w = layer.weights()
+    rc = lib().moe_w4a16_forward_noalloc(ctypes.byref(d), ctypes.byref(w), _p(x), T, _p(y), _p(topk_idx),
+                                         _p(topk_w), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_w4a16_forward_noalloc")
     return y
 
 

@@ -3,6 +3,8 @@
 // allocates, copies or synchronises.
 #include <string.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -151,6 +153,39 @@ int check_weights(const moe_dims_t* d, const moe_weights_t* w) {
   return MOE_OK;
 }
 
+// ---- scratch of moe_w4a16_forward_noalloc -----------------------------------
+// A fixed array in the library's device code: every GPU the library runs on
+// holds its own copy until the process ends.  Its host-side name is only a
+// stand-in; the device address comes from hipGetSymbolAddress, once per
+// device (with that device current), and is kept per device.
+constexpr size_t kNoAllocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!ptr || ((uintptr_t)ptr & 255u)) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+
+__global__ __launch_bounds__(256) void k_zero_words(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
 }  // namespace
 
 extern "C" {
@@ -231,9 +266,9 @@ int moe_route(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, in
   return e == hipSuccess ? MOE_OK : MOE_E_HIP;
 }
 
-static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
-                        int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream,
-                        const StageEvents& se) {
+// Validation of a forward call (no launch); on success *p holds the plan.
+static int forward_check(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
+                         int32_t* topk_idx_out, float* topk_w_out, const void* ws, size_t ws_bytes, Plan* p) {
   int st = check_dims(d);
   if (st != MOE_OK) return st;
   if (T < 0) return MOE_E_INVAL;
@@ -242,19 +277,33 @@ static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint1
   if (st != MOE_OK) return st;
   if (T == 0) return MOE_OK;
   const void* ps[] = {x, y, ws};
-  for (const void* p : ps)
-    if (!p || !aligned16(p)) return MOE_E_INVAL;
+  for (const void* q : ps)
+    if (!q || !aligned16(q)) return MOE_E_INVAL;
   if ((topk_idx_out && !aligned16(topk_idx_out)) || (topk_w_out && !aligned16(topk_w_out))) return MOE_E_INVAL;
-  Plan p;
-  make_plan(*d, T, &p);
-  if (ws_bytes < p.total) return MOE_E_WORKSPACE;
+  make_plan(*d, T, p);
+  if (ws_bytes < p->total) return MOE_E_WORKSPACE;
+  return MOE_OK;
+}
+
+// The layer's launches for a validated call.
+static int forward_launch(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, uint16_t* y,
+                          int32_t* topk_idx_out, float* topk_w_out, void* ws, hipStream_t s, const Plan& p,
+                          const StageEvents& se) {
   Route r = route_ptrs(p, ws);
   if (topk_idx_out) r.topk_idx = topk_idx_out;
   if (topk_w_out) r.topk_w = topk_w_out;
-  hipStream_t s = (hipStream_t)stream;
   if (p.decode) return launch_decode(*d, p, *w, x, r, ws, y, s, se) == hipSuccess ? MOE_OK : MOE_E_HIP;
   if (launch_route(*d, p, *w, x, r, true, s, se.start(0), se.stop(0)) != hipSuccess) return MOE_E_HIP;
   return launch_prefill_experts(*d, p, *w, x, r, ws, y, s, se) == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+static int forward_impl(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
+                        int32_t* topk_idx_out, float* topk_w_out, void* ws, size_t ws_bytes, void* stream,
+                        const StageEvents& se) {
+  Plan p;
+  const int st = forward_check(d, w, x, T, y, topk_idx_out, topk_w_out, ws, ws_bytes, &p);
+  if (st != MOE_OK || T == 0) return st;
+  return forward_launch(d, w, x, y, topk_idx_out, topk_w_out, ws, (hipStream_t)stream, p, se);
 }
 
 int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T, uint16_t* y,
@@ -268,6 +317,26 @@ int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, cons
   if (n_events < 0 || n_events > 6 || (n_events > 0 && !events)) return MOE_E_INVAL;
   return forward_impl(d, w, x, T, y, topk_idx_out, topk_w_out, ws, ws_bytes, stream,
                       StageEvents{events, n_events});
+}
+
+int moe_w4a16_forward_noalloc(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
+                              uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* stream) {
+  Plan p;
+  // validated against a stand-in address (the scratch array is 256-byte
+  // aligned): nothing touches the device before the call is known to be good
+  const int st = forward_check(d, w, x, T, y, topk_idx_out, topk_w_out, (const void*)(uintptr_t)256,
+                               kNoAllocScratchBytes, &p);
+  if (st != MOE_OK || T == 0) return st;
+  void* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return MOE_E_HIP;
+  const hipStream_t s = (hipStream_t)stream;
+  // the completion counters must start at zero (a fill kernel, not a memset
+  // node, so that the call can be captured in a graph)
+  const size_t words = p.sync_bytes / 4;
+  hipLaunchKernelGGL(k_zero_words, dim3((unsigned)std::min<size_t>((words + 255) / 256, 64)), dim3(256), 0, s,
+                     (uint32_t*)ws, words);
+  if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
+  return forward_launch(d, w, x, y, topk_idx_out, topk_w_out, ws, s, p, StageEvents{nullptr, 0});
 }
 
 const char* moe_status_string(int status) {

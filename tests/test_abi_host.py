@@ -127,3 +127,22 @@ def test_top_p_accepted_range(L):
         d = moe.MoeDims(256, 128, 8, 2, 1, 0, p)
         assert moe.moe_packed_bytes(d) == moe.moe_packed_bytes(moe.MoeDims(256, 128, 8, 2, 1, 0))
         assert moe.moe_workspace_bytes(d, 4) == moe.moe_workspace_bytes(moe.MoeDims(256, 128, 8, 2, 1, 0), 4)
+
+
+def test_noalloc_rejects_before_any_launch(L):
+    """moe_w4a16_forward_noalloc validates like moe_w4a16_forward and
+    rejects batches whose workspace would exceed its fixed scratch with
+    MOE_E_WORKSPACE, all before touching the device."""
+    d = moe.MoeDims(6144, 2048, 256, 8, 1, 0)
+    w = moe.MoeWeights(4096, 8192, 4096, None)
+    P = ctypes.c_void_p
+    big = next(t for t in range(16, 1 << 14, 16) if moe.moe_workspace_bytes(d, t) > moe.MOE_NOALLOC_SCRATCH_BYTES)
+    assert moe.moe_workspace_bytes(d, 121) <= moe.MOE_NOALLOC_SCRATCH_BYTES < moe.moe_workspace_bytes(d, 122)
+    f = L.moe_w4a16_forward_noalloc
+    assert f(ctypes.byref(d), ctypes.byref(w), P(16), big, P(16), None, None, None) == moe.MOE_E_WORKSPACE
+    assert f(ctypes.byref(d), ctypes.byref(w), P(16), 0, P(16), None, None, None) == moe.MOE_OK
+    assert f(ctypes.byref(d), ctypes.byref(w), P(16), -1, P(16), None, None, None) == moe.MOE_E_INVAL
+    assert f(ctypes.byref(d), ctypes.byref(w), None, 4, P(16), None, None, None) == moe.MOE_E_INVAL
+    assert f(ctypes.byref(d), ctypes.byref(w), P(16), 4, P(24), None, None, None) == moe.MOE_E_INVAL
+    bad = moe.MoeDims(100, 2048, 256, 8, 1, 0)
+    assert f(ctypes.byref(bad), ctypes.byref(w), P(16), 4, P(16), None, None, None) == moe.MOE_E_UNSUPPORTED
