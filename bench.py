@@ -38,7 +38,7 @@ PROFILES = os.path.join(ROOT, "profiles")
 # path the shared expert's gate/up runs in the routing launch, so the gate/up
 # launch streams the routed experts only.
 STAGES = {"decode": ("route_shared_gate_up", "gate_up", "down"), "prefill": ("route", "gate_up", "down")}
-DOMINANT = {"decode": (1, "k_gu_phase"), "prefill": (1, "k_gu_gemm")}
+DOMINANT = {"decode": (1, "k_gu_phase"), "prefill": (1, "k_expert_gemm<gate_up>")}
 WEIGHT_NAMES = {synth.INT4_ROW: "int4_row", synth.E2M1_B16: "e2m1_b16", synth.INT8_ROW: "int8_row",
                 synth.INT2_ROW: "int2_row"}
 
@@ -251,35 +251,63 @@ class _HostExperts:
         self.router_b = None if layer.router_b is None else layer.router_b.cpu()
 
 
-def cpu_baseline(ch: Chain, budget_s: float = 12.0, max_tokens: int = 64):
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_oracle(host, xs, r, threads, budget_s, max_tokens):
+    """Single-token oracle calls on `threads` threads until the budget or the
+    sample runs out; returns (tokens done, seconds)."""
+    import oracle
+    done, t0 = 0, time.perf_counter()
+    while done < max_tokens and (time.perf_counter() - t0) < budget_s:
+        oracle.forward(host, xs, tokens=[done], experts_needed=[int(e) for e in r.topk_idx[done] if e >= 0],
+                       threads=threads)
+        done += 1
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(ch: Chain, budget_s: float = 10.0, max_tokens: int = 64, single_budget_s: float = 8.0):
+    """The CPU oracle (fp64 C++, OpenMP over independent output rows) on a
+    bounded sample of tokens of the same layer, on all host threads and on
+    one thread.  Tokens are processed one call each (the oracle's cost per
+    token does not depend on the batch), so the same figure serves decode
+    and prefill workloads; the sample's tokens are drawn like the workload's."""
     import numpy as np
     import oracle
 
     layer = ch.canon0
     d = layer.dims
-    n_cand = max_tokens
-    xs = synth.make_tokens(d, n_cand, (ch.name, "cpu-sample"), device="cpu")
+    n_all = oracle.max_threads()  # before any call sets the thread count
+    xs = synth.make_tokens(d, max_tokens, (ch.name, "cpu-sample"), device="cpu")
     r = oracle.route(d, xs, layer.router_w.cpu(), None if layer.router_b is None else layer.router_b.cpu())
-    need = set(np.unique(r.topk_idx).tolist()) | ({d.n_experts} if d.has_shared else set())
+    need = set(np.unique(r.topk_idx[r.topk_idx >= 0]).tolist()) | ({d.n_experts} if d.has_shared else set())
     host = _HostExperts(layer, need)
-    threads = oracle.max_threads()
-    done, t0 = 0, time.perf_counter()
-    while done < n_cand and (time.perf_counter() - t0) < budget_s:
-        oracle.forward(host, xs, tokens=[done], experts_needed=[int(e) for e in r.topk_idx[done]])
-        done += 1
-    el = time.perf_counter() - t0
+    done, el = _time_oracle(host, xs, r, n_all, budget_s, max_tokens)
+    done1, el1 = _time_oracle(host, xs, r, 1, single_budget_s, max_tokens)
+    oracle.forward(host, xs, tokens=[0], experts_needed=[int(e) for e in r.topk_idx[0] if e >= 0], threads=n_all)
     # parity of the GPU path (one call per token, as timed) on the same sample
     pl = moe.PackedLayer(d, ch.layers[0].packed, layer.router_w, layer.router_b)
     xg = xs[:done].to("cuda")
     y = torch.cat([moe.moe_w4a16_forward(pl, xg[t:t + 1].contiguous()) for t in range(done)])
     torch.cuda.synchronize()
-    y_ref = oracle.forward(host, xs, tokens=list(range(done)), experts_needed=sorted(need - {d.n_experts}))
+    y_ref = oracle.forward(host, xs, tokens=list(range(done)), experts_needed=sorted(need - {d.n_experts}),
+                           threads=n_all)
     err = y.double().cpu().numpy() - y_ref
     rel = float(np.linalg.norm(err) / np.linalg.norm(y_ref))
-    return {"value": done / el, "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"{done} single-token decode calls of the {ch.name} layer (seeded tokens), {el:.1f}s, "
-                      f"fp64 C++ oracle with OpenMP over output rows",
+    model = cpu_model()
+    return {"value": done / el, "unit": "tokens/s", "cores": n_all, "kind": "oracle",
+            "sample": f"{done} tokens of the {ch.name} layer (seeded, drawn like its inputs), one oracle call "
+                      f"each, {el:.1f}s on {n_all} threads of {model}; fp64 C++ oracle, OpenMP over output rows",
+            "cpu_model": model,
+            "single_thread": {"value": done1 / el1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{done1} tokens of the same sample, {el1:.1f}s, OMP on one thread"},
             "parity_rel_l2_on_sample": rel}
 
 
@@ -384,7 +412,12 @@ def tiered_decode(n_layers: int = 2, slots: int = 32, tokens: int = 48, warmup: 
                         "pcie_gbps": (read + promos) * pb / dt / 1e9})
         out["modes"][mode] = res
         log(f"[bench] tiered {mode}: " + json.dumps({k: round(v, 4) for k, v in res.items()}))
-    del host, buf, slot_mem
+    del host, buf, slot_mem, layers, pl0
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch._C._host_emptyCache()  # return the pinned host buffers now, not at interpreter exit
+    torch.cuda.empty_cache()
     return out
 
 
@@ -420,7 +453,28 @@ def run_workload(name, L, steps, warmup, stage_reps=4):
     }
     if T > moe.moe_decode_max_tokens():
         res["mfma_util"] = layer_flops(d, T) / (ms_step / 1e3) / (FP16_MFMA_PEAK_TFLOPS * 1e12)
+        res["roofline"] = prefill_roofline(d, T, res["stage_ms"], name)
     return ch, res, touched
+
+
+def prefill_roofline(d, T, stage_ms, workload):
+    """Matrix-core roofline of the grouped-GEMM path: the gate/up launch
+    (k_expert_gemm<., 2, .>, the dominant kernel) and the down launch,
+    algorithmic fp16 flops per launch (2 flops per multiply-add; every
+    (token, expert) pair including the shared expert, without the padding of
+    partly filled tiles) over the launch's mean duration."""
+    pairs = T * (d.top_k + d.has_shared)
+    gu_flops = 2 * 2 * d.hidden * d.inter * pairs
+    dn_flops = 2 * d.hidden * d.inter * pairs
+    gu_ms, dn_ms = stage_ms["gate_up"], stage_ms["down"]
+    achieved = gu_flops / (gu_ms / 1e3) / 1e12
+    return {"bound": "mfma", "kernel": "k_expert_gemm<gate_up>", "achieved": achieved,
+            "peak": FP16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": achieved / FP16_MFMA_PEAK_TFLOPS,
+            "traffic": traffic_record("k_expert_gemm_gu", workload),
+            "algorithmic_flops_per_launch": gu_flops, "avg_launch_ms": gu_ms,
+            "down": {"kernel": "k_expert_gemm<down>+k_combine", "algorithmic_flops_per_launch": dn_flops,
+                     "avg_ms": dn_ms, "achieved": dn_flops / (dn_ms / 1e3) / 1e12,
+                     "frac": dn_flops / (dn_ms / 1e3) / 1e12 / FP16_MFMA_PEAK_TFLOPS}}
 
 
 def main():
@@ -458,23 +512,29 @@ def main():
     ch, res, touched = run_workload(args.workload, args.layers, args.steps, args.warmup)
     d, T = ch.dims, ch.T
     path = path_of(T)
-    st_idx, kname = DOMINANT[path]
-    k_ms = res["stage_ms"][STAGES[path][st_idx]]
     U = res["mean_unique_experts"]
-    alg = sum(dominant_bytes(d, T, u) for u in touched) / len(touched)
-    achieved = alg / (k_ms / 1e3) / 1e9
-    roofline = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(kname, args.workload),
-                "algorithmic_bytes_per_launch": alg, "avg_launch_ms": k_ms}
-    cpu = None
-    if not args.no_cpu_baseline:
+    if path == "decode":
+        st_idx, kname = DOMINANT[path]
+        k_ms = res["stage_ms"][STAGES[path][st_idx]]
+        alg = sum(dominant_bytes(d, T, u) for u in touched) / len(touched)
+        achieved = alg / (k_ms / 1e3) / 1e9
+        roofline = {"bound": "hbm", "kernel": kname, "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": achieved / HBM_PEAK_GBPS, "traffic": traffic_record(kname, args.workload),
+                    "algorithmic_bytes_per_launch": alg, "avg_launch_ms": k_ms}
+    else:
+        roofline = res["roofline"]
+
+    def baseline(chain, **kw):
         try:
-            cpu = cpu_baseline(ch)
+            return cpu_baseline(chain, **kw)
         except Exception as e:  # the baseline is context, never the headline
-            cpu = {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle", "sample": f"failed: {e}"}
+            return {"value": None, "unit": "tokens/s", "cores": None, "kind": "oracle", "sample": f"failed: {e}"}
+
+    cpu = None if args.no_cpu_baseline else baseline(ch)
     secondary = []
     del ch
     torch.cuda.empty_cache()
+    roofline_prefill = cpu_prefill = None
     if not args.no_secondary:
         for name, L, steps in (("decode_b8", 8, 128), ("decode_b1_topp", 8, 512), ("e2m1_b1", 32, 512),
                                ("e2m1_b4", 32, 256), ("int8_b1", 8, 512), ("int2_b1", 8, 512),
@@ -482,6 +542,11 @@ def main():
                                ("prefill_2048_uniform", 2, 8)):
             try:
                 c2, r2, _ = run_workload(name, L, steps, 32, stage_reps=2)
+                if name == "prefill_2048":
+                    roofline_prefill = r2["roofline"]
+                    if not args.no_cpu_baseline:
+                        cpu_prefill = r2["cpu_baseline"] = baseline(c2, budget_s=6.0, max_tokens=32,
+                                                                    single_budget_s=4.0)
                 secondary.append(r2)
                 del c2
                 torch.cuda.empty_cache()
@@ -513,6 +578,8 @@ def main():
         "stage_ms": res["stage_ms"],
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "roofline_prefill": roofline_prefill,
+        "cpu_baseline_prefill": cpu_prefill,
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -258,12 +258,12 @@ __device__ __forceinline__ bool tile_token(const GemmArgs& a, const SlotEntry& s
 // per-token activation sums.
 constexpr int kGemmWaves = 8;
 
-template <int FMT, int NM, int DEPTH>
+template <int FMT, int NM, int DEPTH, int BT>
 __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int nx) {
   typedef Slice<FMT> SL;
-  // tokens per tile: 64 for gate/up (two matrices' accumulators) and for
-  // int2 (two K-steps of A operands), else 128
-  constexpr int BT = (NM == 2 || Slice<FMT>::STEPS == 2) ? kPrefillTileRows : kDownTileRows;
+  // BT tokens per tile: kPrefillTileRows (64) or kDownTileRows (128); the
+  // accumulators take NM x 64 rows x BT tokens per wavefront
+  static_assert(BT == kPrefillTileRows || BT == kDownTileRows, "a tile height with a tile list");
   constexpr int GMAX = BT / 16;              // 16-token groups per tile
   constexpr int NT = 64 * kGemmWaves;
   constexpr int SC = SL::SC, WPS = SL::WPS, XP = SL::XP, STEPS = SL::STEPS;
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   // (one for 32-byte pieces, whose slices carry twice the matrix work)
   constexpr int XR = PH == 16 ? 1 : 2;
   static_assert(DEPTH % XR == 0, "the activation ring slot is c % XR");
-  static_assert((128 / SC) % DEPTH == 0, "K is a multiple of 128, so DEPTH divides the slice count");
+  // the launcher picks DEPTH so that it divides the slice count K / SC
   typedef Piece<PH> P;
   __shared__ __attribute__((aligned(16))) _Float16 sx[3][BT][XP];
   __shared__ int s_act[BT], s_out[BT];
@@ -591,16 +591,20 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   const int nx_gu = (p.I + rows_per_wg - 1) / rows_per_wg, nx_dn = (p.H + rows_per_wg - 1) / rows_per_wg;
   const int mt8_dn = (prefill_max_tiles(p.T, p.k, p.E, p.S, kDownTileRows) + 7) / 8 * 8;
   const dim3 blk(64 * kGemmWaves);
-  auto gemms = [&](auto gu, auto dn, int dn_rows = kDownTileRows) {
+  auto gemms = [&](auto gu, auto dn, int dn_rows) {
     launch_k(gu, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
     launch_k(dn, dim3((dn_rows == kDownTileRows ? mt8_dn : mt8) * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
   };
-  // ring depth: 4 slices for the int4 gate/up, 2 otherwise
+  // Ring depth (K-slices of weights in flight per wavefront): 4 slices for
+  // the int4 gate/up, 2 for the others (deeper rings spill beside the 128
+  // accumulators).  Down tiles hold 128 tokens, except int2 (64: its
+  // 32-byte activation pieces leave no registers for 128).
+  constexpr int G = kPrefillTileRows, D = kDownTileRows;
   switch (d.wfmt) {
-    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4>, k_expert_gemm<MOE_W_INT4_ROW, 1, 2>); break;
-    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2, 2>, k_expert_gemm<MOE_W_INT8_ROW, 1, 2>); break;
-    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2>, kPrefillTileRows); break;
-    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2>); break;
+    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4, G>, k_expert_gemm<MOE_W_INT4_ROW, 1, 2, D>, D); break;
+    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2, 2, G>, k_expert_gemm<MOE_W_INT8_ROW, 1, 2, D>, D); break;
+    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2, G>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2, G>, G); break;
+    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2, G>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2, D>, D); break;
   }
   launch_k(k_combine, dim3((p.H / 2 + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
   return hipGetLastError();

@@ -7,6 +7,10 @@
       HBM traffic per launch of kernel K from a FETCH_SIZE run and a WRITE_SIZE run (rocprofv3 --pmc,
       --output-format csv), each scaled by what the same counter reads for the plain copy kernel that
       `bench.py --calibrate-copy-mb N` runs first (N MB read and N MB written per launch)
+  python -m quantized_moe_expert_02_amd.profile_summary requests PMC_DIR --kernel K [K ...] --copy-mb N
+      --workload W --command C
+      HBM read bytes per launch from the read-request counts by size (32/64/128 B), for the copy kernel
+      and the kernels named, to check the scale factor of FETCH_SIZE
   python -m quantized_moe_expert_02_amd.profile_summary mfma PMC_DIR --kernel K --workload W --command C
       fp16 matrix-core work per launch of the kernels whose names contain K, from one rocprofv3 --pmc run of
       the derived metrics MfmaFlopsF16 (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512) and MfmaUtil (matrix-core busy
@@ -92,11 +96,13 @@ def traffic(args) -> None:
     write_b = kw * 1024.0 * w_scale
     src = os.path.join(ROOT, args.source)
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    print(f"# HBM traffic per launch of {args.kernel} ({args.workload}), rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
+    label = args.label or args.kernel
+    print(f"# HBM traffic per launch of {label} ({args.workload}), rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE")
     print(f"# command: {args.command}")
     print(f"# copy calibration: torch.neg over {args.copy_mb} MB reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE "
           f"{cw:.0f} KiB per launch; scale factors fetch {f_scale:.4f}, write {w_scale:.4f}")
-    print(f"kernel = {args.kernel}")
+    print(f"kernel = {label}")
+    print(f"kernel_match = {args.kernel}")
     print(f"workload = {args.workload}")
     print(f"dispatches = {nf} / {nw}")
     print(f"fetch_kib_per_dispatch = {kf:.1f}")
@@ -106,6 +112,28 @@ def traffic(args) -> None:
     print(f"bytes_per_launch = {fetch_b + write_b:.0f}")
     print(f"source = {args.source}")
     print(f"source_sha256 = {sha}")
+
+
+def requests(args) -> None:
+    """HBM read bytes per launch from the L2's read-request counts by size
+    (TCC_EA0_RDREQ_{32B,64B,128B}_sum), an independent check of the scaled
+    FETCH_SIZE: bytes = 32 n32 + 64 n64 + 128 n128, for the copy kernel and
+    for the named kernels."""
+    cnt = {c: _counter(args.path, c) for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                                               "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")}
+    print(f"# HBM read requests by size per launch, rocprofv3 --pmc TCC_EA0_RDREQ_sum TCC_EA0_RDREQ_32B_sum "
+          f"TCC_EA0_RDREQ_64B_sum TCC_EA0_RDREQ_128B_sum ({args.workload})")
+    print(f"# command: {args.command}")
+    print(f"# bytes = 32 n32 + 64 n64 + 128 n128; copy kernel: torch.neg over {args.copy_mb} MB "
+          f"({args.copy_mb * (1 << 20)} bytes read per launch)")
+    print(f"{'requests':>12} {'n32':>10} {'n64':>12} {'n128':>12} {'bytes':>14}  kernel")
+    for key in [COPY_KERNEL] + args.kernel:
+        row = []
+        for c in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum", "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum"):
+            hits = [x for k, v in cnt[c].items() if key in k for x in v]
+            row.append(sum(hits) / len(hits) if hits else float("nan"))
+        n, n32, n64, n128 = row
+        print(f"{n:12.0f} {n32:10.0f} {n64:12.0f} {n128:12.0f} {32 * n32 + 64 * n64 + 128 * n128:14.0f}  {key}")
 
 
 def mfma(args) -> None:
@@ -156,7 +184,8 @@ def main() -> None:
     b = sub.add_parser("traffic")
     b.add_argument("fetch_dir")
     b.add_argument("write_dir")
-    b.add_argument("--kernel", required=True)
+    b.add_argument("--kernel", required=True, help="substring of the kernel name in the counter output")
+    b.add_argument("--label", default="", help="kernel name for the record (default: --kernel)")
     b.add_argument("--copy-mb", type=int, required=True)
     b.add_argument("--workload", required=True)
     b.add_argument("--source", required=True)
@@ -166,13 +195,19 @@ def main() -> None:
     c.add_argument("--kernel", required=True)
     c.add_argument("--workload", required=True)
     c.add_argument("--command", required=True)
+    r = sub.add_parser("requests")
+    r.add_argument("path")
+    r.add_argument("--kernel", nargs="+", required=True)
+    r.add_argument("--copy-mb", type=int, required=True)
+    r.add_argument("--workload", required=True)
+    r.add_argument("--command", required=True)
     e = sub.add_parser("counters")
     e.add_argument("path")
     e.add_argument("--kernel", required=True)
     e.add_argument("--title", required=True)
     e.add_argument("--command", required=True)
     args = ap.parse_args()
-    {"stats": stats, "traffic": traffic, "mfma": mfma, "counters": counters}[args.mode](args)
+    {"stats": stats, "traffic": traffic, "requests": requests, "mfma": mfma, "counters": counters}[args.mode](args)
 
 
 if __name__ == "__main__":
