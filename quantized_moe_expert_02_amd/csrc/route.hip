@@ -231,13 +231,49 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* s_wave, int& tot
   return base + inc - v;
 }
 
+// Grouped-GEMM tile list of BT-token tiles, longest first: a tile's class is
+// its number of filled 16-token groups (BT / 16 for a full tile), tiles are
+// listed by class in descending order, and within a class by expert, the
+// shared expert (slot 0, all T tokens) first, then the union in order; an
+// expert's full tiles precede its partial one.  So the launch dispatches the
+// long tiles first and ends on short ones.  One block-wide prefix sum per
+// class; every thread places its own expert's tiles (tot tokens, union slot
+// `slot`).  Returns the number of tiles.
+template <int BT>
+__device__ int write_tile_list(const RouteArgs& a, int32_t* list, int tot, int slot, int (*s_buf)[kScanThreads / 64]) {
+  constexpr int G = BT / 16;
+  const int nfull = tot / BT, rest = tot % BT, pcls = (rest + 15) / 16;  // pcls 0: no partial tile
+  const int sfull = a.S ? a.T / BT : 0, srest = a.S ? a.T % BT : 0, spcls = (srest + 15) / 16;
+  int base = 0;
+  for (int c = G; c >= 1; --c) {
+    const int cnt = (c == G ? nfull : 0) + (pcls == c ? 1 : 0);
+    const int sh = (c == G ? sfull : 0) + (spcls == c ? 1 : 0);
+    int total;
+    const int ex = block_exclusive_scan(cnt, s_buf[c & 1], total);
+    if (threadIdx.x == 0)
+      for (int i = 0; i < sh; ++i) {
+        const int pos = base + i;
+        list[2 * pos] = 0;
+        list[2 * pos + 1] = (c == G && i < sfull) ? BT * i : BT * sfull;
+      }
+    for (int i = 0; i < cnt; ++i) {
+      const int pos = base + sh + ex + i;
+      list[2 * pos] = slot;
+      list[2 * pos + 1] = (c == G && i < nfull) ? BT * i : BT * nfull;
+    }
+    base += sh + total;
+  }
+  return base;
+}
+
 // Pass 2 (one block, thread e = expert e): per-expert totals over the
 // chunks; block-wide prefix sums give each expert's pair offset, its place
-// in the union and its first tile in each grouped-GEMM tile list, so every
-// thread writes its own expert's entries; then each (chunk, expert) base
-// offset.
+// in the union and the places of its tiles in each grouped-GEMM tile list
+// (write_tile_list), so every thread writes its own expert's entries; then
+// each (chunk, expert) base offset.
 __global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
-  __shared__ int s_wave[4][kScanThreads / 64];
+  __shared__ int s_wave[2][kScanThreads / 64];
+  __shared__ int s_cls[2][kScanThreads / 64];
   static_assert(kMaxExperts <= kScanThreads, "one thread per expert");
   const int e = threadIdx.x;
   int tot = 0;  // pairs of expert e (16 independent loads in flight)
@@ -250,15 +286,9 @@ __global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
       for (int i = 0; i < 16; ++i) tot += v[i];
     }
   const int used = tot > 0 ? 1 : 0;
-  const int ntl = (tot + kPrefillTileRows - 1) / kPrefillTileRows, ntd = (tot + kDownTileRows - 1) / kDownTileRows;
-  int off_all, nu_all, nt_all, nd_all;
+  int off_all, nu_all;
   const int off = block_exclusive_scan(tot, s_wave[0], off_all);
   const int u = block_exclusive_scan(used, s_wave[1], nu_all);
-  const int tb = block_exclusive_scan(ntl, s_wave[2], nt_all);
-  const int db = block_exclusive_scan(ntd, s_wave[3], nd_all);
-  // grouped-GEMM tiles: the shared expert's first, then the union in order
-  const int nsh = a.S ? (a.T + kPrefillTileRows - 1) / kPrefillTileRows : 0;
-  const int nshd = a.S ? (a.T + kDownTileRows - 1) / kDownTileRows : 0;
   if (used) {
     a.uniq_ids[u] = e;
     a.uniq_off[u] = off;
@@ -269,35 +299,19 @@ __global__ __launch_bounds__(kScanThreads) void k_union_scan(RouteArgs a) {
       sl.p0 = off;
       a.slots[a.S + u] = sl;
     }
-    if (a.tiles) {
-      for (int i = 0; i < ntl; ++i) {
-        a.tiles[2 * (nsh + tb + i)] = a.S + u;
-        a.tiles[2 * (nsh + tb + i) + 1] = i * kPrefillTileRows;
-      }
-      for (int i = 0; i < ntd; ++i) {
-        a.tiles_dn[2 * (nshd + db + i)] = a.S + u;
-        a.tiles_dn[2 * (nshd + db + i) + 1] = i * kDownTileRows;
-      }
-    }
   }
-  if (a.tiles) {
-    for (int i = e; i < nsh; i += kScanThreads) {
-      a.tiles[2 * i] = 0;
-      a.tiles[2 * i + 1] = i * kPrefillTileRows;
-    }
-    for (int i = e; i < nshd; i += kScanThreads) {
-      a.tiles_dn[2 * i] = 0;
-      a.tiles_dn[2 * i + 1] = i * kDownTileRows;
+  if (a.tiles) {  // (uniform) grouped-GEMM tile lists, longest tiles first
+    const int nt = write_tile_list<kPrefillTileRows>(a, a.tiles, tot, a.S + u, s_cls);
+    const int nd = write_tile_list<kDownTileRows>(a, a.tiles_dn, tot, a.S + u, s_cls);
+    if (e == 0) {
+      a.n_tiles[0] = nt;
+      a.n_tiles[1] = nd;
     }
   }
   if (e == 0) {
     *a.n_unique = nu_all;
     a.uniq_off[nu_all] = off_all;
     if (a.slots && a.S) write_slot(a, 0, -1, a.T, -1);
-    if (a.tiles) {
-      a.n_tiles[0] = nsh + nt_all;
-      a.n_tiles[1] = nshd + nd_all;
-    }
   }
   if (a.slots)
     for (int sl = a.S + nu_all + e; sl < a.slots_max; sl += kScanThreads) write_slot(a, sl, 0, 0, 0);
