@@ -477,6 +477,37 @@ def prefill_roofline(d, T, stage_ms, workload):
                      "frac": dn_flops / (dn_ms / 1e3) / 1e12 / FP16_MFMA_PEAK_TFLOPS}}
 
 
+def reference_rates():
+    """Rates the box reaches with library code that is not this project's:
+    HBM read (torch.sum over 4 GiB of binary16), HBM copy (torch.neg, read
+    + write) and a dense binary16 GEMM (torch.matmul, 8192^3, hipBLASLt) --
+    measured context beside the published peaks (8 TB/s, 2.5 PFLOP/s)."""
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps / 1e3
+    n = 2 << 30  # binary16 elements: 4 GiB
+    a = torch.ones(n, dtype=torch.float16, device="cuda")
+    t_sum = timed(lambda: torch.sum(a, dtype=torch.float32), 10)
+    b = torch.empty_like(a)
+    t_neg = timed(lambda: torch.neg(a, out=b), 10)
+    del a, b
+    m = torch.randn((8192, 8192), dtype=torch.float16, device="cuda")
+    w = torch.randn((8192, 8192), dtype=torch.float16, device="cuda")
+    t_mm = timed(lambda: torch.matmul(m, w), 20)
+    del m, w
+    torch.cuda.empty_cache()
+    return {"hbm_read_gbps": 2 * n / t_sum / 1e9, "hbm_copy_gbps": 4 * n / t_neg / 1e9,
+            "fp16_gemm_tflops": 2 * 8192 ** 3 / t_mm / 1e12,
+            "how": "torch.sum over 4 GiB binary16; torch.neg over 4 GiB (read + write); torch.matmul 8192^3 binary16"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -487,6 +518,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--tiered-only", action="store_true", help="run only the tiered-residency decode line")
+    ap.add_argument("--reference-rates", action="store_true",
+                    help="print only the rates torch reaches on this box (HBM read/copy, fp16 GEMM) and exit")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain elementwise copy (torch.neg) over this many MB, so that hardware "
                          "traffic counters taken over the run can be scaled against a kernel of known traffic")
@@ -508,6 +541,9 @@ def main():
 
     if args.tiered_only:
         print(json.dumps(tiered_decode()))
+        return
+    if args.reference_rates:
+        print(json.dumps(reference_rates()))
         return
     ch, res, touched = run_workload(args.workload, args.layers, args.steps, args.warmup)
     d, T = ch.dims, ch.T

@@ -258,14 +258,14 @@ __device__ __forceinline__ bool tile_token(const GemmArgs& a, const SlotEntry& s
 // per-token activation sums.
 constexpr int kGemmWaves = 8;
 
-template <int FMT, int NM, int DEPTH, int BT>
-__global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int nx) {
+template <int FMT, int NM, int DEPTH, int BT, int NW>
+__global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
   typedef Slice<FMT> SL;
   // BT tokens per tile: kPrefillTileRows (64) or kDownTileRows (128); the
   // accumulators take NM x 64 rows x BT tokens per wavefront
   static_assert(BT == kPrefillTileRows || BT == kDownTileRows, "a tile height with a tile list");
   constexpr int GMAX = BT / 16;              // 16-token groups per tile
-  constexpr int NT = 64 * kGemmWaves;
+  constexpr int NT = 64 * NW;
   constexpr int SC = SL::SC, WPS = SL::WPS, XP = SL::XP, STEPS = SL::STEPS;
   constexpr int PH = SC * BT / NT;  // halves per thread and slice (every thread stages one piece)
   constexpr int PPR = SC / PH;      // pieces per token row of a slice
@@ -293,7 +293,7 @@ __global__ __launch_bounds__(64 * kGemmWaves) void k_expert_gemm(GemmArgs a, int
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = (NM == 2) ? a.H : a.I;
   const int R = (NM == 2) ? a.I : a.H;  // rows per matrix
-  const int rb = ngrp * kGemmWaves + wave;
+  const int rb = ngrp * NW + wave;
   const bool active = rb * 64 < R;
   if (tid < BT) {
     int ar = -1, orow = -1;
@@ -587,24 +587,27 @@ hipError_t launch_prefill_experts(const moe_dims_t& d, const Plan& p, const moe_
   a.rows_total = p.rows_total;
   a.L = layout_of(d);
   const int mt8 = (prefill_max_tiles(p.T, p.k, p.E, p.S) + 7) / 8 * 8;
-  const int rows_per_wg = 64 * kGemmWaves;
-  const int nx_gu = (p.I + rows_per_wg - 1) / rows_per_wg, nx_dn = (p.H + rows_per_wg - 1) / rows_per_wg;
   const int mt8_dn = (prefill_max_tiles(p.T, p.k, p.E, p.S, kDownTileRows) + 7) / 8 * 8;
-  const dim3 blk(64 * kGemmWaves);
-  auto gemms = [&](auto gu, auto dn, int dn_rows) {
-    launch_k(gu, dim3(mt8 * nx_gu), blk, s, se.start(1), se.stop(1), a, nx_gu);
-    launch_k(dn, dim3((dn_rows == kDownTileRows ? mt8_dn : mt8) * nx_dn), blk, s, se.start(2), nullptr, a, nx_dn);
+  // one launch of kernel k over the tile list of BT-token tiles, NW
+  // wavefronts (64 rows each) per workgroup, R rows per matrix
+  auto gemm = [&](auto k, int BT, int NW, int R, hipEvent_t start, hipEvent_t stop) {
+    const int nx = (R + 64 * NW - 1) / (64 * NW);
+    launch_k(k, dim3((BT == kDownTileRows ? mt8_dn : mt8) * nx), dim3(64 * NW), s, start, stop, a, nx);
+  };
+  auto gemms = [&](auto gu, auto dn, int dn_rows, int dn_waves) {
+    gemm(gu, kPrefillTileRows, kGemmWaves, p.I, se.start(1), se.stop(1));
+    gemm(dn, dn_rows, dn_waves, p.H, se.start(2), nullptr);
   };
   // Ring depth (K-slices of weights in flight per wavefront): 4 slices for
   // the int4 gate/up, 2 for the others (deeper rings spill beside the 128
   // accumulators).  Down tiles hold 128 tokens, except int2 (64: its
   // 32-byte activation pieces leave no registers for 128).
-  constexpr int G = kPrefillTileRows, D = kDownTileRows;
+  constexpr int G = kPrefillTileRows, D = kDownTileRows, W = kGemmWaves;
   switch (d.wfmt) {
-    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4, G>, k_expert_gemm<MOE_W_INT4_ROW, 1, 2, D>, D); break;
-    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2, 2, G>, k_expert_gemm<MOE_W_INT8_ROW, 1, 2, D>, D); break;
-    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2, G>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2, G>, G); break;
-    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2, G>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2, D>, D); break;
+    case MOE_W_INT4_ROW: gemms(k_expert_gemm<MOE_W_INT4_ROW, 2, 4, G, W>, k_expert_gemm<MOE_W_INT4_ROW, 1, 2, D, W>, D, W); break;
+    case MOE_W_INT8_ROW: gemms(k_expert_gemm<MOE_W_INT8_ROW, 2, 2, G, W>, k_expert_gemm<MOE_W_INT8_ROW, 1, 2, D, W>, D, W); break;
+    case MOE_W_INT2_ROW: gemms(k_expert_gemm<MOE_W_INT2_ROW, 2, 2, G, W>, k_expert_gemm<MOE_W_INT2_ROW, 1, 2, G, W>, G, W); break;
+    default: gemms(k_expert_gemm<MOE_W_E2M1_B16, 2, 2, G, W>, k_expert_gemm<MOE_W_E2M1_B16, 1, 2, D, W>, D, W); break;
   }
   launch_k(k_combine, dim3((p.H / 2 + 255) / 256, p.T), dim3(256), s, nullptr, se.stop(2), a);
   return hipGetLastError();
