@@ -143,8 +143,12 @@ def test_forward_full_size_matches_oracle(name):
     r = oracle_route(layer, x)
     assert min_topk_gap(r, layer.dims.top_k) > 1e-9
     pl = moe.PackedLayer.from_layer(layer)
-    y = moe.moe_w4a16_forward(pl, x)
+    ws = moe.workspace(layer.dims, x.shape[0], DEV)
+    y = moe.moe_w4a16_forward(pl, x, ws=ws)
     torch.cuda.synchronize()
+    # every completion counter is back at zero, and the shared down's wait
+    # for the shared h ended by its condition (no bound reached)
+    assert torch.count_nonzero(ws[: moe.moe_workspace_sync_bytes(layer.dims)]) == 0
     y_ref = oracle_y(layer, x)
     rel, mx = assert_close(y, y_ref, name)
     _log(f"  {name}: U={r.n_unique} rel_l2={rel:.2e} max_abs={mx:.2e}")
