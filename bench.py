@@ -37,7 +37,9 @@ PROFILES = os.path.join(ROOT, "profiles")
 # the dominant kernel: (stage index, name in rocprofv3 output).  On the decode
 # path the shared expert's gate/up runs in the routing launch, so the gate/up
 # launch streams the routed experts only.
-STAGES = {"decode": ("route_shared_gate_up", "gate_up", "down"), "prefill": ("route", "gate_up", "down")}
+# decode stage 0 also runs the shared expert's gate/up when T > 1 (for one
+# token that moves into stage 1)
+STAGES = {"decode": ("route", "gate_up", "down"), "prefill": ("route", "gate_up", "down")}
 DOMINANT = {"decode": (1, "k_gu_phase"), "prefill": (1, "k_expert_gemm<gate_up>")}
 WEIGHT_NAMES = {synth.INT4_ROW: "int4_row", synth.E2M1_B16: "e2m1_b16", synth.INT8_ROW: "int8_row",
                 synth.INT2_ROW: "int2_row"}
@@ -428,9 +430,13 @@ def path_of(T):
 def dominant_bytes(d, T, n_touched):
     """Algorithmic bytes of the dominant (gate/up) kernel: on the decode path
     the routed experts' gate/up weights and scales, x read and the routed h
-    rows written; on the prefill path the shared expert as well."""
+    rows written -- for one token the launch also runs the shared expert's
+    gate/up (its weights and h row); on the prefill path the shared expert as
+    well."""
     if path_of(T) == "decode":
-        return n_touched * expert_gu_bytes(d) + T * d.hidden * 2 + T * d.top_k * d.inter * 2
+        shared = d.has_shared if T == 1 else 0
+        return ((n_touched + shared) * expert_gu_bytes(d) + T * d.hidden * 2
+                + T * (d.top_k + shared) * d.inter * 2)
     return gu_kernel_bytes(d, T, n_touched)
 
 

@@ -155,9 +155,9 @@ int moe_unpack(const moe_dims_t* d, const void* packed, void* q_gate, void* s_ga
  * cumulative weight (fp64, summed in slot order) reaches top_p is kept, and
  * the kept weights are renormalised over the kept slots; dropped slots get
  * topk_idx = -1 and topk_w = 0.
- * Batches of T <= moe_decode_max_tokens() are routed by the same router
- * workgroups as the GEMV path of moe_w4a16_forward, larger ones by the
- * batched router of the grouped-GEMM path.
+ * Batches of T <= moe_decode_max_tokens() are routed by the router
+ * workgroups and the top-k code of the GEMV path of moe_w4a16_forward,
+ * larger ones by the batched router of the grouped-GEMM path.
  * Outputs:
  *   topk_idx int32 [T][k], topk_w fp32 [T][k];
  *   n_unique int32 [1]: distinct experts chosen by the batch;
@@ -190,7 +190,9 @@ int moe_w4a16_forward(const moe_dims_t* d, const moe_weights_t* w, const uint16_
  * (so the interval holds the stage's kernels and the gaps between them, not
  * the launch overhead around them).  Stages on the decode path (T <=
  * moe_decode_max_tokens()): 0 routing + union + shared expert gate/up,
- * 1 routed gate/up + SwiGLU, 2 down projections + combine.  On the
+ * 1 routed gate/up + SwiGLU, 2 down projections + combine; for T == 1,
+ * stage 0 holds the router logits alone and stage 1 the top-k, union and
+ * every gate/up (shared and routed).  On the
  * grouped-GEMM path: 0 routing + union, 1 gate/up + SwiGLU, 2 down +
  * combine.  Adds no synchronisation.  Same arguments and results as
  * moe_w4a16_forward; n_events outside 0..6 or a NULL array with n_events

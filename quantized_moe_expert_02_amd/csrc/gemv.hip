@@ -317,12 +317,16 @@ struct DecArgs {
   int n_router;       // E * rsplit
   int n_router_wg;    // workgroups of router units
   int with_slots;     // forward: also write the slot table (moe_route: no)
+  int gu_routes;      // one token: the routed gate/up workgroups take the top-k
+                      // themselves (the routing launch ends with its router units)
+  int n_sgu_in_gu;    // shared gate/up workgroups placed in the routed gate/up launch
 };
 
 struct SlotInfo {
   const uint8_t* base;
-  int n;   // tokens
-  int p0;  // first entry in pairs (routed) or -1 (shared)
+  int n;     // tokens
+  int p0;    // first entry in pairs (routed) or -1 (shared)
+  int pair;  // >= 0: the pair of a one-token slot, known without the pairs table
 };
 
 // Tables that an earlier launch wrote (slot table, pairs) are read with
@@ -341,6 +345,7 @@ __device__ __forceinline__ bool get_slot(const DecArgs& a, int s, SlotInfo& si) 
     si.base = (const uint8_t*)a.shared;
     si.n = a.T;
     si.p0 = -1;
+    si.pair = -1;
     return true;
   }
   static_assert(sizeof(SlotEntry) == 16, "slot entry is one 16-byte scalar load");
@@ -348,13 +353,17 @@ __device__ __forceinline__ bool get_slot(const DecArgs& a, int s, SlotInfo& si) 
   si.base = reinterpret_cast<const uint8_t*>((uint64_t)e.x | ((uint64_t)e.y << 32));
   si.n = (int)e.z;
   si.p0 = (int)e.w;
+  si.pair = -1;
   return si.n > 0;
 }
 
 // Token index and output row (pair id, or T*k + t for the shared expert)
 // of the i-th token of a slot.
 __device__ __forceinline__ void slot_token(const DecArgs& a, const SlotInfo& si, int i, int& t, int& row) {
-  if (si.p0 < 0) {
+  if (si.pair >= 0) {
+    t = si.pair / a.k;
+    row = si.pair;
+  } else if (si.p0 < 0) {
     t = i;
     row = a.T * a.k + i;
   } else {
@@ -564,6 +573,7 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int it = blockIdx.x * kWpg + wave;
   if (it < a.n_router) router_unit(a, it);
+  if (a.gu_routes) return;  // the routed gate/up launch ranks the token
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);  // this wavefront's logit stores are done
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -589,6 +599,69 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
     if (a.T == 1) union_one(a, ls);
     else union_step(a, ls);
   }
+}
+
+// ---- one token: routing inside the routed gate/up launch ----------------------
+// Every routed gate/up workgroup ranks the token itself from the partial
+// logits that the routing launch wrote (wavefront 0, the same top-k as the
+// routing leader would take, so every workgroup reaches the same slots), and
+// takes the expert of its union slot u: the kept slot whose expert has u kept
+// experts below it.  The routing launch therefore ends with its router units:
+// no arrival chain, no leader, no slot-table lookup before the weight stream.
+// Workgroup 0 also writes the routing outputs, the union and the slot table
+// that the down launch reads.  Returns false when u is past the union (slots
+// dropped by top-p).
+struct RouteOneLds {
+  RankSlots<1> rank;
+  int pe[kMaxTopK];
+  int e, j;
+};
+
+__device__ __forceinline__ bool route_one(const DecArgs& a, int u, bool writer, SlotInfo& si, RouteOneLds& ls) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wave == 0) {
+    topk_tokens(a.z, a.rsplit, (size_t)a.E, a.rbias, a.E, a.k, a.top_p, 1, writer ? a.topk_idx : nullptr,
+                writer ? a.topk_w : nullptr, ls.pe, ls.rank);
+    wave_lds_sync();
+    const int e = lane < a.k ? ls.pe[lane] : -1;
+    int r = 0;  // kept experts below e
+    for (int j = 0; j < a.k; ++j) {
+      const int ej = __builtin_amdgcn_readlane(e, j);
+      r += (ej >= 0 && ej < e) ? 1 : 0;
+    }
+    const uint64_t hit = __ballot(e >= 0 && r == u);
+    const int l = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
+    if (lane == 0) {
+      ls.e = hit ? __builtin_amdgcn_readlane(e, l) : -1;
+      ls.j = l;
+    }
+    if (writer) {  // the union of one token (as union_one) and the slot table
+      const int nu = __popcll(__ballot(e >= 0));
+      if (e >= 0) {
+        a.uniq_ids[r] = e;
+        a.uniq_off[r] = r;
+        SlotEntry se;
+        se.base = (const uint8_t*)a.experts[e];
+        se.n = 1;
+        se.p0 = r;
+        a.slots[a.S + r] = se;
+        a.pairs[r] = lane;
+      }
+      if (lane == 0) {
+        *a.n_unique = nu;
+        a.uniq_off[nu] = nu;
+      }
+      for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
+    }
+  }
+  __syncthreads();
+  const int e = ls.e;
+  if (e < 0) return false;
+  si.base = (const uint8_t*)a.experts[e];
+  si.n = 1;
+  si.p0 = -1;  // unused: the pair is known
+  si.pair = ls.j;
+  return true;
 }
 
 // ---- gate/up: one (slot, 64-row block) per workgroup --------------------------
@@ -726,10 +799,9 @@ __device__ __forceinline__ void gu_tile_group(const DecArgs& a, const uint16_t* 
 }
 
 template <int FMT, int KT>
-__device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __restrict__ x, int s, int rb, int grp,
-                                         int ngrp, int nw, int nch, int tile, int ntiles, GuLds<KT>& ls) {
-  SlotInfo si;
-  if (!get_slot(a, s, si)) return;  // uniform over the workgroup
+__device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __restrict__ x, int s, const SlotInfo& si,
+                                         int rb, int grp, int ngrp, int nw, int nch, int tile, int ntiles,
+                                         GuLds<KT>& ls) {
   const GuScales gs = gu_scales<FMT>(a, si, rb);
   // token tiles tile, tile + ntiles, ... of the slot (several workgroups
   // share a slot's tiles when ntiles > 1)
@@ -883,6 +955,25 @@ __device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rbg, DnLds<
   }
 }
 
+// Shared expert gate/up, workgroup j of its grid: workgroup = (token tile,
+// row block, group of kWpg K-segments); the tiles of one (row block, group)
+// are n_rbg workgroups apart, a multiple of 8, so they run on one XCD and
+// share its L2 copy of the weights.
+template <int FMT, int KT>
+__device__ __forceinline__ void shared_gu(const DecArgs& a, const uint16_t* __restrict__ x, int j, GuLds<KT>& gl) {
+  const int nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw, n_rbg = (a.I / 64) * ngrp;
+  const int r = j % n_rbg;
+  SlotInfo si;
+  get_slot(a, 0, si);
+  gu_group<FMT, KT>(a, x, 0, si, r / ngrp, r % ngrp, ngrp, nw, a.cpu_sgu, j / n_rbg, (a.T + KT - 1) / KT, gl);
+}
+
+// Workgroups of the shared expert's gate/up.
+inline int shared_gu_workgroups(const DecArgs& a, int KT) {
+  const int nw = std::min(kWpg, a.ks_sgu);
+  return a.S * (a.I / 64) * (a.ks_sgu / nw) * ((a.T + KT - 1) / KT);
+}
+
 // ---- kernels ---------------------------------------------------------------------
 template <int FMT, int KT>
 __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint16_t* __restrict__ x) {
@@ -893,13 +984,7 @@ __global__ __launch_bounds__(64 * kWpg) void k_route_phase(DecArgs a, const uint
     router_workgroup(a, ul);
     return;
   }
-  // shared expert: workgroup = (token tile, row block, group of kWpg
-  // K-segments); the tiles of one (row block, group) are n_rbg workgroups
-  // apart, a multiple of 8, so they run on one XCD and share its L2 copy
-  // of the weights
-  const int nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw, n_rbg = (a.I / 64) * ngrp;
-  const int j = b - a.n_router_wg, r = j % n_rbg;
-  gu_group<FMT, KT>(a, x, 0, r / ngrp, r % ngrp, ngrp, nw, a.cpu_sgu, j / n_rbg, (a.T + KT - 1) / KT, gl);
+  shared_gu<FMT, KT>(a, x, b - a.n_router_wg, gl);
 }
 
 // moe_route on small batches: the router workgroups of k_route_phase alone
@@ -912,10 +997,24 @@ __global__ __launch_bounds__(64 * kWpg) void k_route_only(DecArgs a) {
 template <int FMT, int KT>
 __global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_t* __restrict__ x) {
   __shared__ GuLds<KT> gl;
+  __shared__ RouteOneLds rl;
   // workgroup = (slot, row block, group of kWpg K-segments)
+  // with gu_routes, the shared expert's gate/up workgroups come first (they
+  // stream while the routed workgroups rank the token)
+  const int b = blockIdx.x - a.n_sgu_in_gu;
+  if (b < 0) {
+    shared_gu<FMT, KT>(a, x, blockIdx.x, gl);
+    return;
+  }
   const int nw = min(kWpg, a.ks_gu), ngrp = a.ks_gu / nw, per_slot = (a.I / 64) * ngrp;
-  const int r = blockIdx.x % per_slot;
-  gu_group<FMT, KT>(a, x, a.S + blockIdx.x / per_slot, r / ngrp, r % ngrp, ngrp, nw, a.cpu_gu, 0, 1, gl);
+  const int u = b / per_slot, r = b % per_slot;
+  SlotInfo si;
+  if (a.gu_routes) {
+    if (!route_one(a, u, b == 0, si, rl)) return;  // uniform over the workgroup
+  } else if (!get_slot(a, a.S + u, si)) {
+    return;
+  }
+  gu_group<FMT, KT>(a, x, a.S + u, si, r / ngrp, r % ngrp, ngrp, nw, a.cpu_gu, 0, 1, gl);
 }
 
 template <int FMT, int KT>
@@ -926,13 +1025,15 @@ __global__ __launch_bounds__(64 * kWpg) void k_dn_phase(DecArgs a) {
 }
 
 template <int FMT, int KT>
-hipError_t launch_phases(const DecArgs& a, const uint16_t* x, hipStream_t s, const StageEvents& se) {
-  const int nw = min(kWpg, a.ks_sgu);
-  const int sgu_wg = a.S * (a.I / 64) * (a.ks_sgu / nw) * ((a.T + KT - 1) / KT);
+hipError_t launch_phases(DecArgs a, const uint16_t* x, hipStream_t s, const StageEvents& se) {
+  const int sgu_wg = shared_gu_workgroups(a, KT);
+  // one token: the shared gate/up moves to the routed gate/up launch
+  a.n_sgu_in_gu = a.gu_routes ? sgu_wg : 0;
   const dim3 blk(64 * kWpg);
-  launch_k(k_route_phase<FMT, KT>, dim3(a.n_router_wg + sgu_wg), blk, s, se.start(0), se.stop(0), a, x);
+  launch_k(k_route_phase<FMT, KT>, dim3(a.n_router_wg + sgu_wg - a.n_sgu_in_gu), blk, s, se.start(0), se.stop(0), a,
+           x);
   const int gu_wg = (a.slots_max - a.S) * (a.I / 64) * (a.ks_gu / min(kWpg, a.ks_gu));
-  launch_k(k_gu_phase<FMT, KT>, dim3(gu_wg), blk, s, se.start(1), se.stop(1), a, x);
+  launch_k(k_gu_phase<FMT, KT>, dim3(a.n_sgu_in_gu + gu_wg), blk, s, se.start(1), se.stop(1), a, x);
   const int rpw = kWpg / a.ks_dn;
   launch_k(k_dn_phase<FMT, KT>, dim3(a.slots_max * ((a.H / 64 + rpw - 1) / rpw)), blk, s, se.start(2), se.stop(2), a);
   return hipGetLastError();
@@ -986,6 +1087,7 @@ DecArgs dec_args(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, con
   a.n_router = p.E * a.rsplit;
   a.n_router_wg = (a.n_router + kWpg - 1) / kWpg;
   a.with_slots = with_slots ? 1 : 0;
+  a.gu_routes = (with_slots && p.T == 1) ? 1 : 0;
   return a;
 }
 

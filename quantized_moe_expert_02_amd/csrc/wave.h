@@ -273,8 +273,8 @@ struct RankSlots {
 // (ties to the lower expert index): the lane holding it recognises itself
 // from the wave-wide maximum, records it in slot j of rs and pops it, so a
 // round's dependent chain is the reduction, one compare and the pop.
-// Outputs are written with device-coherent stores: idx_out[t * k + j],
-// w_out[...], and slot_expert[t * k + j] (LDS) if set.
+// Outputs are written with device-coherent stores: idx_out[t * k + j] and
+// w_out[...] if idx_out is set, and slot_expert[t * k + j] (LDS) if set.
 template <int kPer, int NT>
 __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstride, const float* bias, int E, int k,
                                            float top_p, int32_t* idx_out, float* w_out, int* slot_expert,
@@ -374,13 +374,17 @@ __device__ __forceinline__ void topk_multi(const double* z, int nz, size_t zstri
     my_key[t] = lane < k ? rs.key[t][lane] : 0ull;
     my_e[t] = lane < k ? rs.e[t][lane] : -1;
   }
+  // the weights are needed for the outputs, or to decide which slots top-p keeps
+  const bool need_w = idx_out || (top_p > 0.0f && top_p < 1.0f);
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
-    const SlotWeight sw = slot_weights(from_order_key(my_key[t]), k, top_p);
+    const SlotWeight sw = need_w ? slot_weights(from_order_key(my_key[t]), k, top_p) : SlotWeight{k, 0.0f};
     if (lane < k) {
       const int32_t e_out = lane < sw.m ? my_e[t] : -1;
-      st_dev(idx_out + t * k + lane, e_out);
-      st_dev(w_out + t * k + lane, sw.w);
+      if (idx_out) {
+        st_dev(idx_out + t * k + lane, e_out);
+        st_dev(w_out + t * k + lane, sw.w);
+      }
       if (slot_expert) slot_expert[t * k + lane] = e_out;
     }
   }
@@ -394,7 +398,8 @@ __device__ __forceinline__ void topk_tokens_per(const double* z, int nz, size_t 
                                                 int k, float top_p, int T, int32_t* idx_out, float* w_out,
                                                 int* slot_expert, RankSlots<1>& rs) {
   for (int t0 = 0; t0 < T; ++t0)
-    topk_multi<kPer, 1>(z + (size_t)t0 * E, nz, zstride, bias, E, k, top_p, idx_out + t0 * k, w_out + t0 * k,
+    topk_multi<kPer, 1>(z + (size_t)t0 * E, nz, zstride, bias, E, k, top_p, idx_out ? idx_out + t0 * k : nullptr,
+                        w_out ? w_out + t0 * k : nullptr,
                         slot_expert + t0 * k, rs);
 }
 
