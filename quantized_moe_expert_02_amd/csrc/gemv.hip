@@ -18,6 +18,8 @@
 // workgroup, device-scope arrival counters across workgroups), so results
 // are deterministic and no float atomics are used.  The three launches are
 // described below, before the kernels.
+#include <utility>
+
 #include "wave.h"
 
 namespace moe {
@@ -601,33 +603,190 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
   }
 }
 
+// ---- one token: top-k by the four wavefronts of a workgroup -------------------
+// Experts are ordered by (logit descending, index ascending), a total order.
+// Fast path (E <= 256, k <= 16): wavefront w holds experts 64w .. 64w+63,
+// one per lane; an expert's rank in that group is the number of members
+// whose key has a larger high word, counted against every lane through row
+// rotations (DPP) of the four row arrangements of the wavefront; the k first
+// of every group are candidates; wavefront 0 ranks the 4k candidates the
+// same way.  That is exact as long as no two of the experts involved share a
+// high word: every expert above a true top-k member is then a candidate of
+// its group, and a non-member counts k or more.  Two candidates on one rank
+// show such a tie (or keys that differ only in their low words), and then
+// -- as for larger E or k -- every expert is ranked exactly against all E
+// keys in LDS, index included.
+struct TopkLds {
+  uint64_t key[kMaxExperts];
+  const uint8_t* ep[kMaxExperts];  // packed expert pointers, loaded beside the logits
+  uint32_t chi[kWpg * 16];         // fast path: each group's candidates by rank, high words
+  int cidx[kWpg * 16];             //   and experts (-1: none)
+  int tie[kWpg];
+  uint64_t sk[kMaxTopK];           // slot j: key and expert
+  int se[kMaxTopK];
+  int ok;
+};
+
+// Expert f (key kf) comes before expert e (key ke).
+__device__ __forceinline__ bool comes_before(uint64_t kf, int f, uint64_t ke, int e) {
+  return kf > ke || (kf == ke && f < e);
+}
+
+// Logit key of expert e (the planes added in order, then the bias, as the
+// serial top-k adds them).  The planes were written by the previous launch:
+// plain loads, so that the workgroups of one XCD share its L2 copy (every
+// workgroup of the launch reads the same few KiB at once).
+__device__ __forceinline__ uint64_t logit_key(const DecArgs& a, int e) {
+  // every plane slot is loaded (a slot past rsplit re-reads plane 0 and is
+  // not added), so that the loads issue together: one memory latency
+  double zs[kMaxLogitParts];
+#pragma unroll
+  for (int s = 0; s < kMaxLogitParts; ++s) zs[s] = a.z[(size_t)(s < a.rsplit ? s : 0) * a.E + e];
+  const float b = a.rbias ? a.rbias[e] : 0.0f;
+  double v = 0.0;
+#pragma unroll
+  for (int s = 0; s < kMaxLogitParts; ++s)
+    if (s < a.rsplit) v += zs[s];
+  if (a.rbias) v += (double)b;
+  return order_key(v);
+}
+
+// Number of lanes whose value is larger than this lane's (values held one
+// per lane): every lane is reached by one of 16 row rotations of one of the
+// four row arrangements (rows as they are, swapped by 16, by 32, by 48).
+template <int... R>
+__device__ __forceinline__ int count_larger_rot(uint32_t v, uint32_t h, std::integer_sequence<int, R...>) {
+  // row_ror:r for r = 1..15 (DPP control 0x120 + r)
+  return ((((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121 + R, 0xF, 0xF, false) > h) ? 1 : 0) + ...);
+}
+
+__device__ __forceinline__ int count_larger(uint32_t h) {
+  const uint32_t x16 = (uint32_t)partner<16>((int)h);
+  const uint32_t v[4] = {h, x16, (uint32_t)partner<32>((int)h), (uint32_t)partner<32>((int)x16)};
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) c += (v[q] > h ? 1 : 0) + count_larger_rot(v[q], h, std::make_integer_sequence<int, 15>{});
+  return c;
+}
+
+// Every lane ends with the OR of the lanes' values.
+__device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
+  v |= (uint32_t)partner<1>((int)v);
+  v |= (uint32_t)partner<2>((int)v);
+  v |= (uint32_t)partner<4>((int)v);
+  v |= (uint32_t)partner<8>((int)v);
+  v |= (uint32_t)partner<16>((int)v);
+  v |= (uint32_t)partner<32>((int)v);
+  return v;
+}
+
+// Called by the whole workgroup.  Afterwards lane j < k of wavefront 0 holds
+// slot j: its key (kj) and expert (ej); ls.ep holds the expert pointers.
+__device__ __forceinline__ void topk_parallel(const DecArgs& a, TopkLds& ls, uint64_t& kj, int& ej) {
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+  const int E = a.E, k = a.k;
+  constexpr int NT = kWpg * 64;
+  for (int e = tid; e < E; e += NT) {
+    ls.key[e] = logit_key(a, e);
+    ls.ep[e] = (const uint8_t*)a.experts[e];
+  }
+  const bool try_fast = E <= NT && k <= 16;
+  if (try_fast) {
+    // (this lane wrote key[tid] above); 0: empty, below every real high word
+    const uint32_t h = tid < E ? (uint32_t)(ls.key[tid] >> 32) : 0u;
+    const int gt = count_larger(h);
+    const bool cand = tid < E && gt < k;
+    if (lane < 16) ls.chi[wave * 16 + lane] = 0u, ls.cidx[wave * 16 + lane] = -1;
+    if (cand) {
+      ls.chi[wave * 16 + gt] = h;
+      ls.cidx[wave * 16 + gt] = tid;
+    }
+    const uint32_t taken = wave_or_u32(cand ? 1u << gt : 0u);
+    const int ncand = __popcll(__ballot(cand));  // (a ballot outside any lane branch)
+    if (lane == 0) ls.tie[wave] = __popc(taken) != ncand;
+  }
+  __syncthreads();
+  bool fast = try_fast;
+  if (fast) {
+#pragma unroll
+    for (int w = 0; w < kWpg; ++w) fast = fast && !ls.tie[w];
+  }
+  if (fast) {
+    if (wave == 0) {
+      // lane l holds candidate (group l / k, rank l % k)
+      const int nc = kWpg * k;
+      const uint32_t h = lane < nc ? ls.chi[(lane / k) * 16 + lane % k] : 0u;
+      const int ci = lane < nc ? ls.cidx[(lane / k) * 16 + lane % k] : -1;
+      const int R = count_larger(h);
+      const bool top = ci >= 0 && R < k;
+      const uint32_t taken = wave_or_u32(top ? 1u << R : 0u);
+      const bool ok = __popcll(__ballot(top)) == k && __popc(taken) == k;
+      if (ok && top) ls.se[R] = ci;
+      wave_lds_sync();
+      if (ok && lane < k) {
+        ej = ls.se[lane];
+        kj = ls.key[ej];
+      }
+      if (lane == 0) ls.ok = ok;
+    }
+    __syncthreads();
+    fast = ls.ok;
+  }
+  if (!fast) {  // exact ranks of every expert against all E keys
+    for (int e = tid; e < E; e += NT) {
+      const uint64_t ke = ls.key[e];
+      int R = 0;
+      for (int f = 0; f < E; ++f) R += comes_before(ls.key[f], f, ke, e) ? 1 : 0;
+      if (R < k) {
+        ls.sk[R] = ke;
+        ls.se[R] = e;
+      }
+    }
+    __syncthreads();
+    if (wave == 0 && lane < k) {
+      kj = ls.sk[lane];
+      ej = ls.se[lane];
+    }
+  }
+}
+
 // ---- one token: routing inside the routed gate/up launch ----------------------
 // Every routed gate/up workgroup ranks the token itself from the partial
-// logits that the routing launch wrote (wavefront 0, the same top-k as the
-// routing leader would take, so every workgroup reaches the same slots), and
-// takes the expert of its union slot u: the kept slot whose expert has u kept
-// experts below it.  The routing launch therefore ends with its router units:
-// no arrival chain, no leader, no slot-table lookup before the weight stream.
-// Workgroup 0 also writes the routing outputs, the union and the slot table
-// that the down launch reads.  Returns false when u is past the union (slots
-// dropped by top-p).
+// logits that the routing launch wrote (the same fp64 logits and order as
+// the routing leader would use, so every workgroup reaches the same slots),
+// and takes the expert of its union slot u: the kept slot whose expert has u
+// kept experts below it.  The routing launch therefore ends with its router
+// units: no arrival chain, no leader, no slot-table lookup before the weight
+// stream.  Workgroup 0 also writes the routing outputs, the union and the
+// slot table that the down launch reads.  Returns false when u is past the
+// union (slots dropped by top-p).
 struct RouteOneLds {
-  RankSlots<1> rank;
-  int pe[kMaxTopK];
+  TopkLds tk;
   int e, j;
 };
 
 __device__ __forceinline__ bool route_one(const DecArgs& a, int u, bool writer, SlotInfo& si, RouteOneLds& ls) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // the ranking shares its SIMDs with the shared expert's streaming
+  // wavefronts: it goes first while it runs
+  __builtin_amdgcn_s_setprio(3);
+  uint64_t kj = 0;
+  int ej = -1;
+  topk_parallel(a, ls.tk, kj, ej);
   if (wave == 0) {
-    topk_tokens(a.z, a.rsplit, (size_t)a.E, a.rbias, a.E, a.k, a.top_p, 1, writer ? a.topk_idx : nullptr,
-                writer ? a.topk_w : nullptr, ls.pe, ls.rank);
-    wave_lds_sync();
-    const int e = lane < a.k ? ls.pe[lane] : -1;
+    // slot j in lane j; the weights are formed only where they are written
+    // or decide which slots top-p keeps
+    const bool need_w = writer || a.top_p_on;
+    const SlotWeight sw = need_w ? slot_weights(from_order_key(kj), a.k, a.top_p) : SlotWeight{a.k, 0.0f};
+    const int e = lane < sw.m ? ej : -1;  // kept slots
+    if (writer && lane < a.k) {
+      a.topk_idx[lane] = e;
+      a.topk_w[lane] = sw.w;
+    }
     int r = 0;  // kept experts below e
     for (int j = 0; j < a.k; ++j) {
-      const int ej = __builtin_amdgcn_readlane(e, j);
-      r += (ej >= 0 && ej < e) ? 1 : 0;
+      const int ej2 = __builtin_amdgcn_readlane(e, j);
+      r += (ej2 >= 0 && ej2 < e) ? 1 : 0;
     }
     const uint64_t hit = __ballot(e >= 0 && r == u);
     const int l = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
@@ -641,7 +800,7 @@ __device__ __forceinline__ bool route_one(const DecArgs& a, int u, bool writer, 
         a.uniq_ids[r] = e;
         a.uniq_off[r] = r;
         SlotEntry se;
-        se.base = (const uint8_t*)a.experts[e];
+        se.base = ls.tk.ep[e];
         se.n = 1;
         se.p0 = r;
         a.slots[a.S + r] = se;
@@ -655,9 +814,10 @@ __device__ __forceinline__ bool route_one(const DecArgs& a, int u, bool writer, 
     }
   }
   __syncthreads();
+  __builtin_amdgcn_s_setprio(0);
   const int e = ls.e;
   if (e < 0) return false;
-  si.base = (const uint8_t*)a.experts[e];
+  si.base = ls.tk.ep[e];
   si.n = 1;
   si.p0 = -1;  // unused: the pair is known
   si.pair = ls.j;
@@ -1000,21 +1160,27 @@ __global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_
   __shared__ RouteOneLds rl;
   // workgroup = (slot, row block, group of kWpg K-segments)
   // with gu_routes, the shared expert's gate/up workgroups come first (they
-  // stream while the routed workgroups rank the token)
+  // stream while the routed workgroups rank the token); one gu_group call
+  // serves both kinds
   const int b = blockIdx.x - a.n_sgu_in_gu;
-  if (b < 0) {
-    shared_gu<FMT, KT>(a, x, blockIdx.x, gl);
-    return;
-  }
-  const int nw = min(kWpg, a.ks_gu), ngrp = a.ks_gu / nw, per_slot = (a.I / 64) * ngrp;
-  const int u = b / per_slot, r = b % per_slot;
   SlotInfo si;
-  if (a.gu_routes) {
-    if (!route_one(a, u, b == 0, si, rl)) return;  // uniform over the workgroup
-  } else if (!get_slot(a, a.S + u, si)) {
-    return;
+  int s, r, ngrp, nw, nch, tile, ntiles;
+  if (b < 0) {
+    nw = min(kWpg, a.ks_sgu), ngrp = a.ks_sgu / nw;
+    const int n_rbg = (a.I / 64) * ngrp;
+    r = blockIdx.x % n_rbg, s = 0, nch = a.cpu_sgu, tile = blockIdx.x / n_rbg, ntiles = (a.T + KT - 1) / KT;
+    get_slot(a, 0, si);
+  } else {
+    nw = min(kWpg, a.ks_gu), ngrp = a.ks_gu / nw;
+    const int per_slot = (a.I / 64) * ngrp, u = b / per_slot;
+    r = b % per_slot, s = a.S + u, nch = a.cpu_gu, tile = 0, ntiles = 1;
+    if (a.gu_routes) {
+      if (!route_one(a, u, b == 0, si, rl)) return;  // uniform over the workgroup
+    } else if (!get_slot(a, s, si)) {
+      return;
+    }
   }
-  gu_group<FMT, KT>(a, x, a.S + u, si, r / ngrp, r % ngrp, ngrp, nw, a.cpu_gu, 0, 1, gl);
+  gu_group<FMT, KT>(a, x, s, si, r / ngrp, r % ngrp, ngrp, nw, nch, tile, ntiles, gl);
 }
 
 template <int FMT, int KT>

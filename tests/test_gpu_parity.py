@@ -191,6 +191,64 @@ def test_forward_one_token_matches_oracle(name, dims):
     assert_close(y, y_ref, name)
 
 
+def _twin_layer(dims, seed, rank_a, rank_b):
+    """A layer whose experts at oracle ranks rank_a and rank_b (of the token)
+    get the same router row, so their logits tie exactly."""
+    layer = synth.make_layer(dims, seed)
+    x = synth.make_tokens(dims, 1, seed)
+    order = np.argsort(-oracle_route(layer, x).z[0], kind="stable")
+    a, b = int(order[rank_a]), int(order[rank_b])
+    rw = layer.router_w.clone()
+    rw[b] = rw[a]
+    layer.router_w = rw
+    return layer, x, (a, b)
+
+
+# (E, k, rank of the copied row, rank of the twin): ties at the top, inside
+# the top-k, across its boundary, and below it; E = 300 takes the serial
+# top-k from the start.  The workgroup-parallel top-k must find the tie and
+# fall back, so equal logits still go to the lower expert index.
+ONE_TOKEN_TIES = [(32, 4, 0, 5), (64, 8, 2, 3), (64, 8, 7, 9), (256, 8, 20, 30), (256, 16, 0, 15), (300, 8, 0, 1)]
+
+
+@pytest.mark.parametrize("E,k,ra,rb", ONE_TOKEN_TIES)
+def test_forward_one_token_tied_logits(E, k, ra, rb):
+    dims = synth.Dims(512, 256, E, k, 1, synth.INT4_ROW)
+    _log("one token tied logits", dims, ra, rb)
+    layer, x, ab = _twin_layer(dims, ("tie1", E, k, ra, rb), ra, rb)
+    r = oracle_route(layer, x)
+    z = r.z[0]
+    assert z[ab[0]] == z[ab[1]]
+    pl = moe.PackedLayer.from_layer(layer)
+    ti = torch.empty((1, k), dtype=torch.int32, device=DEV)
+    tw = torch.empty((1, k), dtype=torch.float32, device=DEV)
+    y = moe.moe_w4a16_forward(pl, x.to(DEV), topk_idx=ti, topk_w=tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
+    np.testing.assert_allclose(tw.cpu().numpy(), r.topk_w, rtol=1e-6, atol=0)
+    assert_close(y, oracle_y(layer, x), f"ties E={E} k={k}")
+
+
+@pytest.mark.parametrize("p,m", [(0.625, 5), (0.626, 6), (0.75, 6), (1e-6, 1), (0.9999, 8)])
+def test_forward_one_token_zero_logits_top_p(p, m):
+    """Zero router weights for one token: every logit is 0, every expert ties
+    (lower index first), and top-p keeps exactly m of the k = 8 slots."""
+    dims = synth.Dims(256, 128, 12, 8, 1, synth.INT4_ROW, top_p=p)
+    layer = synth.make_layer(dims, ("zero-logit-1", p))
+    layer.router_w = torch.zeros_like(layer.router_w)
+    x = synth.make_tokens(dims, 1, ("zero-logit-1", p))
+    r = oracle_route(layer, x)
+    assert (r.topk_idx >= 0).sum() == m
+    pl = moe.PackedLayer.from_layer(layer)
+    ti = torch.empty((1, 8), dtype=torch.int32, device=DEV)
+    tw = torch.empty((1, 8), dtype=torch.float32, device=DEV)
+    y = moe.moe_w4a16_forward(pl, x.to(DEV), topk_idx=ti, topk_w=tw)
+    torch.cuda.synchronize()
+    assert np.array_equal(ti.cpu().numpy(), r.topk_idx)
+    np.testing.assert_allclose(tw.cpu().numpy(), r.topk_w, rtol=1e-6, atol=0)
+    assert_close(y, oracle_y(layer, x), f"zero logits p={p}")
+
+
 def test_forward_deterministic_and_batch_invariant():
     dims = synth.Dims(1024, 256, 64, 4, 1, 0)
     layer = synth.make_layer(dims, "det")
