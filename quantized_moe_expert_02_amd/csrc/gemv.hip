@@ -609,8 +609,8 @@ __device__ __forceinline__ void router_workgroup(const DecArgs& a, UnionLds& ls)
 // one per lane; an expert's rank in that group is the number of members
 // whose key has a larger high word, counted against every lane through row
 // rotations (DPP) of the four row arrangements of the wavefront; the k first
-// of every group are candidates; wavefront 0 ranks the 4k candidates the
-// same way.  That is exact as long as no two of the experts involved share a
+// of every group are candidates; every wavefront ranks the 4k candidates the
+// same way (no barrier afterwards).  That is exact as long as no two of the experts involved share a
 // high word: every expert above a true top-k member is then a candidate of
 // its group, and a non-member counts k or more.  Two candidates on one rank
 // show such a tie (or keys that differ only in their low words), and then
@@ -622,9 +622,9 @@ struct TopkLds {
   uint32_t chi[kWpg * 16];         // fast path: each group's candidates by rank, high words
   int cidx[kWpg * 16];             //   and experts (-1: none)
   int tie[kWpg];
-  uint64_t sk[kMaxTopK];           // slot j: key and expert
-  int se[kMaxTopK];
-  int ok;
+  int se[kWpg][kMaxTopK];          // fast path: each wavefront's slot experts
+  uint64_t sk[kMaxTopK];           // exact path: slot j, key and expert
+  int sx[kMaxTopK];
 };
 
 // Expert f (key kf) comes before expert e (key ke).
@@ -660,12 +660,16 @@ __device__ __forceinline__ int count_larger_rot(uint32_t v, uint32_t h, std::int
   return ((((uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x121 + R, 0xF, 0xF, false) > h) ? 1 : 0) + ...);
 }
 
+// NQ = 4: all 64 lanes; NQ = 2: lanes 0-31 (rows 0 and 1) only, for values
+// held in those lanes.
+template <int NQ>
 __device__ __forceinline__ int count_larger(uint32_t h) {
   const uint32_t x16 = (uint32_t)partner<16>((int)h);
-  const uint32_t v[4] = {h, x16, (uint32_t)partner<32>((int)h), (uint32_t)partner<32>((int)x16)};
+  uint32_t v[4] = {h, x16, 0u, 0u};
+  if (NQ == 4) v[2] = (uint32_t)partner<32>((int)h), v[3] = (uint32_t)partner<32>((int)x16);
   int c = 0;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) c += (v[q] > h ? 1 : 0) + count_larger_rot(v[q], h, std::make_integer_sequence<int, 15>{});
+  for (int q = 0; q < NQ; ++q) c += (v[q] > h ? 1 : 0) + count_larger_rot(v[q], h, std::make_integer_sequence<int, 15>{});
   return c;
 }
 
@@ -680,9 +684,15 @@ __device__ __forceinline__ uint32_t wave_or_u32(uint32_t v) {
   return v;
 }
 
-// Called by the whole workgroup.  Afterwards lane j < k of wavefront 0 holds
-// slot j: its key (kj) and expert (ej); ls.ep holds the expert pointers.
-__device__ __forceinline__ void topk_parallel(const DecArgs& a, TopkLds& ls, uint64_t& kj, int& ej) {
+// Called by the whole workgroup.  On the fast path (returns true) lane l of
+// every wavefront holds candidate l: its expert ci (-1: none) and its rank R
+// among all experts (the slots are the candidates with R < k); with
+// `slots`, lane j < k also gets slot j's key (kj) and expert (ej).  On the
+// exact path (returns false) lane j < k gets kj and ej.  Every wavefront
+// ranks the candidates itself (the same data, the same result), so the fast
+// path ends without a barrier.  ls.ep holds the expert pointers.
+__device__ __forceinline__ bool topk_parallel(const DecArgs& a, TopkLds& ls, bool slots, int& R, int& ci, uint64_t& kj,
+                                              int& ej) {
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int E = a.E, k = a.k;
   constexpr int NT = kWpg * 64;
@@ -690,11 +700,13 @@ __device__ __forceinline__ void topk_parallel(const DecArgs& a, TopkLds& ls, uin
     ls.key[e] = logit_key(a, e);
     ls.ep[e] = (const uint8_t*)a.experts[e];
   }
+  // fast path: group w is experts 64w .. 64w+63, held by wavefront w (the
+  // thread of expert e wrote its key above)
   const bool try_fast = E <= NT && k <= 16;
   if (try_fast) {
-    // (this lane wrote key[tid] above); 0: empty, below every real high word
+    // 0: empty, below every real high word
     const uint32_t h = tid < E ? (uint32_t)(ls.key[tid] >> 32) : 0u;
-    const int gt = count_larger(h);
+    const int gt = count_larger<4>(h);
     const bool cand = tid < E && gt < k;
     if (lane < 16) ls.chi[wave * 16 + lane] = 0u, ls.cidx[wave * 16 + lane] = -1;
     if (cand) {
@@ -712,90 +724,87 @@ __device__ __forceinline__ void topk_parallel(const DecArgs& a, TopkLds& ls, uin
     for (int w = 0; w < kWpg; ++w) fast = fast && !ls.tie[w];
   }
   if (fast) {
-    if (wave == 0) {
-      // lane l holds candidate (group l / k, rank l % k)
-      const int nc = kWpg * k;
-      const uint32_t h = lane < nc ? ls.chi[(lane / k) * 16 + lane % k] : 0u;
-      const int ci = lane < nc ? ls.cidx[(lane / k) * 16 + lane % k] : -1;
-      const int R = count_larger(h);
-      const bool top = ci >= 0 && R < k;
-      const uint32_t taken = wave_or_u32(top ? 1u << R : 0u);
-      const bool ok = __popcll(__ballot(top)) == k && __popc(taken) == k;
-      if (ok && top) ls.se[R] = ci;
+    // lane l holds candidate (group l / k, rank l % k)
+    const int nc = kWpg * k;
+    const uint32_t h = lane < nc ? ls.chi[(lane / k) * 16 + lane % k] : 0u;
+    ci = lane < nc ? ls.cidx[(lane / k) * 16 + lane % k] : -1;
+    R = nc <= 32 ? count_larger<2>(h) : count_larger<4>(h);
+    const bool top = ci >= 0 && R < k;
+    const uint32_t taken = wave_or_u32(top ? 1u << R : 0u);
+    fast = __popcll(__ballot(top)) == k && __popc(taken) == k;  // the same in every wavefront
+    if (fast && slots) {
+      if (top) ls.se[wave][R] = ci;
       wave_lds_sync();
-      if (ok && lane < k) {
-        ej = ls.se[lane];
+      if (lane < k) {
+        ej = ls.se[wave][lane];
         kj = ls.key[ej];
       }
-      if (lane == 0) ls.ok = ok;
     }
-    __syncthreads();
-    fast = ls.ok;
   }
   if (!fast) {  // exact ranks of every expert against all E keys
     for (int e = tid; e < E; e += NT) {
       const uint64_t ke = ls.key[e];
-      int R = 0;
-      for (int f = 0; f < E; ++f) R += comes_before(ls.key[f], f, ke, e) ? 1 : 0;
-      if (R < k) {
-        ls.sk[R] = ke;
-        ls.se[R] = e;
+      int r = 0;
+      for (int f = 0; f < E; ++f) r += comes_before(ls.key[f], f, ke, e) ? 1 : 0;
+      if (r < k) {
+        ls.sk[r] = ke;
+        ls.sx[r] = e;
       }
     }
     __syncthreads();
-    if (wave == 0 && lane < k) {
+    if (lane < k) {
       kj = ls.sk[lane];
-      ej = ls.se[lane];
+      ej = ls.sx[lane];
     }
   }
+  return fast;
 }
 
 // ---- one token: routing inside the routed gate/up launch ----------------------
 // Every routed gate/up workgroup ranks the token itself from the partial
 // logits that the routing launch wrote (the same fp64 logits and order as
-// the routing leader would use, so every workgroup reaches the same slots),
-// and takes the expert of its union slot u: the kept slot whose expert has u
-// kept experts below it.  The routing launch therefore ends with its router
-// units: no arrival chain, no leader, no slot-table lookup before the weight
-// stream.  Workgroup 0 also writes the routing outputs, the union and the
-// slot table that the down launch reads.  Returns false when u is past the
-// union (slots dropped by top-p).
+// the routing leader would use, so every workgroup reaches the same slots)
+// and takes the expert of its slot j (pair j of the token; the order of the
+// gate/up work does not matter, the down launch reads the union).  The
+// routing launch therefore ends with its router units: no arrival chain, no
+// leader, no slot-table lookup before the weight stream.  Workgroup 0 also
+// writes the routing outputs, the union and the slot table that the down
+// launch reads.  Returns false for a slot dropped by top-p.
 struct RouteOneLds {
   TopkLds tk;
-  int e, j;
 };
 
-__device__ __forceinline__ bool route_one(const DecArgs& a, int u, bool writer, SlotInfo& si, RouteOneLds& ls) {
+__device__ __forceinline__ bool route_one(const DecArgs& a, int j, bool writer, SlotInfo& si, RouteOneLds& ls) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   // the ranking shares its SIMDs with the shared expert's streaming
   // wavefronts: it goes first while it runs
   __builtin_amdgcn_s_setprio(3);
+  const bool out = writer && wave == 0;
+  // slots in lane order are needed for the weights: where they are written,
+  // or where they decide which slots top-p keeps
+  const bool need_w = out || a.top_p_on;
+  int R = 0, ci = -1, ej = -1;
   uint64_t kj = 0;
-  int ej = -1;
-  topk_parallel(a, ls.tk, kj, ej);
-  if (wave == 0) {
-    // slot j in lane j; the weights are formed only where they are written
-    // or decide which slots top-p keeps
-    const bool need_w = writer || a.top_p_on;
+  const bool fast = topk_parallel(a, ls.tk, need_w, R, ci, kj, ej);
+  int e_j;  // slot j's expert, or -1 when top-p drops it
+  if (fast && !need_w) {
+    const uint64_t hit = __ballot(ci >= 0 && R == j);
+    e_j = __builtin_amdgcn_readlane(ci, __ffsll((unsigned long long)hit) - 1);
+  } else {
     const SlotWeight sw = need_w ? slot_weights(from_order_key(kj), a.k, a.top_p) : SlotWeight{a.k, 0.0f};
     const int e = lane < sw.m ? ej : -1;  // kept slots
-    if (writer && lane < a.k) {
-      a.topk_idx[lane] = e;
-      a.topk_w[lane] = sw.w;
-    }
-    int r = 0;  // kept experts below e
-    for (int j = 0; j < a.k; ++j) {
-      const int ej2 = __builtin_amdgcn_readlane(e, j);
-      r += (ej2 >= 0 && ej2 < e) ? 1 : 0;
-    }
-    const uint64_t hit = __ballot(e >= 0 && r == u);
-    const int l = hit ? __ffsll((unsigned long long)hit) - 1 : 0;
-    if (lane == 0) {
-      ls.e = hit ? __builtin_amdgcn_readlane(e, l) : -1;
-      ls.j = l;
-    }
-    if (writer) {  // the union of one token (as union_one) and the slot table
+    e_j = __builtin_amdgcn_readlane(e, j);
+    if (out) {  // the routing outputs, the union of one token (as union_one) and the slot table
+      int r = 0;  // kept experts below e
+      for (int jj = 0; jj < a.k; ++jj) {
+        const int e2 = __builtin_amdgcn_readlane(e, jj);
+        r += (e2 >= 0 && e2 < e) ? 1 : 0;
+      }
       const int nu = __popcll(__ballot(e >= 0));
+      if (lane < a.k) {
+        a.topk_idx[lane] = e;
+        a.topk_w[lane] = sw.w;
+      }
       if (e >= 0) {
         a.uniq_ids[r] = e;
         a.uniq_off[r] = r;
@@ -813,14 +822,12 @@ __device__ __forceinline__ bool route_one(const DecArgs& a, int u, bool writer, 
       for (int sl = a.S + nu + lane; sl < a.slots_max; sl += 64) a.slots[sl].n = 0;
     }
   }
-  __syncthreads();
   __builtin_amdgcn_s_setprio(0);
-  const int e = ls.e;
-  if (e < 0) return false;
-  si.base = ls.tk.ep[e];
+  if (e_j < 0) return false;  // the same in every wavefront
+  si.base = ls.tk.ep[e_j];
   si.n = 1;
   si.p0 = -1;  // unused: the pair is known
-  si.pair = ls.j;
+  si.pair = j;
   return true;
 }
 
@@ -1172,6 +1179,8 @@ __global__ __launch_bounds__(64 * kWpg) void k_gu_phase(DecArgs a, const uint16_
     get_slot(a, 0, si);
   } else {
     nw = min(kWpg, a.ks_gu), ngrp = a.ks_gu / nw;
+    // slot u: the union's u-th expert, or with gu_routes the token's u-th
+    // ranked slot
     const int per_slot = (a.I / 64) * ngrp, u = b / per_slot;
     r = b % per_slot, s = a.S + u, nch = a.cpu_gu, tile = 0, ntiles = 1;
     if (a.gu_routes) {
