@@ -293,8 +293,17 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int K = (NM == 2) ? a.H : a.I;
   const int R = (NM == 2) ? a.I : a.H;  // rows per matrix
-  const int rb = ngrp * NW + wave;
+  // A tile with one filled 16-token group does little matrix work per
+  // slice: each wavefront then takes two row blocks (rb, rb + 1), so a
+  // slice moves twice the weights against the same activation staging and
+  // barrier, and the tile needs half of its row groups (the others exit).
+  // (the down GEMM only: the gate/up loop, with two matrices per block,
+  // measured slower in pairs)
+  const bool pair = NM == 1 && min(se.n - m0, BT) <= 16;
+  if (pair && 2 * ngrp * NW * 64 >= R) return;  // uniform over the workgroup
+  const int rb = pair ? 2 * (ngrp * NW + wave) : ngrp * NW + wave;
   const bool active = rb * 64 < R;
+  const bool active1 = pair && (rb + 1) * 64 < R;  // the second block of a pair
   if (tid < BT) {
     int ar = -1, orow = -1;
     const bool ok = tile_token(a, se, m0 + tid, ar, orow);
@@ -333,12 +342,17 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
     wsrc = (const guint4*)(se.base + a.L.d_off) + (size_t)rb * nch * WPS * 64 + lane;
     if (FMT == MOE_W_E2M1_B16) ssrc = se.base + a.L.sdd_off + ((size_t)rb * (K / 128) * 64 + lane) * 8;
   }
-  auto load_w = [&](int c, int m, int p) -> u32x4 {
-    return __builtin_nontemporal_load(wsrc + ((size_t)(c * WPS + p) * NM + m) * 64);
+  // the pair's second block (a block past the matrix re-reads the first; its
+  // results are not stored)
+  const size_t rb_step = active1 ? 1 : 0;
+  const guint4* wsrc1 = wsrc + rb_step * nch * WPS * NM * 64;
+  const uint8_t* ssrc1 = FMT == MOE_W_E2M1_B16 ? ssrc + rb_step * (K / 128) * NM * 64 * 8 : nullptr;
+  auto load_w = [&](int c, int m, int p, int b) -> u32x4 {
+    return __builtin_nontemporal_load((b ? wsrc1 : wsrc) + ((size_t)(c * WPS + p) * NM + m) * 64);
   };
-  auto load_s = [&](int c, int m) -> uint32_t {  // the two scale bytes of the slice, one 16-bit global load
+  auto load_s = [&](int c, int m, int b) -> uint32_t {  // the two scale bytes of the slice, one 16-bit global load
     typedef __attribute__((address_space(1))) const uint16_t gu16;
-    return *(gu16*)(ssrc + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3));
+    return *(gu16*)((b ? ssrc1 : ssrc) + ((size_t)(c / 4) * NM + m) * 64 * 8 + 2 * (c & 3));
   };
 
   f32x4 acc[NM][4][GMAX];  // [matrix][row group q][token group mt]
@@ -349,8 +363,8 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
 #pragma unroll
       for (int mt = 0; mt < GMAX; ++mt) acc[m][q][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 ring[DEPTH][NM][WPS];
-  uint32_t sring[DEPTH][NM];
+  u32x4 ring[DEPTH][NM][WPS], ring1[DEPTH][NM][WPS];  // ring1: the pair's second block
+  uint32_t sring[DEPTH][NM], sring1[DEPTH][NM];
   P xring[XR];
   half8_t av[GMAX], av1[GMAX];  // A operands of K-steps 0 and 1 (int2)
   const int n = lane & 15, g = lane >> 4;
@@ -360,8 +374,10 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
   };
   // The loop body is straight-line code (loads past the last slice re-read
   // it and go unused), so that the load counters stay exact across slices.
-  auto run = [&](auto ACTIVE, auto MTC) {
+  auto run = [&](auto ACTIVE, auto MTC, auto PAIRC) {
     constexpr int MT = decltype(MTC)::value;  // 16-token groups of the tile that hold tokens
+    constexpr bool PR = decltype(PAIRC)::value;  // two row blocks (MT == 1; second in acc[.][.][1])
+    static_assert(!PR || MT == 1, "pairs of row blocks for one-group tiles");
     // slice c+1's A operands are read during slice c, except where they
     // would not fit beside the accumulators (int2: two K-steps per slice;
     // more than 4 token groups)
@@ -379,8 +395,13 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
         for (int m = 0; m < NM; ++m) {
           const int cj = j < nch ? j : nch - 1;
 #pragma unroll
-          for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cj, m, p);
-          sring[j][m] = FMT == MOE_W_E2M1_B16 ? load_s(cj, m) : 0u;
+          for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cj, m, p, 0);
+          sring[j][m] = FMT == MOE_W_E2M1_B16 ? load_s(cj, m, 0) : 0u;
+          if (PR) {
+#pragma unroll
+            for (int p = 0; p < WPS; ++p) ring1[j][m][p] = load_w(cj, m, p, 1);
+            sring1[j][m] = FMT == MOE_W_E2M1_B16 ? load_s(cj, m, 1) : 0u;
+          }
         }
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -411,15 +432,23 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
           const int cn = c + DEPTH < nch ? c + DEPTH : nch - 1;
           // transpose every matrix (which ends the slot's registers), refill
           // the slot, then multiply
-          RawBlock rw[NM];
+          RawBlock rw[NM], rw1[NM];
 #pragma unroll
-          for (int m = 0; m < NM; ++m) rw[m] = to_raw<FMT>(ring[j][m], sring[j][m]);
+          for (int m = 0; m < NM; ++m) {
+            rw[m] = to_raw<FMT>(ring[j][m], sring[j][m]);
+            if (PR) rw1[m] = to_raw<FMT>(ring1[j][m], sring1[j][m]);
+          }
           __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
           for (int m = 0; m < NM; ++m) {
 #pragma unroll
-            for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cn, m, p);
-            if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(cn, m);
+            for (int p = 0; p < WPS; ++p) ring[j][m][p] = load_w(cn, m, p, 0);
+            if (FMT == MOE_W_E2M1_B16) sring[j][m] = load_s(cn, m, 0);
+            if (PR) {
+#pragma unroll
+              for (int p = 0; p < WPS; ++p) ring1[j][m][p] = load_w(cn, m, p, 1);
+              if (FMT == MOE_W_E2M1_B16) sring1[j][m] = load_s(cn, m, 1);
+            }
           }
           // the loads above issue before the matrix work below
           __builtin_amdgcn_sched_barrier(0);
@@ -434,6 +463,10 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
                 for (int mt = 0; mt < MT; ++mt)
                   acc[m][q][mt] =
                       __builtin_amdgcn_mfma_f32_16x16x32_f16(st ? av1[mt] : av[mt], b, acc[m][q][mt], 0, 0, 0);
+                if (PR) {
+                  const half8_t b1 = b_operand<FMT>(rw1[m], q, st);
+                  acc[m][q][1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(st ? av1[0] : av[0], b1, acc[m][q][1], 0, 0, 0);
+                }
               }
           // the barrier below stays after the matrix work
           __builtin_amdgcn_sched_barrier(0);
@@ -453,21 +486,24 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
   // tile skips the matrix work of its empty groups (their accumulators stay
   // zero; the epilogue skips padding tokens)
   typedef std::true_type on;
+  typedef std::false_type off;
   const int ng = (min(se.n - m0, BT) + 15) >> 4;
   if (!active)
-    run(std::false_type{}, std::integral_constant<int, 1>{});
+    run(off{}, std::integral_constant<int, 1>{}, off{});
+  else if (NM == 1 && pair)
+    run(on{}, std::integral_constant<int, 1>{}, std::integral_constant<bool, NM == 1>{});
   else if (ng <= 1)
-    run(on{}, std::integral_constant<int, 1>{});
+    run(on{}, std::integral_constant<int, 1>{}, off{});
   else if (ng == 2)
-    run(on{}, std::integral_constant<int, 2>{});
+    run(on{}, std::integral_constant<int, 2>{}, off{});
   else if (ng == 3)
-    run(on{}, std::integral_constant<int, 3>{});
+    run(on{}, std::integral_constant<int, 3>{}, off{});
   else if (GMAX == 4 || ng == 4)
-    run(on{}, std::integral_constant<int, 4>{});
+    run(on{}, std::integral_constant<int, 4>{}, off{});
   else if (ng <= 6)
-    run(on{}, std::integral_constant<int, GMAX == 8 ? 6 : 4>{});
+    run(on{}, std::integral_constant<int, GMAX == 8 ? 6 : 4>{}, off{});
   else
-    run(on{}, std::integral_constant<int, GMAX>{});
+    run(on{}, std::integral_constant<int, GMAX>{}, off{});
   if (SL::SUB) {  // per-token activation sums: the PPR pieces of a token sit in adjacent lanes
     float s = xsum;
 #pragma unroll
@@ -477,58 +513,66 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
   }
   if (!active) return;
   // epilogue: lane (n, g) holds tokens 16 mt + 4 g + i of row 64 rb + 16 q + n
+  // in acc[.][q][mt]; the second block of a pair holds its token group 0 in
+  // acc[.][q][1]
   constexpr float kSub = 16777216.0f;  // 2^24
   const int gn = (min(se.n - m0, BT) + 15) >> 4;  // token groups that can hold tokens
+  auto epilogue = [&](int rbx, auto ABC) {
+    constexpr int AB = decltype(ABC)::value;     // accumulator index of token group 0
+    constexpr int NG = AB ? 1 : GMAX;            // token groups held
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int row = rb * 64 + 16 * q + n;
-    if (NM == 2) {
-      float sgv, suv;
-      if (row_scaled(FMT)) {
-        sgv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sg_off)[row]);
-        suv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.su_off)[row]);
-      } else {
-        const float* g3 = reinterpret_cast<const float*>(se.base + a.L.g3_off);
-        sgv = g3[0];
-        suv = g3[1];
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int row = rbx * 64 + 16 * q + n;
+      if (NM == 2) {
+        float sgv, suv;
+        if (row_scaled(FMT)) {
+          sgv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sg_off)[row]);
+          suv = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.su_off)[row]);
+        } else {
+          const float* g3 = reinterpret_cast<const float*>(se.base + a.L.g3_off);
+          sgv = g3[0];
+          suv = g3[1];
+        }
 #pragma unroll
-      for (int mt = 0; mt < GMAX; ++mt)
+        for (int mt = 0; mt < NG; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int mm = 16 * mt + 4 * g + i;
-          if (mt >= gn) continue;
-          const int orow = s_out[mm];
-          if (orow < 0) continue;
-          float ga = acc[0][q][mt][i], ua = acc[NM - 1][q][mt][i];
-          if (SL::SUB) {
-            const float off = SL::OFF * s_sum[mm];
-            ga = ga * kSub - off;
-            ua = ua * kSub - off;
+          for (int i = 0; i < 4; ++i) {
+            const int mm = 16 * mt + 4 * g + i;
+            if (mt >= gn) continue;
+            const int orow = s_out[mm];
+            if (orow < 0) continue;
+            float ga = acc[0][q][AB + mt][i], ua = acc[NM - 1][q][AB + mt][i];
+            if (SL::SUB) {
+              const float off = SL::OFF * s_sum[mm];
+              ga = ga * kSub - off;
+              ua = ua * kSub - off;
+            }
+            const float gv = ga * sgv, uv = ua * suv;
+            a.h[(size_t)orow * a.I + row] = __builtin_bit_cast(uint16_t, (_Float16)(silu(gv) * uv));
           }
-          const float gv = ga * sgv, uv = ua * suv;
-          a.h[(size_t)orow * a.I + row] = __builtin_bit_cast(uint16_t, (_Float16)(silu(gv) * uv));
-        }
-    } else {
-      float sd;
-      if (row_scaled(FMT))
-        sd = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sd_off)[row]);
-      else
-        sd = reinterpret_cast<const float*>(se.base + a.L.g3_off)[2];
+      } else {
+        float sd;
+        if (row_scaled(FMT))
+          sd = (float)__builtin_bit_cast(_Float16, reinterpret_cast<const uint16_t*>(se.base + a.L.sd_off)[row]);
+        else
+          sd = reinterpret_cast<const float*>(se.base + a.L.g3_off)[2];
 #pragma unroll
-      for (int mt = 0; mt < GMAX; ++mt)
+        for (int mt = 0; mt < NG; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int mm = 16 * mt + 4 * g + i;
-          if (mt >= gn) continue;
-          const int orow = s_out[mm];
-          if (orow < 0) continue;
-          float da = acc[0][q][mt][i];
-          if (SL::SUB) da = da * kSub - SL::OFF * s_sum[mm];
-          a.part[(size_t)orow * a.H + row] = s_w[mm] * (sd * da);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int mm = 16 * mt + 4 * g + i;
+            if (mt >= gn) continue;
+            const int orow = s_out[mm];
+            if (orow < 0) continue;
+            float da = acc[0][q][AB + mt][i];
+            if (SL::SUB) da = da * kSub - SL::OFF * s_sum[mm];
+            a.part[(size_t)orow * a.H + row] = s_w[mm] * (sd * da);
+          }
+      }
     }
-  }
+  };
+  epilogue(rb, std::integral_constant<int, 0>{});
+  if (active1) epilogue(rb + 1, std::integral_constant<int, 1>{});
 }
 
 // y[t][c] = sum_j part[t*k + j][c] (slot order) + part[T*k + t][c].  A
