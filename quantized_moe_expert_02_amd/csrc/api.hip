@@ -34,7 +34,10 @@ int shared_split(int K) {
 
 // Split of the routed experts' gate/up: four K-segments per workgroup, and
 // more groups of four (partials handed to the last group) while the launch
-// would hold fewer than kGuTargetWaves wavefronts for `slots` experts.
+// would hold fewer than kGuTargetWaves wavefronts for `slots` experts.  The
+// split fixes the order of a token's sums, so it is taken for one token's
+// slots at every batch size: a token's output bits do not depend on the
+// batch it comes in.
 constexpr int kGuTargetWaves = 1024;
 int routed_split(int K, int I, int slots) {
   const int g = K / 128;
@@ -75,7 +78,7 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.slots_max = q.S + (int)std::min<int64_t>(q.E, (int64_t)T * q.k);
   q.rows_total = T * q.k + T;
   // decode K-splits: one wavefront per K-segment, four per workgroup
-  q.ks_gu = routed_split(q.H, q.I, (int)std::min<int64_t>(q.E, (int64_t)T * q.k));  // routed experts
+  q.ks_gu = routed_split(q.H, q.I, std::min(q.E, q.k));  // routed experts
   q.ks_sgu = shared_split(q.H);    // shared expert, streamed while routing
   q.ks_dn = split_factor(q.I, 2);  // 2 K-segments x 2 row blocks per workgroup
   // Counters: the first 256 words for route-stage counters, then one per

@@ -264,6 +264,36 @@ def test_forward_deterministic_and_batch_invariant():
         assert torch.equal(yt[0], y1[t]), t
 
 
+# A token's output bits do not depend on its batch: one token alone (ranked
+# inside the gate/up launch) against the same token in a batch of six, whose
+# union holds more slots.  The gate/up K-split is taken for one token's slots
+# at every batch size (e2m1_s0 would take a narrower one for the batch
+# otherwise).  I = 384 has one down K-segment, k = 32 the most slots.
+ONE_TOKEN_BITWISE = [
+    ("int4_i384", synth.Dims(1024, 384, 32, 8, 1, synth.INT4_ROW)),
+    ("e2m1_s0", synth.Dims(1024, 512, 32, 6, 0, synth.E2M1_B16)),
+    ("int8_topp", synth.Dims(512, 1024, 16, 4, 1, synth.INT8_ROW, top_p=0.6)),
+    ("int2_k12", synth.Dims(512, 768, 64, 12, 1, synth.INT2_ROW)),
+    ("int4_e1000_k32", synth.Dims(512, 256, 1000, 32, 1, synth.INT4_ROW)),
+]
+
+
+@pytest.mark.parametrize("name,dims", ONE_TOKEN_BITWISE)
+def test_one_token_equals_batched_bitwise(name, dims):
+    _log("one token vs batched", name, dims)
+    layer = synth.make_layer(dims, ("bw1", name))
+    x = synth.make_tokens(dims, 6, ("bw1", name)).to(DEV)
+    pl = moe.PackedLayer.from_layer(layer)
+    yb = moe.moe_w4a16_forward(pl, x)
+    for t in range(6):
+        y1 = moe.moe_w4a16_forward(pl, x[t:t + 1].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(y1[0], yb[t]), (name, t)
+    r = oracle_route(layer, x)
+    if min_topk_gap(r, dims.top_k) > 1e-9 and not dims.top_p:
+        assert_close(yb, oracle_y(layer, x), name)
+
+
 def test_forward_zero_input_and_empty_batch():
     layer, x = synth.workload("tiny")
     pl = moe.PackedLayer.from_layer(layer)
