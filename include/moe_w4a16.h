@@ -34,12 +34,19 @@
  *   - Validation happens before any launch; on failure the call returns a
  *     negative moe_status_t, launches nothing and leaves outputs untouched.
  *     No call prints or throws.
- *   - Inputs must be finite.  The same inputs give bitwise-identical outputs
- *     (no floating-point atomics; all reductions run in a fixed order).
+ *   - Inputs must be finite.  The same inputs give bitwise-identical outputs,
+ *     and a token's outputs do not depend on the batch it comes in (decode
+ *     batches, T <= 16): no floating-point atomics; reductions run in a
+ *     fixed order, and the decode path adds each slot's routing-weighted
+ *     down row into the output as an exact 64-bit fixed-point integer (29
+ *     fraction bits), which any arrival order sums alike.  A decode output
+ *     element to which some slot contributes 2^20 or more in magnitude is
+ *     +-inf (NaN where such terms have both signs).
  *   - All device pointers must be 16-byte aligned; packed experts 256-byte.
  *   - The workspace must be zero-filled once before its first use (e.g.
  *     allocated with torch.zeros).  Its first moe_workspace_sync_bytes(d)
- *     bytes hold completion counters that every call leaves at zero again,
+ *     bytes hold completion counters and the decode output accumulators,
+ *     which every call leaves at zero again,
  *     so a zeroed workspace stays valid for any later call and any T, but
  *     two calls that overlap in time must not share one workspace.
  */
@@ -211,7 +218,7 @@ int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, cons
  * small fill kernel on `stream`, then runs the layer.
  * Limit: a call with moe_workspace_bytes(d, T) > MOE_NOALLOC_SCRATCH_BYTES
  * returns MOE_E_WORKSPACE and launches nothing (the 6144 x 2048, 256-expert
- * top-8 int4 layer with a shared expert fits up to T = 121).
+ * top-8 int4 layer with a shared expert fits up to T = 118).
  * Every call on one GPU uses that GPU's single array: calls that overlap in
  * time on one GPU (several streams or host threads) race and give undefined
  * results; serialise them, e.g. on one stream.  Other errors as

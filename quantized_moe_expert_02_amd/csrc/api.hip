@@ -82,14 +82,15 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   q.ks_sgu = shared_split(q.H);    // shared expert, streamed while routing
   q.ks_dn = split_factor(q.I, 2);  // 2 K-segments x 2 row blocks per workgroup
   // Counters: the first 256 words for route-stage counters, then one per
-  // (slot, gate/up row block) for the largest decode batch, then one per
-  // down row block.
+  // (slot, gate/up row block) for the largest decode batch; then the decode
+  // output accumulators, one 64-bit word per output element of the largest
+  // decode batch.  All of it starts at zero and every call leaves it so.
   const int slots_decode = q.S + std::min(q.E, kDecodeMaxTokens * q.k);
   q.c_route = 0;
   q.c_gu = 256;
-  q.c_dn = q.c_gu + (size_t)slots_decode * (q.I / 64);
-  q.n_counters = q.c_dn + q.H / 64;
-  q.sync_bytes = up256(q.n_counters * 4);
+  q.n_counters = q.c_gu + (size_t)slots_decode * (q.I / 64);
+  q.acc_off = up256(q.n_counters * 4);
+  q.sync_bytes = up256(q.acc_off + (size_t)kDecodeMaxTokens * q.H * 8);
   size_t off = q.sync_bytes;
   const size_t Tk = (size_t)T * q.k;
   const size_t cap = std::max<size_t>(1, std::min<size_t>(q.E, Tk));
@@ -112,7 +113,7 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   if (q.decode) {
     const int groups = std::max(q.ks_sgu > 4 ? q.ks_sgu / 4 : 1, q.ks_gu > 4 ? q.ks_gu / 4 : 1);
     q.p_gu_off = off; off = up256(off + (size_t)groups * q.rows_total * 2 * q.I * 4);
-    q.p_dn_off = off; off = up256(off + (size_t)q.rows_total * q.H * 4);
+    q.p_dn_off = 0;  // the down partials go straight into the output accumulators
   } else {
     q.p_gu_off = 0;
     q.p_dn_off = off; off = up256(off + (size_t)q.rows_total * q.H * 4);

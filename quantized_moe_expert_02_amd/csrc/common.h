@@ -101,7 +101,8 @@ struct Plan {
   int ks_gu, ks_sgu, ks_dn;  // split-K factors of the GEMV path (routed / shared gate/up, down)
   bool decode;               // GEMV path
   // counters (uint32), offsets in elements from ws base
-  size_t c_route, c_gu, c_dn, n_counters;
+  size_t c_route, c_gu, n_counters;
+  size_t acc_off;            // byte offset of the decode output accumulators (uint64, in the sync region)
   size_t sync_bytes;
   // byte offsets
   size_t z_off, idx_off, w_off, nu_off, ids_off, off_off, pairs_off;

@@ -268,9 +268,10 @@ __device__ __forceinline__ void stream_ring(const guint4* __restrict__ w, const 
 //                  wavefronts stream the K-segments, reduce through LDS in a
 //                  fixed order and form h (row scales, SwiGLU)
 //   k_dn_phase     one workgroup per (slot, 64-row output block): K-segments
-//                  reduced through LDS into the slot's scaled partial; the
-//                  last slot of a row block combines all slots in a fixed
-//                  order (routing-weighted, shared expert last) into y
+//                  reduced through LDS into the slot's scaled row, which is
+//                  added, routing-weighted, to the token's output row as an
+//                  exact fixed-point sum; the slot that completes a row
+//                  writes it to y
 // "Last" is decided by device-scope arrival counters, which that unit
 // returns to zero, so every call starts from zeroed counters.  Data handed
 // to another workgroup of the same launch is written with device-coherent
@@ -308,10 +309,9 @@ struct DecArgs {
   SlotEntry* slots;
   uint16_t* h;
   float* p_gu;        // one partial plane per group of K-segments (shared and routed rows)
-  float* p_dn;        // [rows_total][H] scaled slot partials
+  uint64_t* y_acc;    // [T][H] output accumulators (fixed point + arrivals), zero between calls
   uint32_t* sync;
   uint32_t* gu_cnt;   // [slot][I/64] arrivals of K-segment groups
-  uint32_t* dn_cnt;   // [H/64]
   int ks_gu, ks_sgu, ks_dn;     // K-segments: routed gate/up, shared gate/up, down
   int cpu_gu, cpu_sgu, cpu_dn;  // chunks per K-segment
   int slots_max, rows_total;
@@ -1011,6 +1011,51 @@ __device__ __forceinline__ void gu_group(const DecArgs& a, const uint16_t* __res
 // memory counter retires in order), so each step of kStageCols columns
 // requests its first weight batches, then stages h while those are in
 // flight, then streams.
+// ---- output combine -----------------------------------------------------------
+// Every (token, slot) pair adds its routing-weighted down row w*o to the
+// token's output row in one 64-bit atomic add per element, as a fixed-point
+// integer (29 fraction bits, rounded to nearest) together with one arrival:
+//   bits  0..55  the sum, two's complement (|sum| < 2^55)
+//   bits 56..61  arrivals (at most kMaxTopK + 1)
+//   bits 62, 63  a term reached +kFixLimit / -kFixLimit (both: not a number)
+// Integer sums are exact and order-free, so the output does not depend on
+// which slot arrives when (deterministic and batch-invariant), and the one
+// round trip that adds a term also tells its lane whether the row is
+// complete: that lane converts the sum to binary16, writes y and returns the
+// word to zero.  Each term is held to 2^-30 absolute, below a quarter of the
+// smallest binary16 step (2^-24), for any output size.
+constexpr double kFixLimit = 1048576.0;  // 2^20: 33 terms of 2^49 units stay below 2^55
+constexpr uint64_t kArrival = 1ull << 56;
+
+__device__ __forceinline__ void combine_add(const DecArgs& a, int tok, int r, float w, float o, uint32_t target) {
+  uint64_t* cell = a.y_acc + (size_t)tok * a.H + r;
+  const double t = (double)w * (double)o;  // exact
+  uint64_t add = kArrival;
+  if (__builtin_fabs(t) < kFixLimit) {
+    const double q = __builtin_rint(t * 0x1p29);  // |q| < 2^49
+    const double hi = __builtin_floor(q * 0x1p-32);
+    add += ((uint64_t)(int64_t)(int32_t)hi << 32) | (uint64_t)(uint32_t)(q - hi * 0x1p32);
+  } else {  // out of range, or not a number: flag it before the arrival that may complete the row
+    const uint64_t flag = t >= kFixLimit ? 1ull << 62 : t <= -kFixLimit ? 1ull << 63 : 3ull << 62;
+    __hip_atomic_fetch_or(cell, flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  }
+  const uint64_t tot = __hip_atomic_fetch_add(cell, add, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + add;
+  const uint64_t low = tot & ((1ull << 62) - 1);
+  const uint32_t n = (uint32_t)((low + (1ull << 55)) >> 56);
+  if (n != target) return;
+  float yv;
+  const uint32_t f = (uint32_t)(tot >> 62);
+  if (f == 0)
+    yv = (float)((double)(int64_t)(low - ((uint64_t)n << 56)) * 0x1p-29);
+  else
+    yv = f == 1 ? __builtin_inff() : f == 2 ? -__builtin_inff() : __builtin_nanf("");
+  a.y[(size_t)tok * a.H + r] = __builtin_bit_cast(uint16_t, (_Float16)yv);
+  __hip_atomic_store(cell, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <int KT>
 struct DnLds {
   u32x4 h[kWpg][KT * kStageVec];  // per wavefront: KT tokens x kStageCols binary16
@@ -1022,6 +1067,26 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
                                         DnLds<KT>& ls) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const bool active = rb < a.H / 64;  // the last workgroup of a slot may overhang
+  // the combine's tokens, routing weights and arrival counts, looked up
+  // before the stream
+  int tk[NT];
+  float wt[NT];
+  uint32_t target[NT];
+  if (active && seg == 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      int tok, row;
+      slot_token(a, si, i0 + t, tok, row);
+      tk[t] = tok;
+      wt[t] = row < a.T * a.k ? ld_const(a.topk_w, row) : 1.f;
+      uint32_t kept = a.k;
+      if (a.top_p_on) {
+        kept = 0;
+        for (int j = 0; j < a.k; ++j) kept += ld_const(a.topk_idx, tok * a.k + j) >= 0 ? 1 : 0;
+      }
+      target[t] = (uint32_t)a.S + kept;
+    }
+  }
   if (active) {
     const int c0 = seg * a.cpu_dn;
     constexpr int C = Fmt<FMT>::C, XPC = Fmt<FMT>::XPC, kStage = kStageCols / C;
@@ -1068,9 +1133,7 @@ __device__ __forceinline__ void dn_tile(const DecArgs& a, const SlotInfo& si, in
     for (int t = 0; t < NT; ++t) {
       float v = 0.f;
       for (int q = 0; q < a.ks_dn; ++q) v += ls.r[wave + q][t][lane];
-      int tok, row;
-      slot_token(a, si, i0 + t, tok, row);
-      st_dev(a.p_dn + (size_t)row * a.H + 64 * rb + lane, v * scale);
+      combine_add(a, tk[t], 64 * rb + lane, wt[t], v * scale, target[t]);
     }
   }
   __syncthreads();  // LDS is reused by the next tile
@@ -1093,32 +1156,6 @@ __device__ __forceinline__ void dn_unit(const DecArgs& a, int s, int rbg, DnLds<
   for (int i0 = 0; i0 < si.n; i0 += KT) {
     if (KT == 1 || si.n - i0 == 1) dn_tile<FMT, 1, KT>(a, si, rb, seg, i0, scale, ls);
     else dn_tile<FMT, KT, KT>(a, si, rb, seg, i0, scale, ls);
-  }
-  if (seg != 0 || rb >= a.H / 64) return;
-  const uint32_t nu = __builtin_amdgcn_readfirstlane(*a.n_unique);
-  if (!arrive_last(a.dn_cnt + rb, (uint32_t)a.S + nu)) return;
-  // last slot of this row block: y[t] = sum over the token's slots in slot
-  // order, routed ones times their routing weight, shared expert last
-  for (int t = 0; t < a.T; ++t) {
-    float acc = 0.f;
-    for (int j0 = 0; j0 < a.k + a.S; j0 += 8) {
-      // all loads first (independent); a slot dropped by top-p has no
-      // partial row, so its (unwritten) row is loaded but not used
-      float o[8], wj[8];
-      int ej[8];
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = j0 + jj;
-        const int row = (j < a.k) ? t * a.k + j : a.T * a.k + t;
-        o[jj] = (j < a.k + a.S) ? ld_dev(a.p_dn + (size_t)row * a.H + r) : 0.f;
-        ej[jj] = (j < a.k && a.top_p_on) ? a.topk_idx[t * a.k + j] : 0;
-        wj[jj] = (j < a.k) ? a.topk_w[t * a.k + j] : 1.f;
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-        if (j0 + jj < a.k + a.S && ej[jj] >= 0) acc += (j0 + jj < a.k) ? wj[jj] * o[jj] : o[jj];
-    }
-    a.y[(size_t)t * a.H + r] = __builtin_bit_cast(uint16_t, (_Float16)acc);
   }
 }
 
@@ -1242,10 +1279,9 @@ DecArgs dec_args(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, con
   a.slots = r.slots;
   a.h = (uint16_t*)((char*)ws + p.h_off);
   a.p_gu = (float*)((char*)ws + p.p_gu_off);
-  a.p_dn = (float*)((char*)ws + p.p_dn_off);
+  a.y_acc = (uint64_t*)((char*)ws + p.acc_off);
   a.sync = (uint32_t*)ws;
   a.gu_cnt = a.sync + p.c_gu;
-  a.dn_cnt = a.sync + p.c_dn;
   a.ks_gu = p.ks_gu;
   a.ks_sgu = p.ks_sgu;
   a.ks_dn = p.ks_dn;

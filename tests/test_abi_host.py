@@ -137,7 +137,7 @@ def test_noalloc_rejects_before_any_launch(L):
     w = moe.MoeWeights(4096, 8192, 4096, None)
     P = ctypes.c_void_p
     big = next(t for t in range(16, 1 << 14, 16) if moe.moe_workspace_bytes(d, t) > moe.MOE_NOALLOC_SCRATCH_BYTES)
-    assert moe.moe_workspace_bytes(d, 121) <= moe.MOE_NOALLOC_SCRATCH_BYTES < moe.moe_workspace_bytes(d, 122)
+    assert moe.moe_workspace_bytes(d, 118) <= moe.MOE_NOALLOC_SCRATCH_BYTES < moe.moe_workspace_bytes(d, 119)
     f = L.moe_w4a16_forward_noalloc
     assert f(ctypes.byref(d), ctypes.byref(w), P(16), big, P(16), None, None, None) == moe.MOE_E_WORKSPACE
     assert f(ctypes.byref(d), ctypes.byref(w), P(16), 0, P(16), None, None, None) == moe.MOE_OK

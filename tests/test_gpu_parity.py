@@ -294,6 +294,38 @@ def test_one_token_equals_batched_bitwise(name, dims):
         assert_close(yb, oracle_y(layer, x), name)
 
 
+def test_decode_output_beyond_binary16():
+    """One slot per output (k = 1, no shared expert) with down rows scaled so
+    that outputs run from inside the binary16 range up to 3.6e6: terms of
+    2^20 and more take the combine's out-of-range flag, terms between 65504
+    and 2^20 its fixed-point sum; both must round to the oracle's binary16
+    (infinities of the right sign).  The outputs inside the range are the
+    rows whose 256-term dot product cancels against a row scale near 65504,
+    so their binary32 sums carry absolute errors far above the usual
+    tolerance; they are checked in relative L2 at 1e-2."""
+    dims = synth.Dims(512, 256, 8, 1, 0, synth.INT4_ROW)
+    layer = synth.make_layer(dims, "sat")
+    layer.s_up = (layer.s_up.float() * 30).half()
+    layer.s_down = (layer.s_down.float() * 1e6).clamp(-65504, 65504).half()
+    pl = moe.PackedLayer.from_layer(layer)
+    ws = moe.workspace(dims, 3, DEV)
+    for T in (1, 3):
+        x = synth.make_tokens(dims, T, ("sat", T))
+        y_ref = oracle.forward(layer, x)
+        a = np.abs(y_ref)
+        assert (a >= 2 ** 20).sum() > 0 and ((a > 65536) & (a < 2 ** 20)).sum() > 0 and (a < 60000).sum() > 0
+        y = moe.moe_w4a16_forward(pl, x.to(DEV), ws=ws)
+        torch.cuda.synchronize()
+        g = y.float().cpu().double().numpy()
+        big = a > 65536  # binary16 rounds these to infinity
+        assert np.all(np.isinf(g[big])) and np.array_equal(np.sign(g[big]), np.sign(y_ref[big])), T
+        small = a < 60000
+        err = np.linalg.norm(g[small] - y_ref[small]) / np.linalg.norm(y_ref[small])
+        assert np.all(np.isfinite(g[small])) and err <= 1e-2, (T, err)
+    # the flagged accumulators were returned to zero like the others
+    assert torch.count_nonzero(ws[: moe.moe_workspace_sync_bytes(dims)]) == 0
+
+
 def test_forward_zero_input_and_empty_batch():
     layer, x = synth.workload("tiny")
     pl = moe.PackedLayer.from_layer(layer)
