@@ -598,6 +598,18 @@ def main():
             secondary.append(tiered_decode())
         except Exception as e:
             secondary.append({"workload": "tiered_decode_b1", "error": str(e)})
+    # achievable rates measured on the same box (library code, not this
+    # project's), beside the published peaks the rooflines use
+    try:
+        ref = reference_rates()
+        for rl in (roofline, roofline_prefill):
+            if rl:
+                # HBM: the elementwise copy's rate (read + write bytes), the
+                # fastest plain stream of the three
+                rl["frac_of_measured"] = rl["achieved"] / (ref["hbm_copy_gbps"] if rl["unit"] == "GB/s"
+                                                           else ref["fp16_gemm_tflops"])
+    except Exception as e:
+        ref = {"error": str(e)}
     out = {
         "metric": METRIC,
         "value": res["tokens_per_s"],
@@ -621,6 +633,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "roofline_prefill": roofline_prefill,
+        "measured_peaks": ref,
         "cpu_baseline_prefill": cpu_prefill,
         "secondary": secondary,
     }

@@ -80,7 +80,10 @@ bool make_plan(const moe_dims_t& d, int T, Plan* p) {
   // decode K-splits: one wavefront per K-segment, four per workgroup
   q.ks_gu = routed_split(q.H, q.I, std::min(q.E, q.k));  // routed experts
   q.ks_sgu = shared_split(q.H);    // shared expert, streamed while routing
-  q.ks_dn = split_factor(q.I, 2);  // 2 K-segments x 2 row blocks per workgroup
+  // down: 2 K-segments x 2 row blocks per workgroup; short rows (I <= 1024)
+  // take 4 K-segments x 1 row block, or their launch holds too few
+  // wavefronts (the segment count divides the 4 wavefronts of a workgroup)
+  q.ks_dn = (q.I <= 1024 && (q.I / 128) % 4 == 0) ? 4 : split_factor(q.I, 2);
   // Counters: the first 256 words for route-stage counters, then one per
   // (slot, gate/up row block) for the largest decode batch; then the decode
   // output accumulators, one 64-bit word per output element of the largest

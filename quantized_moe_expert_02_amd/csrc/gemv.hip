@@ -1291,9 +1291,10 @@ DecArgs dec_args(const moe_dims_t& d, const Plan& p, const moe_weights_t& w, con
   a.cpu_dn = (p.I / C) / p.ks_dn;
   a.slots_max = p.slots_max;
   a.rows_total = p.rows_total;
-  // router units: enough column segments that each needs one batch of loads
+  // router units: enough column segments that each needs one batch of loads,
+  // and at least two per expert (short rows: more units in flight)
   const int n4 = p.H / 4, per = 64 * kLogitsBatch;
-  a.rsplit = std::min(kMaxLogitParts, (n4 + per - 1) / per);
+  a.rsplit = std::min(kMaxLogitParts, std::max(2, (n4 + per - 1) / per));
   a.seg4 = (n4 + a.rsplit - 1) / a.rsplit;
   a.n_router = p.E * a.rsplit;
   a.n_router_wg = (a.n_router + kWpg - 1) / kWpg;
