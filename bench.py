@@ -2,9 +2,10 @@
 
 A step is one call of moe_w4a16_forward (route, union, experts, combine) on
 one batch.  Steps cycle over L independent layer instances (each with all
-E + 1 experts resident and its own router and input) captured in a HIP
-graph, so the touched weights per graph replay far exceed the 256 MB
-Infinity Cache and every step streams its experts from HBM.
+E + 1 experts resident and its own router and input) captured in one HIP
+graph by the library (moe_step_graph_create), so the touched weights per
+graph replay far exceed the 256 MB Infinity Cache and every step streams its
+experts from HBM.
 
 Prints one JSON line: the headline workload (decode, batch 1, 6144 x 2048,
 256 experts top-8 + shared, int4 per-row scales) with a roofline object for
@@ -120,40 +121,33 @@ class Chain:
 
 
 def time_chain(ch: Chain, steps: int, warmup: int):
+    """Replays of the L layer calls as one graph captured by the library
+    (moe_step_graph_create; every layer with its own input), timed with
+    events on the stream the graphs are launched on."""
     L = len(ch.layers)
-    graphs = []
     full, rem = divmod(steps, L)
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for l in range(L):  # eager warm-up of every layer before capture
-            ch.call(l)
-    torch.cuda.current_stream().wait_stream(s)
+    for l in range(L):  # eager warm-up of every layer before capture
+        ch.call(l)
     torch.cuda.synchronize()
-    g_full = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_full):
-        for l in range(L):
-            ch.call(l)
-    g_rem = None
-    if rem:
-        g_rem = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_rem):
-            for l in range(rem):
-                ch.call(l)
+    g_full = moe.StepGraph(ch.layers, ch.x, ch.y, ch.ws)
+    g_rem = moe.StepGraph(ch.layers[:rem], ch.x[:rem], ch.y[:rem], ch.ws) if rem else None
     for _ in range(max(1, -(-warmup // L))):
-        g_full.replay()
+        g_full.launch()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_wall = time.perf_counter()
     e0.record()
     for _ in range(full):
-        g_full.replay()
+        g_full.launch()
     if g_rem is not None:
-        g_rem.replay()
+        g_rem.launch()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
     ms = e0.elapsed_time(e1)
+    g_full.close()
+    if g_rem is not None:
+        g_rem.close()
     return ms, wall
 
 

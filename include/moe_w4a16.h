@@ -23,9 +23,10 @@
  *
  * Conventions for every entry point:
  *   - Pointers are DEVICE pointers unless marked (host).  The caller owns and
- *     allocates every buffer; the library never allocates or frees memory and
- *     keeps no global mutable state, so calls on different streams with
- *     different workspaces may run concurrently.
+ *     allocates every buffer; the library never allocates or frees memory
+ *     (except the graph handle of moe_step_graph_create) and keeps no global
+ *     mutable state, so calls on different streams with different workspaces
+ *     may run concurrently.
  *   - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *     Each call validates its arguments on the host, enqueues its kernels and
  *     returns; outputs are valid once the stream has synchronised.  No call
@@ -226,6 +227,40 @@ int moe_w4a16_forward_profiled(const moe_dims_t* d, const moe_weights_t* w, cons
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
 int moe_w4a16_forward_noalloc(const moe_dims_t* d, const moe_weights_t* w, const uint16_t* x, int32_t T,
                               uint16_t* y, int32_t* topk_idx_out, float* topk_w_out, void* stream);
+
+/* A decode step of several layers captured once as one HIP graph and then
+ * replayed, so that a step costs one graph launch instead of one host launch
+ * per kernel: the way the Ornith engine runs each decode step ("GTX 1070向け
+ * 35BパラメータMoEモデル推論エンジン公開", 648news.com, section "Pascal世代の
+ * 制約をCUDAグラフとカーネル最適化で克服").
+ * moe_step_graph_create records, for l = 0 .. n_layers-1 in order,
+ *   moe_w4a16_forward(d, &w[l], x[l], T, y[l], NULL, NULL, ws, ws_bytes, .)
+ * on a capture stream of its own (nothing else is recorded):
+ *   w: (host) array of n_layers weight structs; x, y: (host) arrays of
+ *   n_layers device pointers (binary16 [T][H] each).  The pointers and the
+ *   shape are fixed at creation; the data behind them is read and written at
+ *   every launch.  Passing x[l+1] == y[l] chains the layers (each consumes the
+ *   previous one's output); distinct buffers give independent layers.
+ *   All layers share the one workspace ws (the zero-fill rule above).
+ * Every layer's arguments are validated as moe_w4a16_forward validates them
+ * before anything touches the device; errors as there, plus MOE_E_INVAL for
+ * n_layers outside 1 .. MOE_STEP_GRAPH_MAX_LAYERS, T < 1, or a NULL array or
+ * out; MOE_E_HIP if the capture or the instantiation fails.  On success
+ * *out receives the handle; otherwise *out is untouched and nothing is kept.
+ * Creation is the one place where the library allocates: the handle and
+ * the HIP runtime's graph objects, freed by moe_step_graph_destroy.
+ * moe_step_graph_launch enqueues the whole step on `stream` (allocating
+ * nothing; MOE_E_INVAL for a NULL handle, MOE_E_HIP if the launch fails).
+ * Launches of one graph, or of graphs sharing a workspace, must not overlap
+ * in time (one stream serialises them).  moe_step_graph_destroy(NULL) is a
+ * no-op; the graph must not be in flight when it is destroyed. */
+#define MOE_STEP_GRAPH_MAX_LAYERS 4096
+typedef struct moe_step_graph_s* moe_step_graph_t;
+int moe_step_graph_create(const moe_dims_t* d, int32_t n_layers, const moe_weights_t* w,
+                          const uint16_t* const* x, int32_t T, uint16_t* const* y, void* ws,
+                          size_t ws_bytes, moe_step_graph_t* out);
+int moe_step_graph_launch(moe_step_graph_t g, void* stream);
+int moe_step_graph_destroy(moe_step_graph_t g);
 
 /* Largest T served by the GEMV path of moe_w4a16_forward. */
 int32_t moe_decode_max_tokens(void);

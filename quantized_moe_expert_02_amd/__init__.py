@@ -23,11 +23,12 @@ _CODE_BITS = {MOE_W_INT4_ROW: 4, MOE_W_E2M1_B16: 4, MOE_W_INT8_ROW: 8, MOE_W_INT
 
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
            "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_w4a16_forward_noalloc",
-           "moe_decode_max_tokens",
+           "moe_decode_max_tokens", "moe_step_graph_create", "moe_step_graph_launch", "moe_step_graph_destroy",
            "moe_status_string", "moe_tier_create", "moe_tier_destroy", "moe_tier_use", "moe_tier_prefetch",
            "moe_tier_slot", "moe_tier_stats", "moe_tier_sync")
 MOE_TIER_LRU, MOE_TIER_HOT = 0, 1
 MOE_NOALLOC_SCRATCH_BYTES = 32 << 20  # include/moe_w4a16.h
+MOE_STEP_GRAPH_MAX_LAYERS = 4096  # include/moe_w4a16.h
 
 
 class MoeDims(ctypes.Structure):
@@ -84,6 +85,12 @@ def lib():
         L.moe_w4a16_forward_noalloc.argtypes = [D, W, P, i32, P, P, P, P]
         L.moe_w4a16_forward_noalloc.restype = ctypes.c_int
         L.moe_decode_max_tokens.restype = i32
+        L.moe_step_graph_create.argtypes = [D, i32, W, P, i32, P, P, sz, ctypes.POINTER(P)]
+        L.moe_step_graph_create.restype = ctypes.c_int
+        L.moe_step_graph_launch.argtypes = [P, P]
+        L.moe_step_graph_launch.restype = ctypes.c_int
+        L.moe_step_graph_destroy.argtypes = [P]
+        L.moe_step_graph_destroy.restype = ctypes.c_int
         L.moe_tier_create.argtypes = [D, i32, P, P, i32, P, P, i32, ctypes.POINTER(P)]
         L.moe_tier_create.restype = ctypes.c_int
         L.moe_tier_destroy.argtypes = [P]
@@ -297,6 +304,50 @@ def moe_w4a16_forward_profiled(layer: PackedLayer, x: torch.Tensor, y: torch.Ten
     if rc != MOE_OK:
         raise MoeError(rc, "moe_w4a16_forward_profiled")
     return y
+
+
+class StepGraph:
+    """Several layer calls captured once as one HIP graph by the library
+    (moe_step_graph_create) and replayed with one launch.  Layer l reads
+    xs[l] and writes ys[l] (pass ys[l] as xs[l + 1] to chain the layers);
+    all layers share the workspace `ws`.  The tensors must stay alive, at the
+    same addresses, for the life of the graph."""
+
+    def __init__(self, layers, xs, ys, ws: Optional[torch.Tensor] = None):
+        if not (len(layers) == len(xs) == len(ys)) or not layers:
+            raise ValueError("one input and one output per layer")
+        d = _dims(layers[0].dims)
+        T = xs[0].shape[0]
+        if ws is None:
+            ws = workspace(d, T, xs[0].device)
+        self._keep = (list(layers), list(xs), list(ys), ws)
+        n = len(layers)
+        w = (MoeWeights * n)(*[pl.weights() for pl in layers])
+        xp = (ctypes.c_void_p * n)(*[x.data_ptr() for x in xs])
+        yp = (ctypes.c_void_p * n)(*[y.data_ptr() for y in ys])
+        h = ctypes.c_void_p()
+        rc = lib().moe_step_graph_create(ctypes.byref(d), n, w, xp, T, yp, _p(ws), ws.numel(), ctypes.byref(h))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_step_graph_create")
+        self._h = h
+
+    def launch(self, stream=None):
+        rc = lib().moe_step_graph_launch(self._h, _stream(stream))
+        if rc != MOE_OK:
+            raise MoeError(rc, "moe_step_graph_launch")
+
+    def close(self):
+        if getattr(self, "_h", None):
+            rc = lib().moe_step_graph_destroy(self._h)
+            self._h = None
+            if rc != MOE_OK:
+                raise MoeError(rc, "moe_step_graph_destroy")
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 # ---- tiered expert residency (include/moe_tier.h) ---------------------------

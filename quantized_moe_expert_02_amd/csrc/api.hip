@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <new>
 
 #include "common.h"
 
@@ -344,6 +345,64 @@ int moe_w4a16_forward_noalloc(const moe_dims_t* d, const moe_weights_t* w, const
                      (uint32_t*)ws, words);
   if (hipGetLastError() != hipSuccess) return MOE_E_HIP;
   return forward_launch(d, w, x, y, topk_idx_out, topk_w_out, ws, s, p, StageEvents{nullptr, 0});
+}
+
+// ---- a decode step of several layers as one HIP graph ----------------------
+struct moe_step_graph_s {
+  hipGraph_t graph;
+  hipGraphExec_t exec;
+  int32_t n_layers;
+};
+
+int moe_step_graph_create(const moe_dims_t* d, int32_t n_layers, const moe_weights_t* w,
+                          const uint16_t* const* x, int32_t T, uint16_t* const* y, void* ws, size_t ws_bytes,
+                          moe_step_graph_t* out) {
+  if (!out || !w || !x || !y) return MOE_E_INVAL;
+  if (n_layers < 1 || n_layers > MOE_STEP_GRAPH_MAX_LAYERS || T < 1) return MOE_E_INVAL;
+  // every layer validated before anything touches the device
+  Plan p;
+  for (int l = 0; l < n_layers; ++l) {
+    const int st = forward_check(d, &w[l], x[l], T, y[l], nullptr, nullptr, ws, ws_bytes, &p);
+    if (st != MOE_OK) return st;
+  }
+  // captured on a stream of the library's own (default priority), so that
+  // nothing else the caller enqueues lands in the graph
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) return MOE_E_HIP;
+  int st = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) == hipSuccess ? MOE_OK : MOE_E_HIP;
+  const bool capturing = st == MOE_OK;
+  for (int l = 0; st == MOE_OK && l < n_layers; ++l)
+    st = forward_launch(d, &w[l], x[l], y[l], nullptr, nullptr, ws, s, p, StageEvents{nullptr, 0});
+  hipGraph_t g = nullptr;
+  if (capturing && hipStreamEndCapture(s, &g) != hipSuccess) st = MOE_E_HIP;
+  hipGraphExec_t ge = nullptr;
+  if (st == MOE_OK && hipGraphInstantiate(&ge, g, nullptr, nullptr, 0) != hipSuccess) st = MOE_E_HIP;
+  moe_step_graph_s* h = nullptr;
+  if (st == MOE_OK) {
+    h = new (std::nothrow) moe_step_graph_s{g, ge, n_layers};
+    if (!h) st = MOE_E_HIP;
+  }
+  (void)hipStreamDestroy(s);
+  if (st != MOE_OK) {
+    if (ge) (void)hipGraphExecDestroy(ge);
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipGetLastError();  // the failure is reported through the status
+    return st;
+  }
+  *out = h;
+  return MOE_OK;
+}
+
+int moe_step_graph_launch(moe_step_graph_t g, void* stream) {
+  if (!g) return MOE_E_INVAL;
+  return hipGraphLaunch(g->exec, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_E_HIP;
+}
+
+int moe_step_graph_destroy(moe_step_graph_t g) {
+  if (!g) return MOE_OK;
+  const bool ok = hipGraphExecDestroy(g->exec) == hipSuccess && hipGraphDestroy(g->graph) == hipSuccess;
+  delete g;
+  return ok ? MOE_OK : MOE_E_HIP;
 }
 
 const char* moe_status_string(int status) {

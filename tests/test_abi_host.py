@@ -146,3 +146,36 @@ def test_noalloc_rejects_before_any_launch(L):
     assert f(ctypes.byref(d), ctypes.byref(w), P(16), 4, P(24), None, None, None) == moe.MOE_E_INVAL
     bad = moe.MoeDims(100, 2048, 256, 8, 1, 0)
     assert f(ctypes.byref(bad), ctypes.byref(w), P(16), 4, P(16), None, None, None) == moe.MOE_E_UNSUPPORTED
+
+
+def test_step_graph_rejects_before_any_launch(L):
+    """moe_step_graph_create validates every layer like moe_w4a16_forward,
+    and its own arguments, before it touches the device; *out stays
+    untouched on failure; destroy(NULL) is a no-op and launch(NULL) an
+    error."""
+    d = moe.MoeDims(256, 128, 8, 2, 1, 0)
+    P = ctypes.c_void_p
+    good = moe.MoeWeights(4096, 8192, 4096, None)
+    ws_b = moe.moe_workspace_bytes(d, 4)
+
+    def create(n=2, T=4, w=None, x=None, y=None, ws=P(16), wsb=ws_b, dims=d, out=True):
+        ws_arr = (moe.MoeWeights * max(n, 1))(*([w or good] * max(n, 1)))
+        xa = (P * max(n, 1))(*(x or [P(1 << 20)] * max(n, 1)))
+        ya = (P * max(n, 1))(*(y or [P(2 << 20)] * max(n, 1)))
+        h = P(12345)
+        rc = L.moe_step_graph_create(ctypes.byref(dims), n, ws_arr, xa, T, ya, ws, wsb,
+                                     ctypes.byref(h) if out else None)
+        assert h.value == 12345  # untouched on every failure below
+        return rc
+
+    assert create(out=False) == moe.MOE_E_INVAL
+    assert create(n=0) == moe.MOE_E_INVAL
+    assert create(n=moe.MOE_STEP_GRAPH_MAX_LAYERS + 1) == moe.MOE_E_INVAL
+    assert create(T=0) == moe.MOE_E_INVAL
+    assert create(x=[P(1 << 20), P(0)]) == moe.MOE_E_INVAL  # second layer without an input
+    assert create(y=[P(2 << 20), P((2 << 20) + 8)]) == moe.MOE_E_INVAL  # misaligned output
+    assert create(wsb=16) == moe.MOE_E_WORKSPACE
+    assert create(w=moe.MoeWeights(4096, None, 4096, None)) == moe.MOE_E_INVAL  # has_shared without shared
+    assert create(dims=moe.MoeDims(256, 100, 8, 2, 1, 0)) == moe.MOE_E_UNSUPPORTED
+    assert L.moe_step_graph_destroy(None) == moe.MOE_OK
+    assert L.moe_step_graph_launch(None, None) == moe.MOE_E_INVAL
