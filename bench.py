@@ -520,6 +520,8 @@ def main():
     ap.add_argument("--tiered-only", action="store_true", help="run only the tiered-residency decode line")
     ap.add_argument("--reference-rates", action="store_true",
                     help="print only the rates torch reaches on this box (HBM read/copy, fp16 GEMM) and exit")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the library-code reference rates (copy, GEMM) measured after the workloads")
     ap.add_argument("--calibrate-copy-mb", type=int, default=0,
                     help="first run a plain elementwise copy (torch.neg) over this many MB, so that hardware "
                          "traffic counters taken over the run can be scaled against a kernel of known traffic")
@@ -595,6 +597,8 @@ def main():
     # achievable rates measured on the same box (library code, not this
     # project's), beside the published peaks the rooflines use
     try:
+        if args.no_measured_peaks:
+            raise RuntimeError("not measured (--no-measured-peaks)")
         ref = reference_rates()
         for rl in (roofline, roofline_prefill):
             if rl:
