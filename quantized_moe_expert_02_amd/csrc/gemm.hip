@@ -566,7 +566,8 @@ __global__ __launch_bounds__(64 * NW) void k_expert_gemm(GemmArgs a, int nx) {
             if (orow < 0) continue;
             float da = acc[0][q][AB + mt][i];
             if (SL::SUB) da = da * kSub - SL::OFF * s_sum[mm];
-            a.part[(size_t)orow * a.H + row] = s_w[mm] * (sd * da);
+            // streamed out (non-temporal): read once, by the combine
+            __builtin_nontemporal_store(s_w[mm] * (sd * da), a.part + (size_t)orow * a.H + row);
           }
       }
     }
