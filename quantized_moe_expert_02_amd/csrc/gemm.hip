@@ -593,7 +593,11 @@ __global__ __launch_bounds__(256) void k_combine(GemmArgs a) {
   for (int j0 = 0; j0 < a.k; j0 += 8) {
     float2 v[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = pt[(size_t)min(j0 + i, a.k - 1) * row];
+    for (int i = 0; i < 8; ++i) {
+      typedef float f2v __attribute__((ext_vector_type(2)));
+      const f2v u = __builtin_nontemporal_load(reinterpret_cast<const f2v*>(pt + (size_t)min(j0 + i, a.k - 1) * row));
+      v[i] = float2{u.x, u.y};
+    }
     __builtin_amdgcn_sched_barrier(0);  // all eight loads in flight before the first add
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
