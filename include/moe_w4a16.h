@@ -262,6 +262,25 @@ int moe_step_graph_create(const moe_dims_t* d, int32_t n_layers, const moe_weigh
 int moe_step_graph_launch(moe_step_graph_t g, void* stream);
 int moe_step_graph_destroy(moe_step_graph_t g);
 
+/* Reference rates for the rooflines (measurement support, not part of the
+ * layer).  The pages find decode speed bound by memory bandwidth ("GLM 5.3
+ * Flash をローカルに導入するには？", vramglass.com, the section on offloading
+ * experts to system memory); these two kernels measure what this GPU
+ * actually reaches, beside its published peaks:
+ *   moe_probe_stream_read: reads every 16-byte vector of buf (bytes, a
+ *     multiple of 16; buf 16-byte aligned) once with 128-bit non-temporal
+ *     loads over `blocks` workgroups of 256 threads (grid stride); writes one
+ *     word per thread to sink (blocks * 256 uint32, 4-byte aligned).
+ *   moe_probe_mfma: `blocks` workgroups of 512 threads; every wavefront runs
+ *     iters rounds of 16 independent v_mfma_f32_16x16x32_f16 (16 x 16 x 32
+ *     multiply-adds each) on register operands and writes one word per
+ *     thread to sink (blocks * 512 uint32).
+ * Both are stream-ordered launches; MOE_E_INVAL for a null or misaligned
+ * pointer, a size that is not a multiple of 16, or blocks / iters < 1;
+ * MOE_E_HIP if the launch fails. */
+int moe_probe_stream_read(const void* buf, size_t bytes, uint32_t* sink, int32_t blocks, void* stream);
+int moe_probe_mfma(uint32_t* sink, int32_t blocks, int32_t iters, void* stream);
+
 /* Largest T served by the GEMV path of moe_w4a16_forward. */
 int32_t moe_decode_max_tokens(void);
 

@@ -24,6 +24,7 @@ _CODE_BITS = {MOE_W_INT4_ROW: 4, MOE_W_E2M1_B16: 4, MOE_W_INT8_ROW: 8, MOE_W_INT
 EXPORTS = ("moe_packed_bytes", "moe_workspace_bytes", "moe_workspace_sync_bytes", "moe_pack", "moe_unpack",
            "moe_route", "moe_w4a16_forward", "moe_w4a16_forward_profiled", "moe_w4a16_forward_noalloc",
            "moe_decode_max_tokens", "moe_step_graph_create", "moe_step_graph_launch", "moe_step_graph_destroy",
+           "moe_probe_stream_read", "moe_probe_mfma",
            "moe_status_string", "moe_tier_create", "moe_tier_destroy", "moe_tier_use", "moe_tier_prefetch",
            "moe_tier_slot", "moe_tier_stats", "moe_tier_sync")
 MOE_TIER_LRU, MOE_TIER_HOT = 0, 1
@@ -91,6 +92,10 @@ def lib():
         L.moe_step_graph_launch.restype = ctypes.c_int
         L.moe_step_graph_destroy.argtypes = [P]
         L.moe_step_graph_destroy.restype = ctypes.c_int
+        L.moe_probe_stream_read.argtypes = [P, sz, P, i32, P]
+        L.moe_probe_stream_read.restype = ctypes.c_int
+        L.moe_probe_mfma.argtypes = [P, i32, i32, P]
+        L.moe_probe_mfma.restype = ctypes.c_int
         L.moe_tier_create.argtypes = [D, i32, P, P, i32, P, P, i32, ctypes.POINTER(P)]
         L.moe_tier_create.restype = ctypes.c_int
         L.moe_tier_destroy.argtypes = [P]
@@ -348,6 +353,21 @@ class StepGraph:
             self.close()
         except Exception:
             pass
+
+
+def probe_stream_read(buf: torch.Tensor, blocks: int, sink: torch.Tensor, stream=None):
+    """One plain streaming read of `buf` (moe_probe_stream_read)."""
+    rc = lib().moe_probe_stream_read(_p(buf), buf.numel() * buf.element_size(), _p(sink), blocks, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_probe_stream_read")
+
+
+def probe_mfma(sink: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """One pure matrix-core loop (moe_probe_mfma); returns its fp16 flops."""
+    rc = lib().moe_probe_mfma(_p(sink), blocks, iters, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_probe_mfma")
+    return blocks * 8 * iters * 16 * 2 * 16 * 16 * 32
 
 
 # ---- tiered expert residency (include/moe_tier.h) ---------------------------

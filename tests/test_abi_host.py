@@ -179,3 +179,15 @@ def test_step_graph_rejects_before_any_launch(L):
     assert create(dims=moe.MoeDims(256, 100, 8, 2, 1, 0)) == moe.MOE_E_UNSUPPORTED
     assert L.moe_step_graph_destroy(None) == moe.MOE_OK
     assert L.moe_step_graph_launch(None, None) == moe.MOE_E_INVAL
+
+
+def test_probe_argument_errors(L):
+    """The roofline probes reject bad arguments before any launch."""
+    P = ctypes.c_void_p
+    assert L.moe_probe_stream_read(None, 1 << 20, P(256), 8, None) == moe.MOE_E_INVAL
+    assert L.moe_probe_stream_read(P(256), (1 << 20) + 8, P(256), 8, None) == moe.MOE_E_INVAL  # not 16-byte vectors
+    assert L.moe_probe_stream_read(P(264), 1 << 20, P(256), 8, None) == moe.MOE_E_INVAL  # misaligned
+    assert L.moe_probe_stream_read(P(256), 1 << 20, P(256), 0, None) == moe.MOE_E_INVAL
+    assert L.moe_probe_mfma(None, 8, 10, None) == moe.MOE_E_INVAL
+    assert L.moe_probe_mfma(P(256), 0, 10, None) == moe.MOE_E_INVAL
+    assert L.moe_probe_mfma(P(256), 8, 0, None) == moe.MOE_E_INVAL
