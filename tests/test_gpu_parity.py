@@ -113,6 +113,9 @@ def _small_cases():
         ("int2_ragged", synth.Dims(384, 384, 33, 3, 0, 3), 7),
         ("int2_dense_e1k1", synth.Dims(128, 128, 1, 1, 0, 3), 3),
         ("int8_dense_e1k1", synth.Dims(128, 128, 1, 1, 0, 2), 1),
+        # k = E: every token takes every expert, the slots still in logit order
+        ("k_equals_e", synth.Dims(256, 128, 8, 8, 1, 0), 3),
+        ("e2m1_k_equals_e_t1", synth.Dims(256, 256, 4, 4, 0, 1), 1),
     ]
 
 
@@ -392,6 +395,9 @@ PREFILL_CASES = [
     ("int8_ragged_t70", synth.Dims(384, 256, 100, 6, 1, 2), 70),
     ("int2_t40", synth.Dims(256, 128, 8, 2, 1, 3), 40),
     ("int2_ragged_t129", synth.Dims(384, 384, 33, 3, 0, 3), 129),
+    ("tiny_t128", synth.Dims(256, 128, 8, 2, 1, 0), 128),
+    ("k_equals_e_t40", synth.Dims(256, 128, 8, 8, 1, 0), 40),
+    ("int2_k_equals_e_t70", synth.Dims(256, 128, 6, 6, 1, 3), 70),
 ]
 
 
