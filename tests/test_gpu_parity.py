@@ -396,6 +396,7 @@ PREFILL_CASES = [
     ("int2_t40", synth.Dims(256, 128, 8, 2, 1, 3), 40),
     ("int2_ragged_t129", synth.Dims(384, 384, 33, 3, 0, 3), 129),
     ("tiny_t128", synth.Dims(256, 128, 8, 2, 1, 0), 128),
+    ("tiny_t3000", synth.Dims(256, 128, 8, 2, 1, 0), 3000),  # union chunks and tiles past 2,048 tokens
     ("k_equals_e_t40", synth.Dims(256, 128, 8, 8, 1, 0), 40),
     ("int2_k_equals_e_t70", synth.Dims(256, 128, 6, 6, 1, 3), 70),
 ]
