@@ -80,3 +80,36 @@ def test_step_graph_chain(name, dims, T, n):
             assert_close(ys[l], oracle_y(canon[l], xs[l].cpu()), f"{name} layer {l}")
     finally:
         sg.close()
+
+
+@pytest.mark.parametrize("name", ["decode_b1", "e2m1_b1"])
+def test_step_graph_full_size_chain(name):
+    """Two layers of a full-size decode workload (all 256 + 1 experts
+    resident, one token) chained through the step graph: each replay equals
+    the eager calls bitwise, and each layer matches the oracle fed the input
+    the GPU gave it (at this width the chained activations keep their scale
+    without any rescaling)."""
+    _log("step graph, full size", name)
+    base, x0 = synth.workload(name, device=DEV)
+    dims = base.dims
+    canon = [base, dataclasses.replace(base, router_w=synth.make_router(dims, ("stepgraph", name, 1),
+                                                                        device=DEV)[0])]
+    pl0 = moe.PackedLayer.from_layer(base)
+    layers = [pl0, moe.PackedLayer(dims, pl0.packed, canon[1].router_w, None)]
+    T = x0.shape[0]
+    ws = moe.workspace(dims, T, DEV)
+    bufs = [x0.clone()] + [torch.zeros((T, dims.hidden), dtype=torch.float16, device=DEV) for _ in range(2)]
+    sg = moe.StepGraph(layers, bufs[:-1], bufs[1:], ws)
+    try:
+        for rep in range(3):
+            for y in bufs[1:]:
+                y.fill_(0)
+            sg.launch()
+            e0 = moe.moe_w4a16_forward(layers[0], bufs[0], ws=ws).clone()
+            e1 = moe.moe_w4a16_forward(layers[1], e0, ws=ws).clone()
+            torch.cuda.synchronize()
+            assert torch.equal(bufs[1], e0) and torch.equal(bufs[2], e1), (name, rep)
+        for l in range(2):
+            assert_close(bufs[l + 1], oracle_y(canon[l], bufs[l]), f"{name} layer {l}")
+    finally:
+        sg.close()
