@@ -647,6 +647,8 @@ def main():
         "cpu_baseline": cpu,
         "roofline_prefill": roofline_prefill,
         "measured_peaks": ref,
+        "layer_hbm_frac_of_measured": (res["layer_hbm_gbps"] / ref["stream_read_gbps"]
+                                       if "stream_read_gbps" in ref else None),
         "cpu_baseline_prefill": cpu_prefill,
         "secondary": secondary,
     }
