@@ -559,11 +559,17 @@ __device__ __forceinline__ void router_unit(const DecArgs& a, int it) {
       }
     }
   }
+  // the tokens' sums, four butterflies at a time interleaved (independent
+  // chains; each token's sum in the same order as wave_sum; tokens past T
+  // hold zeros)
 #pragma unroll
-  for (int t = 0; t < kDecodeMaxTokens; ++t) {
-    if (t < a.T) {
-      const double v = wave_sum(acc[t]);
-      if (lane == 0) st_dev(a.z + ((size_t)seg * a.T + t) * a.E + e, v);
+  for (int t0 = 0; t0 < kDecodeMaxTokens; t0 += 4) {
+    if (t0 < a.T) {
+      double v[4] = {acc[t0], acc[t0 + 1], acc[t0 + 2], acc[t0 + 3]};
+      wave_sum_n(v);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane == 0 && t0 + i < a.T) st_dev(a.z + ((size_t)seg * a.T + t0 + i) * a.E + e, v[i]);
     }
   }
 }

@@ -81,6 +81,23 @@ __device__ __forceinline__ double wave_sum(double v) {
   return v;
 }
 
+// wave_sum of N values at once, the N butterflies interleaved step by step.
+template <int N>
+__device__ __forceinline__ void wave_sum_n(double (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += partner_d<1>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += partner_d<2>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += partner_d<4>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += partner_d<8>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += partner_d<16>(v[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) v[i] += partner_d<32>(v[i]);
+}
+
 __device__ __forceinline__ double readlane_d(double v, int l) {
   const uint64_t u = __builtin_bit_cast(uint64_t, v);
   const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
