@@ -654,3 +654,32 @@ def test_forward_top_p_full_size(name):
     rel, mx = assert_close(y, y_ref, name)
     _log(f"  {name} top-p 0.7: kept {int((r.topk_idx >= 0).sum())}/{r.topk_idx.size} slots, U={r.n_unique} "
          f"rel_l2={rel:.2e}")
+
+
+# Batched routing (2 <= T <= 16): the routing tail ranks each token by
+# counting (groups of 64 experts, candidates, their ranks), falling back to
+# argmax rounds when two keys involved share a high word.  Exact twins of
+# the token's 1st, k-th and (k+1)-th experts, and none, for several E and k.
+BATCH_TIES = [(256, 8, None), (256, 8, 0), (256, 8, 7), (256, 8, 8), (200, 16, None), (200, 16, 15),
+              (100, 6, 2), (256, 17, None), (64, 3, 3)]
+
+
+@pytest.mark.parametrize("E,k,twin_rank", BATCH_TIES)
+def test_route_batched_ranks_and_twins(E, k, twin_rank):
+    dims = synth.Dims(256, 128, E, k, 0, 0)
+    rw, _ = synth.make_router(dims, ("btie", E, k))
+    x = synth.make_tokens(dims, 8, ("btie", E, k))
+    rw = rw.clone()
+    if twin_rank is not None:
+        r0 = oracle.route(dims, x, rw, None)
+        order = np.argsort(-r0.z[0], kind="stable")
+        a = int(order[twin_rank])
+        b = next(e for e in range(E) if e != a and e not in order[:k + 2].tolist())
+        rw[b] = rw[a]  # expert b: an exact twin of token 0's expert at rank twin_rank
+    r = oracle.route(dims, x, rw, None)
+    if twin_rank is None:
+        assert min_topk_gap(r, k) > 1e-9
+    layer = moe.PackedLayer(dims, torch.zeros((E, 256), dtype=torch.uint8, device=DEV), rw.to(DEV), None)
+    out = moe.moe_route(layer, x.to(DEV))
+    torch.cuda.synchronize()
+    _check_route(out, r, 8, k)
